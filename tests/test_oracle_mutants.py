@@ -1,0 +1,140 @@
+"""Plant plausible mistakes in copies of the oracle (CPU only) and check that
+the pins of tests/test_oracle.py catch each one. A pin set that a wrong
+oracle also passes would prove nothing; these tests show that the ones here
+fail on: an initial maximum of 0, an accumulator that is not rescaled, the
+wrong GQA head mapping, a missing or misplaced scale, top-left causal
+alignment, a log-sum-exp in base 2, a merge without the both-empty branch,
+a merge that drops the rescale, and a gather with the page index and slot
+swapped."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle.attention as oatt
+import oracle.state as ost
+import tests.test_oracle as pins
+from tests.conftest import load_golden
+
+
+def online_m0(scores, values, block):
+    # mistake: the running maximum starts at 0 instead of -inf
+    scores = np.asarray(scores, dtype=np.float64)
+    m, l, o = 0.0, 0.0, np.zeros(values.shape[-1])
+    for j in range(0, scores.size, block):
+        xb, vb = scores[j:j + block], values[j:j + block]
+        m_new = max(m, float(xb.max()))
+        alpha = math.exp(m - m_new)
+        p = np.exp(xb - m_new)
+        l = alpha * l + float(p.sum())
+        o = alpha * o + p @ vb
+        m = m_new
+    return m, l, o
+
+
+def online_no_rescale(scores, values, block):
+    # mistake: l is rescaled but the output accumulator is not
+    scores = np.asarray(scores, dtype=np.float64)
+    m, l, o = -np.inf, 0.0, np.zeros(values.shape[-1])
+    for j in range(0, scores.size, block):
+        xb, vb = scores[j:j + block], values[j:j + block]
+        m_new = max(m, float(xb.max()))
+        alpha = math.exp(m - m_new) if np.isfinite(m) else 0.0
+        p = np.exp(xb - m_new)
+        l = alpha * l + float(p.sum())
+        o = o + p @ vb
+        m = m_new
+    return m, l, o
+
+
+def _attention_variant(gqa=None, scale_mode="before", causal_mode="bottom_right", log=np.log):
+    def att(q, k, v, scale, causal=False, key_mask=None, row_mask=None, rows=None):
+        q, k, v = oatt._f64(q), oatt._f64(k), oatt._f64(v)
+        b_, h, t_q, d = q.shape
+        h_kv, t_k = k.shape[1], k.shape[2]
+        g = h // h_kv
+        rows = np.arange(t_q) if rows is None else np.asarray(rows)
+        o = np.zeros((b_, h, rows.size, v.shape[-1]))
+        lse = np.full((b_, h, rows.size), -np.inf)
+        for b in range(b_):
+            km = None if key_mask is None else np.asarray(key_mask)[b]
+            rm = None if row_mask is None else np.asarray(row_mask)[b]
+            if causal and causal_mode == "top_left":
+                vis = oatt.visible_mask(rows, t_k, t_k, True, km, rm)
+            else:
+                vis = oatt.visible_mask(rows, t_k, t_q, causal, km, rm)
+            for i in range(h):
+                kv = gqa(i, h, h_kv) if gqa else i // g
+                x = q[b, i, rows] @ k[b, kv].T
+                if scale_mode == "before":
+                    x = scale * x
+                x = np.where(vis, x, -np.inf)
+                ne = vis.any(axis=1)
+                if not ne.any():
+                    continue
+                xr = x[ne]
+                m = xr.max(axis=1)
+                p = np.exp(xr - m[:, None])
+                l = p.sum(axis=1)
+                o[b, i, ne] = (p / l[:, None]) @ v[b, kv]
+                lse[b, i, ne] = m + log(l)
+        return o, lse
+    return att
+
+
+def merge_no_empty_branch(a, b):
+    (ma, la, xa), (mb, lb, xb) = a, b
+    m = max(ma, mb)
+    with np.errstate(invalid="ignore"):
+        sa, sb = np.exp(ma - m), np.exp(mb - m)
+    return m, la * sa + lb * sb, np.asarray(xa) * sa + np.asarray(xb) * sb
+
+
+def merge_no_rescale(a, b):
+    (ma, la, xa), (mb, lb, xb) = a, b
+    m = max(ma, mb)
+    if np.isneginf(m):
+        return ost.EMPTY_M, 0.0, np.zeros_like(np.asarray(xa, dtype=np.float64))
+    return m, la + lb, np.asarray(xa) + np.asarray(xb)
+
+
+def gather_swapped(pool, block_table, seq_lens, s_max, out=None):
+    import torch
+    pool_c = pool.detach().cpu()
+    bt = np.asarray(block_table)
+    n_pages, page, h_kv, d = pool_c.shape
+    out = pool_c.new_zeros((bt.shape[0], h_kv, s_max, d)) if out is None else out
+    for b in range(bt.shape[0]):
+        p = np.arange(int(seq_lens[b]))
+        phys = bt[b, p % bt.shape[1]].astype(np.int64)      # mistake: wrong index
+        slot = (p // bt.shape[1] % page).astype(np.int64)
+        out[b, :, :p.size] = pool_c[torch.from_numpy(phys), torch.from_numpy(slot)].permute(1, 0, 2)
+    return out
+
+
+CASES = [
+    ("online_ref", online_m0, pins.test_online_row_far_below_zero, ()),
+    ("online_ref", online_no_rescale, pins.test_online_equals_safe_softmax_with_late_outlier, (load_golden,)),
+    ("attention_ref", _attention_variant(gqa=lambda i, h, hk: i % hk), pins.test_gqa_head_mapping, ()),
+    ("attention_ref", _attention_variant(scale_mode="none"), pins.test_causal_row_zero_is_its_single_key, ()),
+    ("attention_ref", _attention_variant(scale_mode="none"), pins.test_matches_torch_softmax_and_logsumexp, ()),
+    ("attention_ref", _attention_variant(causal_mode="top_left"), pins.test_bottom_right_causal_alignment, ()),
+    ("attention_ref", _attention_variant(log=np.log2), pins.test_worked_example_two_blocks, (load_golden,)),
+    ("merge_ref", merge_no_empty_branch, pins.test_state_and_merge_empty_branches, ()),
+    ("merge_ref", merge_no_rescale, pins.test_worked_example_two_blocks, (load_golden,)),
+    ("paged_gather_ref", gather_swapped, pins.test_paged_gather_recovers_ground_truth, ()),
+]
+
+
+@pytest.mark.parametrize("name,mutant,pin,args", CASES,
+                         ids=[f"{c[0]}-{c[1].__name__ if hasattr(c[1], '__name__') else i}-{c[2].__name__}"
+                              for i, c in enumerate(CASES)])
+def test_pin_catches_mutant(monkeypatch, name, mutant, pin, args):
+    # the unmodified oracle passes the pin ...
+    pin(*args)
+    # ... and the planted mistake fails it
+    monkeypatch.setattr(pins, name, mutant)
+    with pytest.raises((AssertionError, FloatingPointError, ValueError)):
+        with np.errstate(all="ignore"):
+            pin(*args)
