@@ -1,0 +1,280 @@
+"""Benchmark of the tiled online-softmax attention kernels on one MI355X.
+
+A step is one attn_prefill_fwd call over the Llama-3-8B layer prefill
+workload (B=1, h=32, h_kv=8, d_h=128, T=8192, causal, bf16, synthetic N(0,1)
+inputs already resident in HBM). ``value`` is its useful-FLOP throughput:
+4 * d_h * h * T(T+1)/2 = 5.498e11 FLOP per step (causal: only key/query
+pairs with j <= t count).
+
+Also reported, on the same line:
+* ``roofline``: the prefill kernel's achieved TFLOP/s (algorithmic FLOP per
+  launch over the mean launch time measured with HIP events on the launch
+  stream) against MI355X's dense bf16 MFMA peak, 2.5 PFLOP/s;
+* ``decode``: split-KV decode (stage 1 + merge) on the batch-1 70B-TP8 shard
+  shape (32768 contiguous keys; 40 distinct KV copies rotated so that every
+  step reads from HBM, not from the 256 MB last-level cache) and on the
+  64-sequence paged Llama-3-8B shape, as KV GB/s against 8 TB/s; the paged
+  gather as GB/s moved;
+* ``prefill_other``: the tiny and the numerics-stress prefill shapes;
+* ``cpu_baseline``: the float64 oracle timed on the host CPU on a bounded
+  sample of the same prefill workload (a slice of query rows of one head).
+
+``python bench.py --gpus N --steps K --warmup W``. Only one GPU is used; N > 1
+exits with a message.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill TFLOP/s (% MFMA peak); decode KV GB/s (% HBM peak) on 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, published
+HEAD_DIM = 128
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def causal_pairs(t_q, t_k):
+    off = t_k - t_q
+    return sum(min(t_k, t + off + 1) for t in range(t_q)) if t_q <= 4096 else \
+        t_q * (t_q + 1) // 2 + off * t_q
+
+
+def visible_pairs(inp):
+    """Number of visible (query, key) pairs per head, summed over the batch."""
+    total = 0
+    for b in range(inp["B"]):
+        km = np.ones(inp["T_k"], dtype=bool) if inp["key_mask"] is None else inp["key_mask"][b] != 0
+        rm = np.ones(inp["T_q"], dtype=bool) if inp["row_mask"] is None else inp["row_mask"][b] != 0
+        cum = np.concatenate([[0], np.cumsum(km)])
+        off = inp["T_k"] - inp["T_q"]
+        t = np.arange(inp["T_q"])
+        lim = np.minimum(inp["T_k"], t + off + 1) if inp["causal"] else np.full(inp["T_q"], inp["T_k"])
+        total += int((cum[lim] * rm).sum())
+    return total
+
+
+def time_loop(fn, steps, warmup):
+    """Mean ms per call: HIP events on torch's current stream (the stream the
+    library launches on), bracketed by device synchronisations."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall = time.perf_counter()
+    t0.record()
+    for i in range(steps):
+        fn(i)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall
+    return t0.elapsed_time(t1) / steps, wall
+
+
+def bench_prefill(name, steps, warmup, dev):
+    import torch
+    from online_softmax_tiled_amd import api
+    from online_softmax_tiled_amd.workloads import make_config
+    inp = make_config(name)
+    q, k, v = (inp[n].to(dev) for n in "qkv")
+    km = None if inp["key_mask"] is None else torch.from_numpy(inp["key_mask"]).to(dev)
+    rm = None if inp["row_mask"] is None else torch.from_numpy(inp["row_mask"]).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    flop = 4.0 * HEAD_DIM * inp["h"] * visible_pairs(inp)
+
+    def step(i=0):
+        api.prefill(q, k, v, causal=inp["causal"], scale=inp["scale"], key_mask=km, row_mask=rm,
+                    out=out, lse=lse)
+
+    ms, wall = time_loop(step, steps, warmup)
+    return dict(inp=inp, flop=flop, ms=ms, wall=wall, tflops=flop / (ms * 1e-3) / 1e12)
+
+
+def bench_decode_contiguous(steps, warmup, dev, copies=40):
+    import torch
+    from online_softmax_tiled_amd import api
+    from online_softmax_tiled_amd.workloads import make_config
+    dec = make_config("decode_70b_tp8_s32768")
+    q = dec["q"].to(dev)
+    sl = torch.from_numpy(dec["seq_lens"]).to(dev)
+    k0, v0 = dec["k"].to(dev), dec["v"].to(dev)
+    ks = [k0] + [k0.clone() for _ in range(copies - 1)]
+    vs = [v0] + [v0.clone() for _ in range(copies - 1)]
+    B, h, d = q.shape
+    h_kv = k0.shape[1]
+    chunk, splits = api.decode_plan(dec["seq_lens"], h, h_kv, device=dev)
+    po = torch.empty((B, h, splits, d), dtype=torch.float32, device=dev)
+    pm = torch.empty((B, h, splits), dtype=torch.float32, device=dev)
+    pl = torch.empty_like(pm)
+    o = torch.empty((B, h, d), dtype=q.dtype, device=dev)
+    lse = torch.empty((B, h), dtype=torch.float32, device=dev)
+    kv_bytes = 2 * int(dec["seq_lens"].sum()) * h_kv * d * q.element_size()
+
+    def split_only(i=0):
+        j = i % copies
+        api.decode_split(q, ks[j], vs[j], sl, chunk, splits, scale=dec["scale"], part_o=po, part_m=pm, part_l=pl)
+
+    def full(i=0):
+        split_only(i)
+        api.merge_states(po, pm, pl, sl, chunk, q.dtype, out=o, lse=lse)
+
+    ms_split, _ = time_loop(split_only, steps, warmup)
+    ms, _ = time_loop(full, steps, warmup)
+    return dict(workload="decode_70b_tp8_s32768", kv_bytes=kv_bytes, us_per_step=ms * 1e3,
+                split_us=ms_split * 1e3, gbs=kv_bytes / (ms * 1e-3) / 1e9,
+                frac_hbm=kv_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, plan=[chunk, splits],
+                rotated_kv_copies=copies)
+
+
+def bench_decode_paged(steps, warmup, dev, dec):
+    import torch
+    from online_softmax_tiled_amd import api
+    q = dec["q"].to(dev)
+    sl = torch.from_numpy(dec["seq_lens"]).to(dev)
+    kp, vp = dec["k_pool"].to(dev), dec["v_pool"].to(dev)
+    bt = torch.from_numpy(dec["block_table"]).to(dev)
+    B, h, d = q.shape
+    h_kv = kp.shape[2]
+    chunk, splits = api.decode_plan(dec["seq_lens"], h, h_kv, device=dev)
+    po = torch.empty((B, h, splits, d), dtype=torch.float32, device=dev)
+    pm = torch.empty((B, h, splits), dtype=torch.float32, device=dev)
+    pl = torch.empty_like(pm)
+    o = torch.empty((B, h, d), dtype=q.dtype, device=dev)
+    lse = torch.empty((B, h), dtype=torch.float32, device=dev)
+    kv_bytes = 2 * int(dec["seq_lens"].sum()) * h_kv * d * q.element_size()
+
+    def split_only(i=0):
+        api.decode_split(q, kp, vp, sl, chunk, splits, block_table=bt, page_size=dec["page_size"],
+                         scale=dec["scale"], part_o=po, part_m=pm, part_l=pl)
+
+    def full(i=0):
+        split_only()
+        api.merge_states(po, pm, pl, sl, chunk, q.dtype, out=o, lse=lse)
+
+    ms_split, _ = time_loop(split_only, steps, warmup)
+    ms, _ = time_loop(full, steps, warmup)
+    s_max = int(dec["seq_lens"].max())
+    gout = torch.empty((B, h_kv, s_max, d), dtype=q.dtype, device=dev)
+
+    def gather(i=0):
+        api.paged_gather(kp, bt, sl, s_max, out=gout)
+
+    ms_g, _ = time_loop(gather, max(3, steps // 4), 2)
+    del gout
+    gather_bytes = kv_bytes  # K pool rows read + the same bytes written (one pool)
+    return dict(workload="paged_decode_llama3_8b_b64", kv_bytes=kv_bytes, us_per_step=ms * 1e3,
+                split_us=ms_split * 1e3, gbs=kv_bytes / (ms * 1e-3) / 1e9,
+                frac_hbm=kv_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, plan=[chunk, splits],
+                gather_us=ms_g * 1e3, gather_gbs=gather_bytes / (ms_g * 1e-3) / 1e9)
+
+
+def cpu_baseline(inp, budget_s=15.0):
+    """The float64 oracle on the host CPU over a bounded sample of the prefill
+    workload: query rows of head 0, growing until about budget_s seconds."""
+    import threadpoolctl
+    from oracle import attention_ref
+    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
+    t_q = inp["T_q"]
+    rows_n, total_rows, total_flop, total_t = 64, 0, 0.0, 0.0
+    rng = np.random.default_rng(0)
+    q1 = inp["q"][:, :1]
+    while total_t < budget_s and total_rows < t_q:
+        rows = np.sort(rng.choice(t_q, size=min(rows_n, t_q), replace=False))
+        t = time.perf_counter()
+        attention_ref(q1, inp["k"][:, :1], inp["v"][:, :1], inp["scale"], inp["causal"], rows=rows)
+        total_t += time.perf_counter() - t
+        total_flop += 4.0 * HEAD_DIM * float(np.minimum(rows + 1, inp["T_k"]).sum())
+        total_rows += rows.size
+        rows_n *= 2
+    return dict(value=total_flop / total_t / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
+                sample=f"{total_rows} random query rows of head 0 of the T=8192 causal prefill "
+                       f"(float64 numpy, materialised), {total_t:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="only the headline prefill")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested); "
+              "the attention kernels here run on a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from online_softmax_tiled_amd import api
+    dev = torch.device("cuda:0")
+    log(f"device: {torch.cuda.get_device_name(dev)}, {api.version()}")
+
+    res = bench_prefill("llama3_8b_prefill_t8192", args.steps, args.warmup, dev)
+    log(f"prefill T=8192: {res['ms']:.3f} ms/step, {res['tflops']:.1f} TFLOP/s")
+    tflops = res["tflops"]
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama3_8b_prefill_t8192", "B": 1, "h": 32, "h_kv": 8, "T": 8192,
+                   "d_h": 128, "causal": True, "flop_per_step": res["flop"]},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }
+    inp = res.pop("inp")
+    if not args.no_extras:
+        other = {}
+        for name in ("tiny_prefill", "stress_prefill_t4096"):
+            r = bench_prefill(name, max(10, args.steps), 3, dev)
+            other[name] = {"ms": round(r["ms"], 4), "tflops": round(r["tflops"], 2),
+                           "frac_mfma": round(r["tflops"] / PEAK_BF16_TFLOPS, 4)}
+            log(f"prefill {name}: {r['ms']:.4f} ms, {r['tflops']:.1f} TFLOP/s")
+        line["prefill_other"] = other
+        decode = {}
+        r3 = bench_decode_contiguous(max(200, args.steps), 20, dev)
+        log(f"decode 70b-tp8: {r3['us_per_step']:.2f} us/step ({r3['split_us']:.2f} split), {r3['gbs']:.0f} GB/s")
+        decode[r3.pop("workload")] = r3
+        from online_softmax_tiled_amd.workloads import make_config
+        log("generating the paged decode workload ...")
+        dec = make_config("paged_decode_llama3_8b_b64")
+        r4 = bench_decode_paged(max(20, args.steps), 3, dev, dec)
+        log(f"decode paged b64: {r4['us_per_step']:.1f} us/step ({r4['split_us']:.1f} split), {r4['gbs']:.0f} GB/s; "
+            f"gather {r4['gather_gbs']:.0f} GB/s")
+        decode[r4.pop("workload")] = r4
+        for v in decode.values():
+            for key in list(v):
+                if isinstance(v[key], float):
+                    v[key] = round(v[key], 4)
+        line["decode"] = decode
+    if not args.no_cpu_baseline:
+        log("timing the float64 oracle on the host CPU ...")
+        line["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

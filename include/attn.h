@@ -1,0 +1,194 @@
+/*
+ * attn.h -- C ABI of libattn.so: exact scaled-dot-product attention computed
+ * tile by tile with the online-softmax (m, l, O~) recurrence on AMD Instinct
+ * MI355X (gfx950). The score matrix never reaches device memory.
+ *
+ * The operations follow four web pages:
+ *  [NA] "Naive attention and the online softmax" (mlinterviewnotes.com,
+ *       inference course 03-01)
+ *  [OR] "The Online Softmax Recurrence" (inferenceinterviews.com)
+ *  [DA] "Decode attention: FlashDecoding, split-K, paged kernels"
+ *       (mlinterviewnotes.com, inference course 03-03)
+ *  [MI] "Merge normalized attention without averaging tile outputs"
+ *       (study.greatitself.com)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Layouts are row-major and contiguous. Element types: dtype 0 = IEEE fp16,
+ *   1 = bfloat16 for Q/K/V/O; statistics, partials and LSE are always fp32
+ *   ([NA] section "What has to be fp32"; [OR] section "Where it breaks").
+ * - Every pointer except *_host arguments is a device pointer owned by the
+ *   caller. The library allocates no device memory and keeps no state apart
+ *   from a per-thread error message.
+ * - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *   stream). Nothing synchronises.
+ * - GQA: query head i reads KV head i / g with g = h / h_kv ([NA] opening
+ *   section; [DA] section "Where GQA enters").
+ * - LSE is the natural log-sum-exp m + ln(l) of the visible logits of a row
+ *   ([NA] section "The state that gets passed around is the log-sum-exp").
+ * - A row with no visible key gets an output of all-zero bits (+0.0) and
+ *   LSE = -inf ([MI], last paragraph: zero output as the extension for a
+ *   fully masked row).
+ * - Return value: ATTN_OK, or an error code. Arguments are validated before
+ *   anything is launched; on error nothing is launched and attn_last_error()
+ *   describes the problem. Nothing aborts and no C++ exception crosses the
+ *   ABI.
+ * - Supported today: d_h = 128; dtype f16 or bf16; h a multiple of h_kv;
+ *   paged KV with page_size a positive multiple of 16 ([DA], paged
+ *   addressing: kernel block sizes are multiples of 16). Anything else
+ *   returns ATTN_ERR_UNSUPPORTED.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_DTYPE_F16 0
+#define ATTN_DTYPE_BF16 1
+
+#define ATTN_OK 0
+#define ATTN_ERR_INVALID 1     /* malformed argument (null pointer, negative size, ...) */
+#define ATTN_ERR_UNSUPPORTED 2 /* well-formed but outside the support matrix */
+#define ATTN_ERR_HIP 3         /* the HIP runtime rejected a launch */
+
+/*
+ * Prefill: O = softmax(scale * Q K^T restricted to visible keys) V, per
+ * (batch, query head, query row), with the per-row LSE.
+ * [NA] opening section (shapes Q [h,T,d_h], K/V [h_kv,T,d_h]), sections (3)
+ * "The online recurrence" and "Extending the recurrence to the output"
+ * (one pass over key tiles, divide once at the end).
+ *
+ *   q        [B, h, T_q, d_h]      dtype
+ *   k, v     [B, h_kv, T_k, d_h]   dtype
+ *   key_mask [B, T_k] uint8 or NULL; nonzero = the key may be attended.
+ *   row_mask [B, T_q] uint8 or NULL; zero = every key of that query row is
+ *            masked (the row gets the zero output).
+ *   o        [B, h, T_q, d_h]      dtype (written)
+ *   lse      [B, h, T_q] fp32 or NULL (written if not NULL)
+ *   scale    multiplies Q K^T before masking (normally 1/sqrt(d_h)).
+ *   causal   nonzero: query t sees key j iff j <= t + T_k - T_q (aligned to
+ *            the bottom-right corner); requires T_q <= T_k.
+ * Visible = causal condition AND key_mask AND row_mask. Masked keys are
+ * excluded, never given a finite stand-in value ([MI], paragraph on fully
+ * masked tiles).
+ */
+int attn_prefill_fwd(const void* q, const void* k, const void* v,
+                     const uint8_t* key_mask, const uint8_t* row_mask,
+                     void* o, float* lse,
+                     int B, int h, int h_kv, int T_q, int T_k, int d_h,
+                     int dtype, float scale, int causal, void* stream);
+
+/*
+ * Decode plan (host only, pure): choose the split-KV chunk length so the
+ * stage-1 grid fills the GPU. [DA] sections "The grid" (the smallest split
+ * count that fills the machine in one wave) and "SGLang: a split count
+ * computed per sequence" (more splits for longer contexts).
+ *
+ *   seq_lens_host [B] host int32, the KV length of each sequence.
+ *   num_cus       compute units of the device (256 on MI355X).
+ *   chunk_keys    (out) keys per split: a multiple of 64, at least 64.
+ *   max_splits    (out) ceil(max_b seq_lens[b] / chunk_keys), at least 1:
+ *                 the split dimension of the partial buffers.
+ * The split count of sequence b is n_b = ceil(seq_lens[b] / chunk_keys);
+ * units = h_kv * sum_b n_b is at least num_cus whenever the keys allow it.
+ */
+int attn_decode_plan(int B, const int32_t* seq_lens_host, int h, int h_kv, int d_h,
+                     int num_cus, int32_t* chunk_keys, int32_t* max_splits);
+
+/*
+ * Decode stage 1 (split-KV, FlashDecoding): one query token per sequence;
+ * the KV of sequence b is cut into contiguous slices of chunk_keys keys and
+ * each slice emits an unnormalised partial state per query head.
+ * [DA] opening section (split-K over keys, partial O~, m, l), section
+ * "Segment length, and the early exit", section "Where GQA enters" (all g
+ * query heads of a KV head share one read of the KV), and the paged
+ * addressing that follows "What the merge costs".
+ *
+ *   q            [B, h, d_h] dtype
+ *   k, v         contiguous: [B, h_kv, s_max, d_h] (block_table == NULL);
+ *                paged: pools [num_pages, page_size, h_kv, d_h].
+ *   block_table  NULL, or [B, max_pages] int32 physical page ids: key p of
+ *                sequence b is slot p % page_size of page
+ *                block_table[b * max_pages + p / page_size].
+ *   num_pages    pages in each pool (paged only). A key whose page id lies
+ *                outside [0, num_pages) is excluded, never dereferenced.
+ *   seq_lens     [B] int32 device, KV length of each sequence. Must not
+ *                exceed s_max (contiguous) or max_pages * page_size (paged);
+ *                keys past that bound are never read.
+ *   chunk_keys   positive multiple of 16 (attn_decode_plan returns a
+ *                multiple of 64).
+ *   max_splits   split dimension of the partial buffers.
+ *   part_o       [B, h, max_splits, d_h] fp32: O~_i = sum exp(x - m_i) v
+ *   part_m       [B, h, max_splits] fp32: m_i, the reference maximum of
+ *                split i in natural-log units (-inf for a split with no key)
+ *   part_l       [B, h, max_splits] fp32: l_i = sum exp(x - m_i)
+ * Split i of sequence b covers keys [i*chunk_keys, (i+1)*chunk_keys), the
+ * last split (i = max_splits-1) also takes any keys beyond. Exactly the splits
+ * i < n_b = min(max_splits, ceil(seq_lens[b]/chunk_keys)) are written; the
+ * others are left untouched and never read by attn_merge_states.
+ * (m_i, l_i, O~_i) is a state in the sense of [OR] section "The recurrence":
+ * m_i is its reference point (this library stores the largest logit of the
+ * split), and any reference gives the same merged result.
+ */
+int attn_decode_split(const void* q, const void* k, const void* v,
+                      const int32_t* block_table, int max_pages, int page_size, int num_pages,
+                      const int32_t* seq_lens, int s_max,
+                      int B, int h, int h_kv, int d_h,
+                      int chunk_keys, int max_splits, int dtype, float scale,
+                      float* part_o, float* part_m, float* part_l, void* stream);
+
+/*
+ * Decode stage 2: merge the split partials of each (sequence, head).
+ * [DA] "Stage 2" reduction in section "Where GQA enters" (global maximum,
+ * rescale each split's l and O~ by exp(m_i - max), sum, divide once, zero
+ * when the total mass is zero); [MI] paragraph on merging disjoint tiles;
+ * [NA] section "The base case is a NaN factory" (an empty state never
+ * produces NaN).
+ *
+ *   part_o/part_m/part_l  as written by attn_decode_split.
+ *   seq_lens     [B] int32 device; with chunk_keys it gives the valid split
+ *                count n_b, computed exactly as attn_decode_split does, so
+ *                producer and reducer agree ([DA] section "CUDA graphs need
+ *                the split count pinned").
+ *   o            [B, h, d_h] dtype (written); lse [B, h] fp32 or NULL.
+ * A split with m_i = -inf or l_i = 0 is empty and contributes nothing.
+ */
+int attn_merge_states(const float* part_o, const float* part_m, const float* part_l,
+                      const int32_t* seq_lens, int chunk_keys,
+                      int B, int h, int max_splits, int d_h,
+                      void* o, float* lse, int dtype, void* stream);
+
+/*
+ * Paged-KV gather: copy each sequence's keys (or values) out of a paged pool
+ * into a contiguous tensor, bit for bit. [DA] paged addressing after section
+ * "What the merge costs": position p lives in page block_table[b][p / P] at
+ * slot p % P.
+ *
+ *   pool        [num_pages, page_size, h_kv, d_h] dtype
+ *   block_table [B, max_pages] int32 device
+ *   seq_lens    [B] int32 device, each <= min(s_max, max_pages * page_size)
+ *   num_pages   pages in the pool; positions whose page id lies outside
+ *               [0, num_pages) are left untouched.
+ *   out         [B, h_kv, s_max, d_h] dtype; positions p >= seq_lens[b] are
+ *               left untouched. page_size may be any positive value here.
+ */
+int attn_paged_gather(const void* pool, const int32_t* block_table, const int32_t* seq_lens,
+                      int B, int h_kv, int d_h, int page_size, int max_pages, int num_pages,
+                      int s_max, int dtype, void* out, void* stream);
+
+/* Message describing the last error returned on the calling thread ("" if
+ * none). The pointer stays valid until the next call on that thread. */
+const char* attn_last_error(void);
+
+/* Library version string. */
+const char* attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

@@ -1,0 +1,200 @@
+// C ABI of libattn.so: argument validation, error reporting and dispatch to
+// the gfx950 kernels. Every argument is checked before anything is launched;
+// errors come back as codes with a per-thread message, never as exceptions
+// or aborts. The conditions the pages treat as hard errors (the head count
+// must be a multiple of the KV head count and the head size must be one the
+// kernel was built for, "Decode attention: FlashDecoding, split-K, paged
+// kernels", section "The kernel vLLM deleted"; kernel block sizes are
+// multiples of 16, same page, paged addressing and section "Kernel block
+// size vs allocator block size") are rejected here.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "attn.h"
+
+namespace attn {
+hipError_t prefill_fwd(const void* q, const void* k, const void* v, const uint8_t* key_mask,
+                       const uint8_t* row_mask, void* o, float* lse, int B, int h, int h_kv,
+                       int T_q, int T_k, int dtype, float scale, int causal, hipStream_t stream);
+hipError_t decode_split(const void* q, const void* k, const void* v, const int32_t* block_table,
+                        int max_pages, int page_size, int num_pages, const int32_t* seq_lens,
+                        int s_max, int B, int h, int h_kv, int chunk_keys, int max_splits,
+                        int dtype, float scale, float* part_o, float* part_m, float* part_l,
+                        hipStream_t stream);
+hipError_t merge_states(const float* part_o, const float* part_m, const float* part_l,
+                        const int32_t* seq_lens, int chunk_keys, int B, int h, int max_splits,
+                        void* o, float* lse, int dtype, hipStream_t stream);
+hipError_t paged_gather(const void* pool, const int32_t* block_table, const int32_t* seq_lens,
+                        int B, int h_kv, int page_size, int max_pages, int num_pages, int s_max,
+                        void* out, hipStream_t stream);
+int decode_plan(int B, const int32_t* seq_lens, int h_kv, int num_cus, int32_t* chunk_keys,
+                int32_t* max_splits);
+}  // namespace attn
+
+namespace {
+
+constexpr int kHeadDim = 128;
+constexpr int kMaxGroup = 16;   // decode: query heads per KV head
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return ATTN_OK;
+}
+
+int from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(ATTN_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+#define REQUIRE(cond, code, ...)          \
+  do {                                    \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+int check_common(const char* fn, int dtype, int d_h) {
+  REQUIRE(dtype == ATTN_DTYPE_F16 || dtype == ATTN_DTYPE_BF16, ATTN_ERR_UNSUPPORTED,
+          "%s: dtype %d is not supported (0 = f16, 1 = bf16)", fn, dtype);
+  REQUIRE(d_h == kHeadDim, ATTN_ERR_UNSUPPORTED, "%s: head size %d is not supported (only %d)", fn, d_h,
+          kHeadDim);
+  return ATTN_OK;
+}
+
+int check_heads(const char* fn, int h, int h_kv) {
+  REQUIRE(h > 0 && h_kv > 0, ATTN_ERR_INVALID, "%s: head counts must be positive (h=%d, h_kv=%d)", fn, h, h_kv);
+  REQUIRE(h % h_kv == 0, ATTN_ERR_INVALID, "%s: h=%d is not a multiple of h_kv=%d", fn, h, h_kv);
+  return ATTN_OK;
+}
+
+int check_scale(const char* fn, float scale) {
+  REQUIRE(std::isfinite(scale) && scale > 0.f, ATTN_ERR_INVALID, "%s: scale must be finite and > 0 (got %g)", fn,
+          (double)scale);
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_prefill_fwd(const void* q, const void* k, const void* v, const uint8_t* key_mask,
+                     const uint8_t* row_mask, void* o, float* lse, int B, int h, int h_kv, int T_q,
+                     int T_k, int d_h, int dtype, float scale, int causal, void* stream) {
+  const char* fn = "attn_prefill_fwd";
+  if (int e = check_common(fn, dtype, d_h)) return e;
+  if (int e = check_heads(fn, h, h_kv)) return e;
+  if (int e = check_scale(fn, scale)) return e;
+  REQUIRE(B >= 0 && T_q >= 0 && T_k >= 0, ATTN_ERR_INVALID, "%s: negative size (B=%d, T_q=%d, T_k=%d)", fn, B,
+          T_q, T_k);
+  REQUIRE(!causal || T_q <= T_k, ATTN_ERR_UNSUPPORTED, "%s: causal attention needs T_q <= T_k (T_q=%d, T_k=%d)",
+          fn, T_q, T_k);
+  const long rows = (long)B * h * T_q;
+  REQUIRE(rows * kHeadDim < (1L << 40), ATTN_ERR_INVALID, "%s: problem too large", fn);
+  if (rows == 0) return ok();
+  REQUIRE(q && o, ATTN_ERR_INVALID, "%s: q and o must not be NULL", fn);
+  REQUIRE(T_k == 0 || (k && v), ATTN_ERR_INVALID, "%s: k and v must not be NULL", fn);
+  return from_hip(attn::prefill_fwd(q, k, v, key_mask, row_mask, o, lse, B, h, h_kv, T_q, T_k, dtype, scale,
+                                    causal, static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+int attn_decode_plan(int B, const int32_t* seq_lens_host, int h, int h_kv, int d_h, int num_cus,
+                     int32_t* chunk_keys, int32_t* max_splits) {
+  const char* fn = "attn_decode_plan";
+  if (int e = check_heads(fn, h, h_kv)) return e;
+  REQUIRE(d_h == kHeadDim, ATTN_ERR_UNSUPPORTED, "%s: head size %d is not supported (only %d)", fn, d_h,
+          kHeadDim);
+  REQUIRE(B >= 0, ATTN_ERR_INVALID, "%s: negative batch %d", fn, B);
+  REQUIRE(num_cus > 0, ATTN_ERR_INVALID, "%s: num_cus must be positive (got %d)", fn, num_cus);
+  REQUIRE(chunk_keys && max_splits, ATTN_ERR_INVALID, "%s: output pointers must not be NULL", fn);
+  REQUIRE(B == 0 || seq_lens_host, ATTN_ERR_INVALID, "%s: seq_lens_host must not be NULL", fn);
+  for (int b = 0; b < B; ++b)
+    REQUIRE(seq_lens_host[b] >= 0, ATTN_ERR_INVALID, "%s: seq_lens[%d] = %d is negative", fn, b, seq_lens_host[b]);
+  attn::decode_plan(B, seq_lens_host, h_kv, num_cus, chunk_keys, max_splits);
+  return ok();
+}
+
+int attn_decode_split(const void* q, const void* k, const void* v, const int32_t* block_table, int max_pages,
+                      int page_size, int num_pages, const int32_t* seq_lens, int s_max, int B, int h, int h_kv,
+                      int d_h, int chunk_keys, int max_splits, int dtype, float scale, float* part_o,
+                      float* part_m, float* part_l, void* stream) {
+  const char* fn = "attn_decode_split";
+  if (int e = check_common(fn, dtype, d_h)) return e;
+  if (int e = check_heads(fn, h, h_kv)) return e;
+  if (int e = check_scale(fn, scale)) return e;
+  REQUIRE(h / h_kv <= kMaxGroup, ATTN_ERR_UNSUPPORTED, "%s: %d query heads per KV head (at most %d supported)",
+          fn, h / h_kv, kMaxGroup);
+  REQUIRE(B >= 0, ATTN_ERR_INVALID, "%s: negative batch %d", fn, B);
+  REQUIRE(chunk_keys > 0 && chunk_keys % 16 == 0, ATTN_ERR_INVALID,
+          "%s: chunk_keys must be a positive multiple of 16 (got %d)", fn, chunk_keys);
+  REQUIRE(max_splits >= 1 && max_splits <= 65535, ATTN_ERR_INVALID, "%s: max_splits must be in [1, 65535] (got %d)",
+          fn, max_splits);
+  REQUIRE(h_kv <= 65535 && B <= 65535, ATTN_ERR_UNSUPPORTED, "%s: grid too large", fn);
+  if (block_table) {
+    REQUIRE(page_size > 0 && page_size % 16 == 0, ATTN_ERR_UNSUPPORTED,
+            "%s: page_size must be a positive multiple of 16 (got %d)", fn, page_size);
+    REQUIRE(max_pages > 0 && num_pages > 0, ATTN_ERR_INVALID, "%s: max_pages and num_pages must be positive", fn);
+  } else {
+    REQUIRE(s_max >= 0, ATTN_ERR_INVALID, "%s: negative s_max %d", fn, s_max);
+  }
+  if (B == 0) return ok();
+  REQUIRE(q && k && v && seq_lens && part_o && part_m && part_l, ATTN_ERR_INVALID,
+          "%s: a required pointer is NULL", fn);
+  return from_hip(attn::decode_split(q, k, v, block_table, max_pages, page_size, num_pages, seq_lens, s_max, B, h,
+                                     h_kv, chunk_keys, max_splits, dtype, scale, part_o, part_m, part_l,
+                                     static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+int attn_merge_states(const float* part_o, const float* part_m, const float* part_l, const int32_t* seq_lens,
+                      int chunk_keys, int B, int h, int max_splits, int d_h, void* o, float* lse, int dtype,
+                      void* stream) {
+  const char* fn = "attn_merge_states";
+  if (int e = check_common(fn, dtype, d_h)) return e;
+  REQUIRE(B >= 0 && h > 0, ATTN_ERR_INVALID, "%s: bad sizes (B=%d, h=%d)", fn, B, h);
+  REQUIRE(chunk_keys > 0, ATTN_ERR_INVALID, "%s: chunk_keys must be positive (got %d)", fn, chunk_keys);
+  REQUIRE(max_splits >= 1, ATTN_ERR_INVALID, "%s: max_splits must be >= 1 (got %d)", fn, max_splits);
+  if (B == 0) return ok();
+  REQUIRE((long)B * h < (1L << 31), ATTN_ERR_UNSUPPORTED, "%s: grid too large", fn);
+  REQUIRE(part_o && part_m && part_l && seq_lens && o, ATTN_ERR_INVALID, "%s: a required pointer is NULL", fn);
+  return from_hip(attn::merge_states(part_o, part_m, part_l, seq_lens, chunk_keys, B, h, max_splits, o, lse, dtype,
+                                     static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+int attn_paged_gather(const void* pool, const int32_t* block_table, const int32_t* seq_lens, int B, int h_kv,
+                      int d_h, int page_size, int max_pages, int num_pages, int s_max, int dtype, void* out,
+                      void* stream) {
+  const char* fn = "attn_paged_gather";
+  if (int e = check_common(fn, dtype, d_h)) return e;
+  REQUIRE(B >= 0 && h_kv > 0 && s_max >= 0, ATTN_ERR_INVALID, "%s: bad sizes (B=%d, h_kv=%d, s_max=%d)", fn, B,
+          h_kv, s_max);
+  REQUIRE(page_size > 0 && max_pages > 0 && num_pages > 0, ATTN_ERR_INVALID,
+          "%s: page_size, max_pages and num_pages must be positive", fn);
+  REQUIRE(B <= 65535, ATTN_ERR_UNSUPPORTED, "%s: grid too large", fn);
+  if (B == 0 || s_max == 0) return ok();
+  REQUIRE(pool && block_table && seq_lens && out, ATTN_ERR_INVALID, "%s: a required pointer is NULL", fn);
+  return from_hip(attn::paged_gather(pool, block_table, seq_lens, B, h_kv, page_size, max_pages, num_pages, s_max,
+                                     out, static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+const char* attn_last_error(void) { return g_last_error.c_str(); }
+
+const char* attn_version(void) { return "libattn 0.1 (gfx950)"; }
+
+}  // extern "C"

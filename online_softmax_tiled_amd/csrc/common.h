@@ -1,0 +1,105 @@
+// Shared device helpers for the gfx950 (CDNA4) attention kernels: element
+// types, MFMA wrappers, packed conversions, fp32 exp2/log2 on the hardware
+// transcendental unit, and the error plumbing of the host side.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn.h"
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Hardware base-2 exponential and logarithm (v_exp_f32 / v_log_f32). The
+// kernels keep logits in base-2 units (x * scale * log2 e) so that one
+// multiply-add and one v_exp_f32 give exp(x - m); exp2(-inf) = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Per-dtype operations. DT = ATTN_DTYPE_F16 or ATTN_DTYPE_BF16. Operands are
+// passed around as raw 16-byte vectors (u32x4 = 8 elements).
+template <int DT>
+struct Elem;
+
+template <>
+struct Elem<ATTN_DTYPE_BF16> {
+  // D(32x32 fp32) += A(32x16) * B(16x32); A lane l holds row l%32, k in
+  // [8*(l/32), 8*(l/32)+8); B lane l holds column l%32, same k range.
+  static __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  // D(16x16 fp32) += A(16x32) * B(32x16); A lane l holds row l%16, k in
+  // [8*(l/16), 8*(l/16)+8); B lane l holds column l%16, same k range.
+  static __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  // Two fp32 -> two bf16 (round to nearest even), lo in bits [15:0].
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  }
+  static __device__ __forceinline__ float to_f32(uint16_t x) {
+    return __builtin_bit_cast(float, (uint32_t)x << 16);
+  }
+};
+
+template <>
+struct Elem<ATTN_DTYPE_F16> {
+  static __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  }
+  static __device__ __forceinline__ float to_f32(uint16_t x) {
+    return (float)__builtin_bit_cast(_Float16, x);
+  }
+};
+
+// Byte select of v_perm_b32: result byte i = byte sel[i] of {hi:lo} (0-3 lo).
+__device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+// (low half of a, low half of b) and (high half of a, high half of b).
+__device__ __forceinline__ uint32_t pack_lo16(uint32_t a, uint32_t b) { return perm_b32(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) { return perm_b32(b, a, 0x07060302u); }
+
+// Max of x over lanes l and l ^ 32 (the two halves of a wave64), using the
+// gfx950 lane-swap between the halves.
+__device__ __forceinline__ float max_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, x), false, false);
+  return __builtin_bit_cast(float, r[0]) + __builtin_bit_cast(float, r[1]);
+}
+
+__device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ void store8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
+
+}  // namespace attn

@@ -1,0 +1,338 @@
+// Split-KV decode (stage 1) for gfx950, and the host-side split plan.
+//
+// "Decode attention: FlashDecoding, split-K, paged kernels": with one query
+// token per sequence the query axis gives almost no parallelism, so the key
+// axis is cut into contiguous slices, each slice runs the online-softmax loop
+// over its own keys, and each emits an unnormalised partial state (O~, m, l)
+// that a second kernel merges (opening section; section "Segment length, and
+// the early exit"). All g query heads of a KV head are handled by one
+// workgroup, so each K/V byte is read from HBM once (section "Where GQA
+// enters"). Paged KV is addressed through the block table: key p of sequence
+// b is slot p % P of page table[b][p / P] (the paged addressing after
+// section "What the merge costs").
+//
+// Workgroup = one (sequence b, KV head, split); 4 waves take 32-key tiles of
+// the split round-robin, each with its own state, and merge the four states
+// through LDS at the end.
+//
+// Per 32-key tile and wave (v_mfma_f32_16x16x32, the g <= 16 query heads of
+// the group as the 16 columns, unused columns zero):
+//   S^T = K Q^T: A = K rows loaded straight from global memory (lane l: key
+//   l%16 of a 16-key block, d in [8*(l/16) + 32c, +8)), B = Q^T in VGPRs.
+//   Accumulator: lane l holds head l%16 and keys 4*(l/16) + r of the block.
+//   Row max: in-lane over 8 scores, then across the four 16-lane rows.
+//   O~^T += V^T P^T: P^T comes from the score registers as the B operand
+//   (keys 4a+r of block 0 then of block 1, a = l/16); V^T is staged through a
+//   per-wave LDS region, stored transposed so the A operand (8 keys of one d)
+//   is one 16-byte LDS read.
+// Keys outside the split, past the sequence, or on a page id outside the
+// pool are excluded (score -inf) and their V rows are zeroed before use, so
+// poisoned (NaN) slots never reach the result.
+#include "common.h"
+
+namespace attn {
+namespace {
+
+constexpr int kD = 128;
+constexpr int kWaves = 4;
+constexpr int kTile = 32;              // keys per wave tile
+constexpr int kVtStr = kTile + 8;      // V^T row stride in LDS (elements): 80 B
+constexpr int kWaveLds = kD * kVtStr;  // elements per wave region
+
+struct DecodeParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* bt;
+  const int32_t* seq_lens;
+  float* part_o;
+  float* part_m;
+  float* part_l;
+  int max_pages, page_size, num_pages;
+  int s_max;
+  int B, h, h_kv, g;
+  int chunk, max_splits;
+  float c;     // scale * log2(e)
+};
+
+// Max of x over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float max_rows16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, x), false, false);
+  x = fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+  return max_halves(x);
+}
+__device__ __forceinline__ float sum_rows16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, x), false, false);
+  x = __builtin_bit_cast(float, r[0]) + __builtin_bit_cast(float, r[1]);
+  return sum_halves(x);
+}
+
+// Position of tile key kk (0..31) inside a V^T row: the A operand of lane
+// group a covers keys 4a..4a+3 and 16+4a..16+4a+3, stored contiguously.
+__device__ __forceinline__ int vt_pos(int kk) { return ((kk & 12) << 1) | ((kk & 16) >> 2) | (kk & 3); }
+
+template <int DT, bool PAGED>
+__global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
+  using E = Elem<DT>;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kWaves * kWaveLds];
+
+  const int split = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+  const int s_raw = p.seq_lens[b];
+  if (s_raw <= 0) return;
+  const int n_split = min(p.max_splits, (s_raw + p.chunk - 1) / p.chunk);
+  if (split >= n_split) return;
+  const int cap = PAGED ? p.max_pages * p.page_size : p.s_max;
+  const int s_len = min(s_raw, cap);
+  const int k_lo = split * p.chunk;
+  const int k_hi = split == p.max_splits - 1 ? s_len : min(s_len, k_lo + p.chunk);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 15;   // query head inside the group
+  const int row = lane >> 4;   // 16-lane row 0..3
+
+  // Q^T as B operands: lane holds head col, d in [8*row + 32c, +8).
+  u32x4 qf[4];
+  {
+    const bool ok = col < p.g;
+    const uint16_t* qp = p.q + ((size_t)b * p.h + kvh * p.g + (ok ? col : 0)) * kD + row * 8;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qf[c] = ok ? load16(qp + c * 32) : u32x4{0, 0, 0, 0};
+  }
+
+  const long kstride = PAGED ? p.h_kv : 1;   // rows between consecutive keys
+
+  uint16_t* vt = lds + wave * kWaveLds;
+  f32x4 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = f32x4{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;   // replicated across the 4 rows after reduction
+
+  const int n_tiles = (k_hi - k_lo + kTile - 1) / kTile;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  for (int t = wave_u; t < n_tiles; t += kWaves) {
+    const int kt = k_lo + t * kTile;
+    // Each 16-key block lies inside one page (pages hold a multiple of 16
+    // keys and blocks start at multiples of 16): resolve its row once.
+    long rbase[2];
+    bool bok[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key0 = kt + kb * 16;
+      bok[kb] = key0 < k_hi;
+      if (PAGED) {
+        int page = bok[kb] ? p.bt[(size_t)b * p.max_pages + key0 / p.page_size] : 0;
+        page = __builtin_amdgcn_readfirstlane(page);
+        bok[kb] = bok[kb] && page >= 0 && page < p.num_pages;
+        rbase[kb] = ((long)(bok[kb] ? page : 0) * p.page_size + key0 % p.page_size) * p.h_kv + kvh;
+      } else {
+        rbase[kb] = ((long)b * p.h_kv + kvh) * p.s_max + key0;
+      }
+    }
+    // K: lane loads key 16kb + col, d-chunks 8*row + 32c.
+    u32x4 kf[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bool ok = bok[kb] && kt + kb * 16 + col < k_hi;
+      const uint16_t* kp = p.k + (rbase[kb] + (ok ? col : 0) * kstride) * kD + row * 8;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) kf[kb][c] = ok ? load16(kp + c * 32) : u32x4{0, 0, 0, 0};
+    }
+    // V: lane (d-chunk col, key group row) loads keys 4*row+i and 16+4*row+i.
+    u32x4 vf[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int kb = i >> 2;
+      const int ko = row * 4 + (i & 3);
+      const bool ok = bok[kb] && kt + kb * 16 + ko < k_hi;
+      vf[i] = ok ? load16(p.v + (rbase[kb] + ko * kstride) * kD + col * 8) : u32x4{0, 0, 0, 0};
+    }
+
+    f32x4 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x4{};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) s[kb] = E::mfma16(kf[kb][c], qf[c], s[kb]);
+    }
+    // Exclude keys outside [k_lo, k_hi) or on an invalid page: register r of
+    // block kb holds key kt + 16kb + 4row + r.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = bok[kb] && kt + kb * 16 + row * 4 + r < k_hi;
+        s[kb][r] = ok ? s[kb][r] : -INFINITY;
+      }
+    }
+
+    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    mx = max_rows16(mx);
+    const float m_new = fmaxf(m_run, mx * p.c);
+    const float base = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - base);
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float e = fast_exp2(__builtin_fmaf(s[kb][r], p.c, -base));
+        s[kb][r] = e;
+        rs += e;
+      }
+    }
+    l_run = l_run * alpha + sum_rows16(rs);
+    m_run = m_new;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] *= alpha;
+
+    // Stage V^T: lane (col = d-chunk, row = key group) writes 8 d-rows x 8 keys.
+    const int pos = vt_pos(row * 4);   // keys 4row..4row+3 -> pos..pos+3; 16+4row.. -> pos+4..
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int d = col * 8 + 2 * e;
+      store16(&vt[d * kVtStr + pos],
+              u32x4{pack_lo16(vf[0][e], vf[1][e]), pack_lo16(vf[2][e], vf[3][e]),
+                    pack_lo16(vf[4][e], vf[5][e]), pack_lo16(vf[6][e], vf[7][e])});
+      store16(&vt[(d + 1) * kVtStr + pos],
+              u32x4{pack_hi16(vf[0][e], vf[1][e]), pack_hi16(vf[2][e], vf[3][e]),
+                    pack_hi16(vf[4][e], vf[5][e]), pack_hi16(vf[6][e], vf[7][e])});
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    const u32x4 pf = u32x4{E::pack2(s[0][0], s[0][1]), E::pack2(s[0][2], s[0][3]),
+                           E::pack2(s[1][0], s[1][1]), E::pack2(s[1][2], s[1][3])};
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      acc[db] = E::mfma16(load16(&vt[(db * 16 + col) * kVtStr + row * 8]), pf, acc[db]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // Merge the 4 wave states through LDS (reusing the V^T regions).
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(lds);            // [wave][16 heads][128 d]
+  float* red_ml = red + kWaves * 16 * kD;                 // [wave][16][2]
+  // acc[db] lane (col, row) reg r: head col, d = 16db + 4row + r
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+    *reinterpret_cast<f32x4*>(&red[(wave * 16 + col) * kD + db * 16 + row * 4]) = acc[db];
+  if (row == 0) {
+    red_ml[(wave * 16 + col) * 2 + 0] = m_run;
+    red_ml[(wave * 16 + col) * 2 + 1] = l_run;
+  }
+  __syncthreads();
+
+  // 256 threads: head j = tid / 32 (+8 per pass), 4 d-values each.
+  for (int j = tid >> 5; j < p.g; j += 8) {
+    const int d = (tid & 31) * 4;
+    float mw[kWaves], m_all = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      mw[w] = red_ml[(w * 16 + j) * 2];
+      m_all = fmaxf(m_all, mw[w]);
+    }
+    f32x4 o = f32x4{};
+    float l_all = 0.f;
+    if (m_all != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float wt = fast_exp2(mw[w] - m_all);   // empty wave: 2^-inf = 0
+        l_all += wt * red_ml[(w * 16 + j) * 2 + 1];
+        o += wt * *reinterpret_cast<const f32x4*>(&red[(w * 16 + j) * kD + d]);
+      }
+    }
+    const size_t hs = (size_t)b * p.h + kvh * p.g + j;
+    *reinterpret_cast<f32x4*>(&p.part_o[(hs * p.max_splits + split) * kD + d]) = o;
+    if ((tid & 31) == 0) {
+      p.part_m[hs * p.max_splits + split] = m_all == -INFINITY ? -INFINITY : m_all * kLn2;
+      p.part_l[hs * p.max_splits + split] = l_all;
+    }
+  }
+}
+
+template <int DT>
+hipError_t dispatch_decode(const DecodeParams& p, bool paged, hipStream_t stream) {
+  const dim3 grid((unsigned)p.max_splits, (unsigned)p.h_kv, (unsigned)p.B);
+  if (paged)
+    hipLaunchKernelGGL((decode_split_kernel<DT, true>), grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<DT, false>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t decode_split(const void* q, const void* k, const void* v, const int32_t* block_table,
+                        int max_pages, int page_size, int num_pages, const int32_t* seq_lens,
+                        int s_max, int B, int h, int h_kv, int chunk_keys, int max_splits,
+                        int dtype, float scale, float* part_o, float* part_m, float* part_l,
+                        hipStream_t stream) {
+  DecodeParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.bt = block_table;
+  p.seq_lens = seq_lens;
+  p.part_o = part_o;
+  p.part_m = part_m;
+  p.part_l = part_l;
+  p.max_pages = max_pages;
+  p.page_size = page_size;
+  p.num_pages = num_pages;
+  p.s_max = s_max;
+  p.B = B;
+  p.h = h;
+  p.h_kv = h_kv;
+  p.g = h / h_kv;
+  p.chunk = chunk_keys;
+  p.max_splits = max_splits;
+  p.c = scale * kLog2e;
+  if (B == 0 || h == 0) return hipSuccess;
+  if (dtype == ATTN_DTYPE_BF16) return dispatch_decode<ATTN_DTYPE_BF16>(p, block_table != nullptr, stream);
+  return dispatch_decode<ATTN_DTYPE_F16>(p, block_table != nullptr, stream);
+}
+
+// Split plan. The unsplit grid has B * h_kv workgroups; the split count that
+// first fills the machine is ceil(num_cus / (B * h_kv)) ("Decode attention:
+// FlashDecoding, split-K, paged kernels", section "The grid"). Here the key
+// slice length is chosen instead, so ragged batches are balanced too: aim at
+// about 16 workgroups per CU of total work (several per CU keep enough loads
+// in flight and even out ragged lengths), never below 128 keys per slice
+// unless that is needed to reach one workgroup per CU, never below 64.
+int decode_plan(int B, const int32_t* seq_lens, int h_kv, int num_cus, int32_t* chunk_keys,
+                int32_t* max_splits) {
+  long total = 0;
+  int s_max = 0;
+  for (int b = 0; b < B; ++b) {
+    total += seq_lens[b];
+    s_max = seq_lens[b] > s_max ? seq_lens[b] : s_max;
+  }
+  auto units = [&](long chunk) {
+    long u = 0;
+    for (int b = 0; b < B; ++b) u += (seq_lens[b] + chunk - 1) / chunk;
+    return u * h_kv;
+  };
+  const long target = 16L * num_cus;
+  long chunk = (total * h_kv + target - 1) / target;
+  chunk = ((chunk + 63) / 64) * 64;
+  if (chunk < 128) chunk = 128;
+  while (chunk > 64 && units(chunk) < num_cus) chunk -= 64;
+  if (chunk < 64) chunk = 64;
+  *chunk_keys = (int32_t)chunk;
+  long ms = (s_max + chunk - 1) / chunk;
+  *max_splits = (int32_t)(ms < 1 ? 1 : ms);
+  return 0;
+}
+
+}  // namespace attn

@@ -1,0 +1,196 @@
+"""C-ABI tests that need no GPU: the library loads, exports every symbol the
+header declares, rejects bad arguments before launching anything, and plans
+decode splits (host-only logic) consistently with the pages' arithmetic."""
+
+import ctypes
+import json
+import math
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from tests.conftest import ROOT, load_golden
+
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from online_softmax_tiled_amd import api
+    if not os.path.exists(api.LIB_PATH):
+        from online_softmax_tiled_amd.build import build
+        build()
+    return api.load()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(attn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    syms = declared_symbols()
+    for name in ("attn_prefill_fwd", "attn_decode_plan", "attn_decode_split", "attn_merge_states",
+                 "attn_paged_gather", "attn_last_error"):
+        assert name in syms
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from online_softmax_tiled_amd import api
+    out = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s(attn_\w+)$", out, re.M))
+    for name in declared_symbols():
+        assert name in exported, name
+        assert hasattr(lib, name)
+    assert set(api.EXPORTS) == set(declared_symbols())
+
+
+def test_one_hip_runtime_is_mapped(lib):
+    maps = open("/proc/self/maps").read()
+    paths = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(paths) == 1, paths
+
+
+def test_version_and_empty_error(lib):
+    from online_softmax_tiled_amd import api
+    assert "gfx950" in api.version()
+
+
+NULL = None
+
+
+def prefill_call(lib, **kw):
+    args = dict(q=1, k=1, v=1, km=NULL, rm=NULL, o=1, lse=NULL, B=1, h=4, h_kv=1, T_q=8, T_k=8,
+                d=128, dtype=1, scale=0.088, causal=1)
+    args.update(kw)
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.attn_prefill_fwd(p(args["q"]), p(args["k"]), p(args["v"]), p(args["km"]), p(args["rm"]),
+                                p(args["o"]), p(args["lse"]), args["B"], args["h"], args["h_kv"],
+                                args["T_q"], args["T_k"], args["d"], args["dtype"], args["scale"],
+                                args["causal"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(d=64), 2, "head size"),
+    (dict(dtype=5), 2, "dtype"),
+    (dict(h=6, h_kv=4), 1, "multiple"),
+    (dict(h_kv=0), 1, "positive"),
+    (dict(scale=0.0), 1, "scale"),
+    (dict(scale=float("nan")), 1, "scale"),
+    (dict(T_q=9, T_k=8, causal=1), 2, "T_q <= T_k"),
+    (dict(B=-1), 1, "negative"),
+    (dict(q=None), 1, "NULL"),
+    (dict(k=None), 1, "NULL"),
+])
+def test_prefill_rejects_before_launch(lib, kw, code, msg):
+    from online_softmax_tiled_amd import api
+    assert prefill_call(lib, **kw) == code
+    assert msg in api.last_error()
+
+
+def test_prefill_empty_problem_is_ok_without_launch(lib):
+    assert prefill_call(lib, B=0, q=None, k=None, v=None, o=None) == 0
+    assert prefill_call(lib, T_q=0, T_k=0, causal=0, q=None, k=None, v=None, o=None) == 0
+
+
+def split_call(lib, **kw):
+    args = dict(q=1, k=1, v=1, bt=NULL, max_pages=0, page_size=16, num_pages=0, sl=1, s_max=64, B=1,
+                h=8, h_kv=1, d=128, chunk=64, splits=1, dtype=1, scale=0.088, po=1, pm=1, pl=1)
+    args.update(kw)
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.attn_decode_split(p(args["q"]), p(args["k"]), p(args["v"]), p(args["bt"]), args["max_pages"],
+                                 args["page_size"], args["num_pages"], p(args["sl"]), args["s_max"], args["B"],
+                                 args["h"], args["h_kv"], args["d"], args["chunk"], args["splits"],
+                                 args["dtype"], args["scale"], p(args["po"]), p(args["pm"]), p(args["pl"]), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(h=34, h_kv=2), 2),               # 17 query heads per KV head
+    (dict(chunk=40), 1),                   # not a multiple of 16
+    (dict(chunk=0), 1),
+    (dict(splits=0), 1),
+    (dict(bt=1, page_size=8, max_pages=4, num_pages=4), 2),   # page not a multiple of 16
+    (dict(bt=1, page_size=16, max_pages=0, num_pages=4), 1),
+    (dict(pm=None), 1),
+    (dict(d=96), 2),
+])
+def test_decode_split_rejects_before_launch(lib, kw, code):
+    assert split_call(lib, **kw) == code
+
+
+def test_merge_and_gather_reject_before_launch(lib):
+    p = ctypes.c_void_p
+    assert lib.attn_merge_states(p(1), p(1), p(1), p(1), 0, 1, 8, 4, 128, p(1), None, 1, None) == 1
+    assert lib.attn_merge_states(p(1), p(1), p(1), p(1), 64, 1, 8, 0, 128, p(1), None, 1, None) == 1
+    assert lib.attn_merge_states(p(1), None, p(1), p(1), 64, 1, 8, 4, 128, p(1), None, 1, None) == 1
+    assert lib.attn_merge_states(p(1), p(1), p(1), p(1), 64, 1, 8, 4, 64, p(1), None, 1, None) == 2
+    assert lib.attn_paged_gather(p(1), p(1), p(1), 1, 8, 128, 0, 4, 4, 64, 1, p(1), None) == 1
+    assert lib.attn_paged_gather(p(1), None, p(1), 1, 8, 128, 16, 4, 4, 64, 1, p(1), None) == 1
+    assert lib.attn_paged_gather(p(1), p(1), p(1), 1, 8, 128, 16, 4, 4, 64, 3, p(1), None) == 2
+
+
+# ---------------------------------------------------------------- decode plan
+
+def plan(lens, h, h_kv, cus):
+    from online_softmax_tiled_amd import api
+    return api.decode_plan(lens, h, h_kv, num_cus=cus)
+
+
+def test_plan_reaches_first_wave_split_count_of_the_pages(lib):
+    # "The grid": S* = ceil(N_SM / G_2D); at batch 1 the unsplit grid is one
+    # workgroup per KV head here, and the plan must give at least S* splits.
+    g = load_golden("decode_shape_arithmetic.json")
+    for case, h, h_kv in zip(g["first_wave_splits"], (32, 8), (8, 1)):
+        assert case["unsplit_grid"] == h_kv
+        s_star = math.ceil(case["num_sm"] / case["unsplit_grid"])
+        assert s_star == case["splits"]
+        for s in (2560, 8192, 32768):
+            chunk, splits = plan([s], h, h_kv, case["num_sm"])
+            if s >= s_star * 64:
+                assert math.ceil(s / chunk) >= s_star
+
+
+def test_plan_properties(lib):
+    rng = np.random.default_rng(0)
+    for _ in range(200):
+        B = int(rng.integers(1, 65))
+        h_kv = int(rng.choice([1, 2, 4, 8]))
+        lens = rng.integers(0, 40000, size=B)
+        cus = int(rng.choice([132, 256, 304]))
+        chunk, splits = plan(lens, h_kv * 4, h_kv, cus)
+        assert chunk % 64 == 0 and chunk >= 64
+        assert splits == max(1, math.ceil(int(lens.max()) / chunk))
+        units = h_kv * sum(math.ceil(int(s) / chunk) for s in lens)
+        if units < cus:       # only when the keys cannot fill the GPU
+            assert chunk == 64
+        assert plan(lens, h_kv * 4, h_kv, cus) == (chunk, splits)      # deterministic
+
+
+def test_plan_on_the_measured_workloads(lib):
+    # 70B TP8 shard, batch 1, 32768 keys on 256 CUs: one slice per CU.
+    assert plan([32768], 8, 1, 256) == (128, 256)
+    # 64 ragged sequences at Llama-3-8B shape: thousands of slices, <=16 per sequence.
+    rng = np.random.default_rng(1004)
+    lens = rng.integers(512, 16384, size=64, endpoint=True)
+    chunk, splits = plan(lens, 32, 8, 256)
+    units = 8 * sum(math.ceil(int(s) / chunk) for s in lens)
+    assert units >= 16 * 256 * 0.9 and splits <= 16
+
+
+def test_plan_rejects_bad_input(lib):
+    from online_softmax_tiled_amd import api
+    with pytest.raises(api.AttnError):
+        plan([-1], 8, 1, 256)
+    with pytest.raises(api.AttnError):
+        plan([10], 8, 1, 0)
+    with pytest.raises(api.AttnError):
+        plan([10], 8, 3, 256)
+
+
+def test_partial_state_bytes_arithmetic():
+    # "What the merge costs": S (d_h + 2) 4 bytes per token-head.
+    g = load_golden("decode_shape_arithmetic.json")["partial_bytes_per_token_head"]
+    assert g["splits"] * (g["head_dim"] + 2) * 4 == g["bytes"]

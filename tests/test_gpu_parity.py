@@ -1,0 +1,297 @@
+"""GPU parity: every kernel, called through the C ABI, against the float64
+oracle on the same seeded inputs.
+
+Tolerances (max abs error on outputs; LSE relative error |d| / max(1, |LSE|)):
+fp16 outputs 2e-3, bf16 outputs 1e-2, LSE 1e-4; the paged gather and the
+outputs of rows with no visible key (+0.0 bits, LSE -inf) are bit-exact.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import (attention_ref, decode_ref, finalize_ref, merge_partials_ref, paged_gather_ref,
+                    split_states_ref)
+from online_softmax_tiled_amd import api
+from online_softmax_tiled_amd.workloads import make_config, make_decode, make_prefill
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f16": 2e-3, "bf16": 1e-2}
+LSE_TOL = 1e-4
+DEV = torch.device("cuda:0")
+
+
+def to_dev(x):
+    if x is None:
+        return None
+    if isinstance(x, np.ndarray):
+        x = torch.from_numpy(np.ascontiguousarray(x))
+    return x.to(DEV).contiguous()
+
+
+def lse_rel(a, b):
+    return np.abs(a - b) / np.maximum(1.0, np.abs(b))
+
+
+def assert_outputs(o_gpu_t, lse_gpu, o_ref, lse_ref, dtype, what):
+    """o_gpu_t: torch output (any leading shape, last dim d); refs float64."""
+    o_gpu = o_gpu_t.float().cpu().numpy().astype(np.float64)
+    empty = np.isneginf(lse_ref)
+    err = float(np.max(np.abs(o_gpu - o_ref))) if o_ref.size else 0.0
+    assert err <= TOL[dtype], f"{what}: max abs err {err:.3e} > {TOL[dtype]}"
+    if lse_gpu is not None:
+        assert np.array_equal(np.isneginf(lse_gpu), empty), f"{what}: empty-row LSE mismatch"
+        fin = ~empty
+        if fin.any():
+            rel = float(lse_rel(lse_gpu[fin], lse_ref[fin]).max())
+            assert rel <= LSE_TOL, f"{what}: LSE rel err {rel:.3e}"
+    if empty.any():
+        bits = o_gpu_t.view(torch.int16).cpu().numpy()
+        assert np.all(bits[empty] == 0), f"{what}: empty rows are not +0.0 bits"
+    return err
+
+
+# ------------------------------------------------------------------ prefill
+
+def run_prefill(inp, rows=None):
+    o, lse = api.prefill(to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"]), causal=inp["causal"],
+                         scale=inp["scale"], key_mask=to_dev(inp["key_mask"]),
+                         row_mask=to_dev(inp["row_mask"]))
+    torch.cuda.synchronize()
+    o_ref, lse_ref = attention_ref(inp["q"], inp["k"], inp["v"], inp["scale"], inp["causal"],
+                                   inp["key_mask"], inp["row_mask"], rows=rows)
+    lse_g = lse.cpu().numpy().astype(np.float64)
+    if rows is not None:
+        o = o[:, :, torch.from_numpy(np.asarray(rows)).to(DEV)]
+        lse_g = lse_g[:, :, rows]
+    return o, lse_g, o_ref, lse_ref
+
+
+def test_prefill_tiny_config():
+    inp = make_config("tiny_prefill")
+    o, lse, o_ref, lse_ref = run_prefill(inp)
+    assert_outputs(o, lse, o_ref, lse_ref, "f16", "tiny prefill")
+
+
+@pytest.mark.parametrize("B,h,h_kv,T_q,T_k,dtype,causal", [
+    (1, 4, 1, 1, 1, "bf16", True),
+    (1, 4, 1, 33, 33, "bf16", True),
+    (2, 8, 2, 100, 100, "f16", True),
+    (1, 8, 8, 70, 70, "bf16", True),       # g = 1
+    (1, 8, 4, 64, 200, "bf16", True),      # g = 2, T_q < T_k (bottom-right)
+    (1, 16, 2, 96, 96, "bf16", False),     # g = 8, no mask
+    (2, 4, 1, 130, 257, "f16", False),
+    (1, 32, 8, 300, 300, "bf16", True),
+])
+def test_prefill_shapes(B, h, h_kv, T_q, T_k, dtype, causal):
+    inp = make_prefill(B, h, h_kv, T_q, T_k, 128, dtype, seed=T_q * 7 + T_k + h, causal=causal)
+    o, lse, o_ref, lse_ref = run_prefill(inp)
+    assert_outputs(o, lse, o_ref, lse_ref, dtype, f"prefill {B}x{h}/{h_kv} {T_q}x{T_k}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_prefill_masks_and_empty_rows(dtype):
+    # per-key mask, tile masks, masked rows, and rows left empty by masked
+    # early tiles under the causal mask
+    inp = make_prefill(2, 8, 2, 200, 200, 128, dtype, seed=5, causal=True, key_tile=64,
+                       key_tile_p=0.3, key_p=0.2, row_mask_count=7)
+    inp["key_mask"][0, :70] = 0          # rows 0..69 of batch 0 see nothing
+    inp["key_mask"][1, 128:192] = 0
+    o, lse, o_ref, lse_ref = run_prefill(inp)
+    assert np.isneginf(lse_ref[0, :, :70]).all()
+    assert_outputs(o, lse, o_ref, lse_ref, dtype, "masked prefill")
+
+
+def test_prefill_all_keys_masked():
+    inp = make_prefill(1, 4, 1, 40, 40, 128, "bf16", seed=6, causal=False)
+    inp["key_mask"] = np.zeros((1, 40), dtype=np.uint8)
+    o, lse, o_ref, lse_ref = run_prefill(inp)
+    assert np.isneginf(lse).all()
+    assert_outputs(o, lse, o_ref, lse_ref, "bf16", "all keys masked")
+
+
+def test_prefill_stress_config_reduced():
+    inp = make_config("stress_prefill_t4096", T_q=1024, T_k=1024)
+    o, lse, o_ref, lse_ref = run_prefill(inp)
+    assert_outputs(o, lse, o_ref, lse_ref, "bf16", "stress prefill T=1024")
+
+
+def test_prefill_stress_config_full():
+    inp = make_config("stress_prefill_t4096")
+    o, lse, o_ref, lse_ref = run_prefill(inp)
+    assert np.isneginf(lse_ref).any()
+    assert_outputs(o, lse, o_ref, lse_ref, "bf16", "stress prefill T=4096")
+
+
+def test_prefill_llama3_8b_t8192_sampled_rows():
+    inp = make_config("llama3_8b_prefill_t8192")
+    rng = np.random.default_rng(2)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 63, 64, 4095, 8190, 8191],
+                                     rng.choice(8192, 55, replace=False)]))
+    o, lse, o_ref, lse_ref = run_prefill(inp, rows=rows)
+    assert_outputs(o, lse, o_ref, lse_ref, "bf16", "llama3-8b prefill T=8192 (sampled rows)")
+
+
+def test_prefill_causal_single_key_row_is_exact():
+    # row 0 under a causal mask sees only key 0: its output is v_0 exactly
+    inp = make_prefill(1, 8, 2, 64, 64, 128, "bf16", seed=8, causal=True)
+    o, lse = api.prefill(to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"]), causal=True,
+                         scale=inp["scale"])
+    torch.cuda.synchronize()
+    for i in range(8):
+        assert torch.equal(o[0, i, 0].cpu(), inp["v"][0, i // 4, 0])
+
+
+# ------------------------------------------------------------------ gather
+
+@pytest.mark.parametrize("page_size,spare", [(16, 0), (16, 5), (32, 3), (48, 1)])
+def test_paged_gather_bit_exact(page_size, spare):
+    dec = make_decode(B=6, h=8, h_kv=2, d=128, dtype="bf16", seed=page_size + spare,
+                      len_range=(1, 300), paged=True, page_size=page_size, spare_pages=spare)
+    dec["seq_lens"][2] = 0
+    s_max = int(dec["seq_lens"].max()) + 5
+    sentinel = torch.full((6, 2, s_max, 128), -7.0, dtype=torch.bfloat16)
+    out = api.paged_gather(to_dev(dec["k_pool"]), to_dev(dec["block_table"]), to_dev(dec["seq_lens"]),
+                           s_max, out=to_dev(sentinel.clone()))
+    torch.cuda.synchronize()
+    ref = paged_gather_ref(dec["k_pool"], dec["block_table"], dec["seq_lens"], s_max, out=sentinel.clone())
+    assert torch.equal(out.cpu().view(torch.int16), ref.view(torch.int16))
+    for b in range(6):
+        s = int(dec["seq_lens"][b])
+        assert torch.equal(out[b, :, :s].cpu(), dec["k_seqs"][b])
+
+
+@pytest.fixture(scope="module")
+def paged_llama():
+    return make_config("paged_decode_llama3_8b_b64")
+
+
+def test_paged_gather_llama3_8b_b64_full(paged_llama):
+    dec = paged_llama
+    s_max = int(dec["seq_lens"].max())
+    bt, sl = to_dev(dec["block_table"]), to_dev(dec["seq_lens"])
+    for pool, seqs in ((dec["k_pool"], dec["k_seqs"]), (dec["v_pool"], dec["v_seqs"])):
+        out = api.paged_gather(to_dev(pool), bt, sl, s_max)
+        torch.cuda.synchronize()
+        out = out.cpu()
+        for b in range(dec["B"]):
+            s = int(dec["seq_lens"][b])
+            assert torch.equal(out[b, :, :s].view(torch.int16), seqs[b].reshape(8, s, 128).view(torch.int16))
+        del out
+
+
+# ------------------------------------------------------------------ merge
+
+def test_merge_on_oracle_partials():
+    rng = np.random.default_rng(9)
+    B, h, h_kv, S, chunk = 5, 8, 2, 6, 64
+    lens = np.array([0, 1, 64, 200, 384], dtype=np.int32)
+    q = rng.normal(size=(B, h, 128))
+    po = np.full((B, h, S, 128), np.nan, dtype=np.float32)     # unused slots poisoned
+    pm = np.full((B, h, S), np.nan, dtype=np.float32)
+    pl = np.full((B, h, S), np.nan, dtype=np.float32)
+    o_ref = np.zeros((B, h, 128))
+    lse_ref = np.full((B, h), -np.inf)
+    for b in range(B):
+        s = int(lens[b])
+        k = rng.normal(size=(h_kv, s, 128)) * 2
+        v = rng.normal(size=(h_kv, s, 128))
+        m, l, a = split_states_ref(q[b], k, v, s, 0.25, chunk)
+        n = m.shape[1]
+        if b == 3:                       # make one split empty
+            m[:, 1], l[:, 1], a[:, 1] = -np.inf, 0.0, 0.0
+        po[b, :, :n], pm[b, :, :n], pl[b, :, :n] = a, m, l
+        for i in range(h):
+            o_ref[b, i], lse_ref[b, i] = merge_partials_ref(po[b, i, :n], pm[b, i, :n], pl[b, i, :n])
+    o, lse = api.merge_states(to_dev(po), to_dev(pm), to_dev(pl), to_dev(lens), chunk, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert_outputs(o, lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16", "merge")
+    of, lf = api.merge_states(to_dev(po), to_dev(pm), to_dev(pl), to_dev(lens), chunk, torch.float16)
+    torch.cuda.synchronize()
+    assert_outputs(of, lf.cpu().numpy().astype(np.float64), o_ref, lse_ref, "f16", "merge f16")
+
+
+def test_merge_many_splits():
+    rng = np.random.default_rng(10)
+    B, h, S = 1, 8, 256
+    m = rng.normal(0, 20, size=(B, h, S)).astype(np.float32)
+    l = (rng.random((B, h, S)) * 30 + 1).astype(np.float32)
+    a = (rng.normal(size=(B, h, S, 128)) * l[..., None]).astype(np.float32)
+    lens = np.array([S * 128], dtype=np.int32)
+    o, lse = api.merge_states(to_dev(a), to_dev(m), to_dev(l), to_dev(lens), 128, torch.float16)
+    torch.cuda.synchronize()
+    o_ref = np.zeros((B, h, 128))
+    lse_ref = np.zeros((B, h))
+    for i in range(h):
+        o_ref[0, i], lse_ref[0, i] = merge_partials_ref(m[0, i], l[0, i], a[0, i])
+    assert_outputs(o, lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "f16", "merge 256 splits")
+
+
+# ------------------------------------------------------------------ decode
+
+def run_decode(dec, plan=None):
+    paged = dec["paged"]
+    q = to_dev(dec["q"])
+    sl = to_dev(dec["seq_lens"])
+    if paged:
+        k, v, bt = to_dev(dec["k_pool"]), to_dev(dec["v_pool"]), to_dev(dec["block_table"])
+        ps = dec["page_size"]
+    else:
+        k, v, bt, ps = to_dev(dec["k"]), to_dev(dec["v"]), None, 16
+    o, lse, plan = api.decode(q, k, v, sl, seq_lens_host=dec["seq_lens"], block_table=bt, page_size=ps,
+                              scale=dec["scale"], plan=plan)
+    torch.cuda.synchronize()
+    return o, lse.cpu().numpy().astype(np.float64), plan
+
+
+@pytest.mark.parametrize("paged,page_size", [(False, 16), (True, 16), (True, 32)])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_decode_small(paged, page_size, dtype):
+    lens = [1, 5, 16, 17, 63, 64, 65, 300, 1000, 0]
+    dec = make_decode(B=len(lens), h=16, h_kv=4, d=128, dtype=dtype, seed=11 + page_size, seq_lens=lens,
+                      paged=paged, page_size=page_size, spare_pages=3)
+    o_ref, lse_ref = decode_ref(dec["q"], dec["k_seqs"], dec["v_seqs"], dec["seq_lens"], dec["scale"])
+    for plan in (None, (64, 16), (1024, 1), (64, 2)):     # includes last split taking the rest
+        o, lse, used = run_decode(dec, plan)
+        assert_outputs(o, lse, o_ref, lse_ref, dtype, f"decode paged={paged} plan={used}")
+
+
+def test_decode_split_partials_match_slices():
+    dec = make_decode(B=2, h=8, h_kv=1, d=128, dtype="bf16", seed=12, seq_lens=[700, 129], paged=False)
+    chunk, S = 128, 6
+    po, pm, pl = api.decode_split(to_dev(dec["q"]), to_dev(dec["k"]), to_dev(dec["v"]), to_dev(dec["seq_lens"]),
+                                  chunk, S, scale=dec["scale"])
+    torch.cuda.synchronize()
+    po, pm, pl = po.cpu().numpy(), pm.cpu().numpy(), pl.cpu().numpy()
+    for b in range(2):
+        s = int(dec["seq_lens"][b])
+        qb = dec["q"][b].double().numpy()
+        kb = dec["k_seqs"][b].double().numpy()
+        vb = dec["v_seqs"][b].double().numpy()
+        m, l, a = split_states_ref(qb, kb, vb, s, dec["scale"], chunk)
+        n = min(S, math.ceil(s / chunk))
+        for i in range(8):
+            for sp in range(n):
+                o_g, lse_g = finalize_ref((float(pm[b, i, sp]), float(pl[b, i, sp]), po[b, i, sp].astype(np.float64)))
+                o_r, lse_r = finalize_ref((m[i, sp], l[i, sp], a[i, sp]))
+                assert np.max(np.abs(o_g - o_r)) < 1e-2
+                assert abs(lse_g - lse_r) / max(1.0, abs(lse_r)) < LSE_TOL
+                assert abs(float(pm[b, i, sp]) - m[i, sp]) < 1e-4 * max(1.0, abs(m[i, sp]))
+
+
+def test_decode_70b_tp8_s32768():
+    dec = make_config("decode_70b_tp8_s32768")
+    o_ref, lse_ref = decode_ref(dec["q"], dec["k_seqs"], dec["v_seqs"], dec["seq_lens"], dec["scale"])
+    for plan in (None, (32768, 1), (64, 512)):
+        o, lse, used = run_decode(dec, plan)
+        assert_outputs(o, lse, o_ref, lse_ref, "bf16", f"70b-tp8 decode plan={used}")
+
+
+def test_decode_llama3_8b_b64_paged(paged_llama):
+    dec = paged_llama
+    o_ref, lse_ref = decode_ref(dec["q"], dec["k_seqs"], dec["v_seqs"], dec["seq_lens"], dec["scale"])
+    o, lse, used = run_decode(dec)
+    assert_outputs(o, lse, o_ref, lse_ref, "bf16", f"paged decode B=64 plan={used}")
