@@ -17,7 +17,8 @@ Also reported, on the same line:
   gather as GB/s moved;
 * ``prefill_other``: the tiny and the numerics-stress prefill shapes;
 * ``cpu_baseline``: the float64 oracle timed on the host CPU on a bounded
-  sample of the same prefill workload (a slice of query rows of one head).
+  sample of the same prefill workload (blocks of random query rows, about
+  15 s of oracle time).
 
 ``python bench.py --gpus N --steps K --warmup W``. Only one GPU is used; N > 1
 exits with a message.
@@ -67,11 +68,12 @@ def visible_pairs(inp):
 
 
 def time_loop(fn, steps, warmup):
-    """Mean ms per call: HIP events on torch's current stream (the stream the
-    library launches on), bracketed by device synchronisations."""
+    """Mean ms per call of eager launches: HIP events on torch's current
+    stream (the stream the library launches on), bracketed by device
+    synchronisations."""
     import torch
-    for _ in range(warmup):
-        fn()
+    for i in range(warmup):
+        fn(i)
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -83,6 +85,35 @@ def time_loop(fn, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall
     return t0.elapsed_time(t1) / steps, wall
+
+
+def time_graph(fn, steps, reps=5):
+    """Mean ms per call when ``steps`` calls are captured in one HIP graph and
+    the graph is replayed ``reps`` times: the device time of the kernels and
+    the gaps between them, without the host's per-call launch cost."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            fn(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / (reps * steps)
+    del graph
+    return ms
 
 
 def bench_prefill(name, steps, warmup, dev):
@@ -133,12 +164,14 @@ def bench_decode_contiguous(steps, warmup, dev, copies=40):
         split_only(i)
         api.merge_states(po, pm, pl, sl, chunk, q.dtype, out=o, lse=lse)
 
-    ms_split, _ = time_loop(split_only, steps, warmup)
-    ms, _ = time_loop(full, steps, warmup)
+    ms_eager, _ = time_loop(full, steps, warmup)
+    ms_split = time_graph(split_only, copies * 5)
+    ms = time_graph(full, copies * 5)
     return dict(workload="decode_70b_tp8_s32768", kv_bytes=kv_bytes, us_per_step=ms * 1e3,
-                split_us=ms_split * 1e3, gbs=kv_bytes / (ms * 1e-3) / 1e9,
+                split_us=ms_split * 1e3, eager_us_per_step=ms_eager * 1e3,
+                gbs=kv_bytes / (ms * 1e-3) / 1e9,
                 frac_hbm=kv_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, plan=[chunk, splits],
-                rotated_kv_copies=copies)
+                rotated_kv_copies=copies, timing="HIP graph of split+merge steps, replayed")
 
 
 def bench_decode_paged(steps, warmup, dev, dec):
@@ -168,6 +201,7 @@ def bench_decode_paged(steps, warmup, dev, dec):
 
     ms_split, _ = time_loop(split_only, steps, warmup)
     ms, _ = time_loop(full, steps, warmup)
+    ms_graph = time_graph(full, 10, reps=2)
     s_max = int(dec["seq_lens"].max())
     gout = torch.empty((B, h_kv, s_max, d), dtype=q.dtype, device=dev)
 
@@ -178,32 +212,36 @@ def bench_decode_paged(steps, warmup, dev, dec):
     del gout
     gather_bytes = kv_bytes  # K pool rows read + the same bytes written (one pool)
     return dict(workload="paged_decode_llama3_8b_b64", kv_bytes=kv_bytes, us_per_step=ms * 1e3,
-                split_us=ms_split * 1e3, gbs=kv_bytes / (ms * 1e-3) / 1e9,
+                split_us=ms_split * 1e3, graph_us_per_step=ms_graph * 1e3,
+                gbs=kv_bytes / (ms * 1e-3) / 1e9,
                 frac_hbm=kv_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, plan=[chunk, splits],
                 gather_us=ms_g * 1e3, gather_gbs=gather_bytes / (ms_g * 1e-3) / 1e9)
 
 
 def cpu_baseline(inp, budget_s=15.0):
     """The float64 oracle on the host CPU over a bounded sample of the prefill
-    workload: query rows of head 0, growing until about budget_s seconds."""
+    workload: blocks of 256 random query rows, one query head at a time, until
+    about budget_s seconds of oracle time have been spent."""
     import threadpoolctl
     from oracle import attention_ref
     threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
-    t_q = inp["T_q"]
-    rows_n, total_rows, total_flop, total_t = 64, 0, 0.0, 0.0
+    t_q, g = inp["T_q"], inp["h"] // inp["h_kv"]
     rng = np.random.default_rng(0)
-    q1 = inp["q"][:, :1]
-    while total_t < budget_s and total_rows < t_q:
-        rows = np.sort(rng.choice(t_q, size=min(rows_n, t_q), replace=False))
+    heads = rows_total = 0
+    flop = spent = 0.0
+    while spent < budget_s and rows_total < 64 * t_q:
+        i = heads % inp["h"]
+        rows = np.sort(rng.choice(t_q, size=min(256, t_q), replace=False))
         t = time.perf_counter()
-        attention_ref(q1, inp["k"][:, :1], inp["v"][:, :1], inp["scale"], inp["causal"], rows=rows)
-        total_t += time.perf_counter() - t
-        total_flop += 4.0 * HEAD_DIM * float(np.minimum(rows + 1, inp["T_k"]).sum())
-        total_rows += rows.size
-        rows_n *= 2
-    return dict(value=total_flop / total_t / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
-                sample=f"{total_rows} random query rows of head 0 of the T=8192 causal prefill "
-                       f"(float64 numpy, materialised), {total_t:.1f} s")
+        attention_ref(inp["q"][:, i:i + 1], inp["k"][:, i // g:i // g + 1], inp["v"][:, i // g:i // g + 1],
+                      inp["scale"], inp["causal"], rows=rows)
+        spent += time.perf_counter() - t
+        flop += 4.0 * HEAD_DIM * float(np.minimum(rows + 1, inp["T_k"]).sum())
+        rows_total += rows.size
+        heads += 1
+    return dict(value=flop / spent / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
+                sample=f"{rows_total} random query rows ({heads} blocks of 256, cycling over the heads) of the T=8192 causal "
+                       f"prefill, float64 numpy materialised attention, {spent:.1f} s of oracle time")
 
 
 def main():

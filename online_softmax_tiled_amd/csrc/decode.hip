@@ -55,18 +55,15 @@ struct DecodeParams {
   float c;     // scale * log2(e)
 };
 
-// Max of x over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48).
+// Max / sum of x over the four 16-lane rows of a wave (lanes l, l^16,
+// l^32, l^48).
 __device__ __forceinline__ float max_rows16(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
-                                            __builtin_bit_cast(uint32_t, x), false, false);
-  x = fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
-  return max_halves(x);
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
 }
 __device__ __forceinline__ float sum_rows16(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
-                                            __builtin_bit_cast(uint32_t, x), false, false);
-  x = __builtin_bit_cast(float, r[0]) + __builtin_bit_cast(float, r[1]);
-  return sum_halves(x);
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
 }
 
 // Position of tile key kk (0..31) inside a V^T row: the A operand of lane

@@ -13,9 +13,12 @@
 // attention without averaging tile outputs", paragraph on fully masked
 // tiles).
 //
-// One workgroup of 256 threads per (sequence, head): 8 groups of 32 threads
-// take every 8th split, each thread 4 consecutive d values; the 8 group sums
-// are combined through LDS.
+// Layout: one workgroup of 256 threads per (sequence, head, d-slice). With
+// many splits the head dimension is cut into ND = 4 slices so that more
+// workgroups share the partial traffic. Inside a workgroup, thread (s, f)
+// of SL split lanes x FL float4 lanes sums splits s, s + SL, ... for 4
+// consecutive d values, with the loads of 4 splits in flight at a time; the
+// SL partial sums are then added through LDS.
 #include "common.h"
 
 namespace attn {
@@ -39,14 +42,20 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
-template <int DT>
+// ND: d-slices per (sequence, head); each slice is kD / ND values, handled
+// by FL = kD / ND / 4 float4 lanes and SL = 256 / FL split lanes.
+template <int DT, int ND>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   using E = Elem<DT>;
+  constexpr int kSlice = kD / ND;
+  constexpr int FL = kSlice / 4;
+  constexpr int SL = 256 / FL;
   __shared__ float red_m[4];
-  __shared__ __attribute__((aligned(16))) float red_o[8][kD];
-  __shared__ float red_l[8];
+  __shared__ __attribute__((aligned(16))) float red_o[SL][kSlice];
+  __shared__ float red_l[SL];
 
   const int bh = blockIdx.x;
+  const int d0 = blockIdx.y * kSlice;
   const int b = bh / p.h;
   const int tid = threadIdx.x;
   const int s_len = p.seq_lens[b];
@@ -63,42 +72,66 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   __syncthreads();
   const float big = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
 
-  uint16_t* op = p.o + (size_t)bh * kD;
+  uint16_t* op = p.o + (size_t)bh * kD + d0;
   if (big == -INFINITY) {   // no visible key in any split: zero output
-    if (tid < kD / 2) reinterpret_cast<uint32_t*>(op)[tid] = 0u;
-    if (tid == 0 && p.lse != nullptr) p.lse[bh] = -INFINITY;
+    if (tid < kSlice / 2) reinterpret_cast<uint32_t*>(op)[tid] = 0u;
+    if (tid == 0 && blockIdx.y == 0 && p.lse != nullptr) p.lse[bh] = -INFINITY;
     return;
   }
 
-  const int grp = tid >> 5;
-  const int d = (tid & 31) * 4;
+  const int sl = tid / FL;
+  const int d = (tid % FL) * 4;
   f32x4 acc = f32x4{};
   float lacc = 0.f;
-  for (int i = grp; i < n; i += 8) {
-    const float li = p.part_l[base + i];
-    if (!(li > 0.f)) continue;
-    const float w = fast_exp2((p.part_m[base + i] - big) * kLog2e);
-    lacc += w * li;
-    acc += w * *reinterpret_cast<const f32x4*>(&p.part_o[(base + i) * kD + d]);
+  for (int i0 = sl; i0 < n; i0 += 4 * SL) {
+    float li[4], mi[4];
+    f32x4 oi[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * SL;
+      const bool ok = i < n;
+      li[u] = ok ? p.part_l[base + i] : 0.f;
+      mi[u] = ok ? p.part_m[base + i] : -INFINITY;
+      oi[u] = ok ? *reinterpret_cast<const f32x4*>(&p.part_o[(base + i) * kD + d0 + d]) : f32x4{};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (li[u] > 0.f) {
+        const float w = fast_exp2((mi[u] - big) * kLog2e);
+        lacc += w * li[u];
+        acc += w * oi[u];
+      }
+    }
   }
-  *reinterpret_cast<f32x4*>(&red_o[grp][d]) = acc;
-  if ((tid & 31) == 0) red_l[grp] = lacc;
+  *reinterpret_cast<f32x4*>(&red_o[sl][d]) = acc;
+  if (tid % FL == 0) red_l[sl] = lacc;
   __syncthreads();
-  if (tid < kD / 2) {
+  if (tid < kSlice / 2) {
     float l_all = 0.f;
 #pragma unroll
-    for (int gi = 0; gi < 8; ++gi) l_all += red_l[gi];
+    for (int s = 0; s < SL; ++s) l_all += red_l[s];
     const int dd = tid * 2;
     float o0 = 0.f, o1 = 0.f;
-#pragma unroll
-    for (int gi = 0; gi < 8; ++gi) {
-      o0 += red_o[gi][dd];
-      o1 += red_o[gi][dd + 1];
+#pragma unroll 8
+    for (int s = 0; s < SL; ++s) {
+      o0 += red_o[s][dd];
+      o1 += red_o[s][dd + 1];
     }
     const float inv = 1.f / l_all;
     reinterpret_cast<uint32_t*>(op)[tid] = E::pack2(o0 * inv, o1 * inv);
-    if (tid == 0 && p.lse != nullptr) p.lse[bh] = big + fast_log2(l_all) * kLn2;
+    if (tid == 0 && blockIdx.y == 0 && p.lse != nullptr) p.lse[bh] = big + fast_log2(l_all) * kLn2;
   }
+}
+
+template <int DT>
+hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
+  // Many splits and few (sequence, head) pairs: cut d into 4 slices.
+  if (p.max_splits >= 64 && (long)p.B * p.h < 1024) {
+    hipLaunchKernelGGL((merge_kernel<DT, 4>), dim3((unsigned)(p.B * p.h), 4), dim3(256), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((merge_kernel<DT, 1>), dim3((unsigned)(p.B * p.h), 1), dim3(256), 0, stream, p);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -108,12 +141,8 @@ hipError_t merge_states(const float* part_o, const float* part_m, const float* p
                         void* o, float* lse, int dtype, hipStream_t stream) {
   MergeParams p{part_o, part_m, part_l, seq_lens, static_cast<uint16_t*>(o), lse, B, h, max_splits, chunk_keys};
   if (B == 0 || h == 0) return hipSuccess;
-  const dim3 grid((unsigned)(B * h));
-  if (dtype == ATTN_DTYPE_BF16)
-    hipLaunchKernelGGL(merge_kernel<ATTN_DTYPE_BF16>, grid, dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL(merge_kernel<ATTN_DTYPE_F16>, grid, dim3(256), 0, stream, p);
-  return hipGetLastError();
+  if (dtype == ATTN_DTYPE_BF16) return launch_merge<ATTN_DTYPE_BF16>(p, stream);
+  return launch_merge<ATTN_DTYPE_F16>(p, stream);
 }
 
 }  // namespace attn

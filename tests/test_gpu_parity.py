@@ -4,6 +4,13 @@ oracle on the same seeded inputs.
 Tolerances (max abs error on outputs; LSE relative error |d| / max(1, |LSE|)):
 fp16 outputs 2e-3, bf16 outputs 1e-2, LSE 1e-4; the paged gather and the
 outputs of rows with no visible key (+0.0 bits, LSE -inf) are bit-exact.
+
+Where the output format itself cannot hold the absolute tolerance -- a bf16
+value in [4, 8) is stored with a spacing of 2^-5, so even the exact result
+rounded to nearest is up to 0.0156 away -- an element may exceed the
+tolerance only if it is a faithful rounding of the exact value (closer to it
+than one unit in the last place of the format). The logit-std-30 stress
+workload has such elements (|O| up to 5.1).
 """
 
 import math
@@ -20,6 +27,7 @@ from online_softmax_tiled_amd.workloads import make_config, make_decode, make_pr
 pytestmark = pytest.mark.gpu
 
 TOL = {"f16": 2e-3, "bf16": 1e-2}
+MANT_BITS = {"f16": 10, "bf16": 7}
 LSE_TOL = 1e-4
 DEV = torch.device("cuda:0")
 
@@ -40,8 +48,19 @@ def assert_outputs(o_gpu_t, lse_gpu, o_ref, lse_ref, dtype, what):
     """o_gpu_t: torch output (any leading shape, last dim d); refs float64."""
     o_gpu = o_gpu_t.float().cpu().numpy().astype(np.float64)
     empty = np.isneginf(lse_ref)
-    err = float(np.max(np.abs(o_gpu - o_ref))) if o_ref.size else 0.0
-    assert err <= TOL[dtype], f"{what}: max abs err {err:.3e} > {TOL[dtype]}"
+    diff = np.abs(o_gpu - o_ref)
+    err = float(np.max(diff)) if o_ref.size else 0.0
+    over = diff > TOL[dtype]
+    if over.any():
+        # allowed only where the format's spacing exceeds the tolerance and the
+        # output is a faithful rounding of the exact value
+        mag = np.abs(o_ref[over])
+        ulp = np.exp2(np.floor(np.log2(np.where(mag > 0, mag, 1.0))) - MANT_BITS[dtype])
+        half_ulp_too_big = ulp / 2 > TOL[dtype]
+        faithful = diff[over] < ulp
+        bad = ~(half_ulp_too_big & faithful)
+        assert not bad.any(), (f"{what}: max abs err {err:.3e} > {TOL[dtype]} "
+                               f"({int(bad.sum())} elements not explained by the output format)")
     if lse_gpu is not None:
         assert np.array_equal(np.isneginf(lse_gpu), empty), f"{what}: empty-row LSE mismatch"
         fin = ~empty
@@ -161,7 +180,7 @@ def test_paged_gather_bit_exact(page_size, spare):
     assert torch.equal(out.cpu().view(torch.int16), ref.view(torch.int16))
     for b in range(6):
         s = int(dec["seq_lens"][b])
-        assert torch.equal(out[b, :, :s].cpu(), dec["k_seqs"][b])
+        assert torch.equal(out[b, :, :s].cpu(), dec["k_seqs"][b][:, :s])
 
 
 @pytest.fixture(scope="module")
@@ -205,7 +224,7 @@ def test_merge_on_oracle_partials():
             m[:, 1], l[:, 1], a[:, 1] = -np.inf, 0.0, 0.0
         po[b, :, :n], pm[b, :, :n], pl[b, :, :n] = a, m, l
         for i in range(h):
-            o_ref[b, i], lse_ref[b, i] = merge_partials_ref(po[b, i, :n], pm[b, i, :n], pl[b, i, :n])
+            o_ref[b, i], lse_ref[b, i] = merge_partials_ref(pm[b, i, :n], pl[b, i, :n], po[b, i, :n])
     o, lse = api.merge_states(to_dev(po), to_dev(pm), to_dev(pl), to_dev(lens), chunk, torch.bfloat16)
     torch.cuda.synchronize()
     assert_outputs(o, lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16", "merge")
@@ -295,3 +314,49 @@ def test_decode_llama3_8b_b64_paged(paged_llama):
     o_ref, lse_ref = decode_ref(dec["q"], dec["k_seqs"], dec["v_seqs"], dec["seq_lens"], dec["scale"])
     o, lse, used = run_decode(dec)
     assert_outputs(o, lse, o_ref, lse_ref, "bf16", f"paged decode B=64 plan={used}")
+
+
+def test_decode_graph_replay_matches_eager():
+    # split + merge captured in one HIP graph; every replay, with eager work
+    # and synchronisations in between, must reproduce the eager result bit
+    # for bit (same kernels, same inputs).
+    dec = make_decode(B=4, h=16, h_kv=2, d=128, dtype="bf16", seed=21, seq_lens=[7, 640, 2000, 129],
+                      paged=True, page_size=16)
+    q, sl = to_dev(dec["q"]), to_dev(dec["seq_lens"])
+    kp, vp, bt = to_dev(dec["k_pool"]), to_dev(dec["v_pool"]), to_dev(dec["block_table"])
+    chunk, splits = api.decode_plan(dec["seq_lens"], 16, 2)
+    po = torch.empty((4, 16, splits, 128), dtype=torch.float32, device=DEV)
+    pm = torch.empty((4, 16, splits), dtype=torch.float32, device=DEV)
+    pl = torch.empty_like(pm)
+    o = torch.empty((4, 16, 128), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((4, 16), dtype=torch.float32, device=DEV)
+
+    def step():
+        api.decode_split(q, kp, vp, sl, chunk, splits, block_table=bt, scale=dec["scale"],
+                         part_o=po, part_m=pm, part_l=pl)
+        api.merge_states(po, pm, pl, sl, chunk, torch.bfloat16, out=o, lse=lse)
+
+    step()
+    torch.cuda.synchronize()
+    o_eager, lse_eager = o.clone(), lse.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(4):
+        o.fill_(1.0)
+        lse.fill_(0.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), o_eager.view(torch.int16)), rep
+        assert torch.equal(lse, lse_eager), rep
+        step()                              # eager work between replays
+        torch.cuda.synchronize()
+    o_ref, lse_ref = decode_ref(dec["q"], dec["k_seqs"], dec["v_seqs"], dec["seq_lens"], dec["scale"])
+    assert_outputs(o, lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16", "graph decode")
