@@ -39,6 +39,7 @@ namespace {
 
 constexpr int kHeadDim = 128;
 constexpr int kMaxGroup = 16;   // decode: query heads per KV head
+constexpr int kMaxSeq = 1 << 23;  // prefill: keys or queries per (batch, head)
 
 thread_local std::string g_last_error;
 
@@ -102,6 +103,9 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, const uint8_t*
           T_q, T_k);
   REQUIRE(!causal || T_q <= T_k, ATTN_ERR_UNSUPPORTED, "%s: causal attention needs T_q <= T_k (T_q=%d, T_k=%d)",
           fn, T_q, T_k);
+  // Tiles are addressed with 32-bit byte offsets inside one (batch, head) slab.
+  REQUIRE(T_q <= kMaxSeq && T_k <= kMaxSeq, ATTN_ERR_UNSUPPORTED, "%s: sequence longer than %d (T_q=%d, T_k=%d)", fn,
+          kMaxSeq, T_q, T_k);
   const long rows = (long)B * h * T_q;
   REQUIRE(rows * kHeadDim < (1L << 40), ATTN_ERR_INVALID, "%s: problem too large", fn);
   if (rows == 0) return ok();

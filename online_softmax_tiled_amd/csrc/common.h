@@ -56,6 +56,11 @@ struct Elem<ATTN_DTYPE_BF16> {
   static __device__ __forceinline__ float to_f32(uint16_t x) {
     return __builtin_bit_cast(float, (uint32_t)x << 16);
   }
+  // acc + lo + hi of a packed pair, in fp32 (v_dot2 with a (1, 1) operand).
+  static __device__ __forceinline__ float add_pair(uint32_t pair, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), __builtin_bit_cast(bf16x2, 0x3F803F80u),
+                                           acc, false);
+  }
 };
 
 template <>
@@ -75,6 +80,10 @@ struct Elem<ATTN_DTYPE_F16> {
   static __device__ __forceinline__ float to_f32(uint16_t x) {
     return (float)__builtin_bit_cast(_Float16, x);
   }
+  static __device__ __forceinline__ float add_pair(uint32_t pair, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), __builtin_bit_cast(f16x2, 0x3C003C00u), acc,
+                                  false);
+  }
 };
 
 // Byte select of v_perm_b32: result byte i = byte sel[i] of {hi:lo} (0-3 lo).
@@ -90,6 +99,25 @@ __device__ __forceinline__ float max_halves(float x) { return fmaxf(x, __shfl_xo
 __device__ __forceinline__ float sum_halves(float x) { return x + __shfl_xor(x, 32); }
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Buffer resource over [base, base + bytes): a raw buffer load past the end
+// returns zeros instead of touching memory, so tile loads need no branches.
+// Word 3 (0x00020000) is the CDNA default for untyped 32-bit data.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
+}
+
+// gfx950 transposing LDS read of four 16-bit elements. Within each group of
+// 16 lanes, result element k of lane i is element i % 4 of the 8 bytes that
+// lane 4k + i / 4 addresses.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
+}
 __device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ void store8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
 

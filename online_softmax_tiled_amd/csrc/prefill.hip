@@ -14,26 +14,40 @@
 //   blocks are numbered first.
 //
 // Per 64-key tile and wave
+//   K and V tiles are staged into LDS in their natural row-major layout with
+//   range-checked buffer loads (rows past T_k read as zeros), double
+//   buffered, one barrier per tile.
 //   S^T = K Q^T on v_mfma_f32_32x32x16 (A = K rows from LDS, B = the wave's
 //   Q rows held in VGPRs for the whole kernel). In the accumulator layout
 //   lane l holds query row l%32 and, for register r of 32-key block kb, key
-//   kb*32 + 8*(r/4) + 4*(l/32) + r%4. A row's 64 scores thus sit in one lane
-//   pair (l, l^32): the row max is an in-lane max plus one half swap.
-//   Online update in base 2: c = scale*log2(e), m' = max(m, c*max s),
-//   alpha = 2^(m - m'), p = 2^(c*s - m'), l = alpha*l + sum p, O~ *= alpha.
-//   While a row has seen no visible key (m' = -inf) the subtracted reference
-//   is 0 instead of m', so -inf - (-inf) is never formed ("Merge normalized
-//   attention without averaging tile outputs", paragraph on fully masked
-//   tiles).
-//   O~^T += V^T P^T on the same MFMA: P^T is used straight from the score
-//   registers as the B operand (rounded to the operand dtype); V^T comes
-//   from LDS, where the staging threads stored V transposed with bits 2 and
-//   3 of the key index swapped inside each 16-key group so that each A
-//   operand is one 16-byte LDS read.
-//   Masking (causal, key range, key mask) is applied only in tiles that
-//   need it; tiles with no visible key for a wave are skipped.
+//   kb*32 + 8*(r/4) + 4*(l/32) + r%4.
+//   O~^T += V^T P^T on the same MFMA: P^T is the B operand straight from the
+//   score registers (rounded to the operand dtype; the 8 keys of lane group
+//   h in 16-key chunk cc are 16cc + 4h + {0..3} and 16cc + 8 + 4h + {0..3});
+//   the V^T A operand is two transposing LDS reads of 4 consecutive keys x 1
+//   column each from the natural V tile.
 //
-// Epilogue: O = O~/l rounded to the output dtype, LSE = (m + log2 l) ln 2.
+// Online softmax in base 2, c = scale * log2(e): p = 2^(c*s - m) where m is
+// the row's reference maximum. The reference moves only when a score exceeds
+// it by more than kTau (then m <- the row's new maximum and l, O~ are
+// multiplied by alpha = 2^(m_old - m_new)); otherwise p <= 2^kTau and no
+// rescale is done. This is the recurrence of the pages with a reference that
+// is allowed to lag the running maximum: every term stays relative to the
+// same m in l and O~, so the result is unchanged in exact arithmetic, and
+// p <= 2^8 fits the fp32 state and the fp16/bf16 operands. While a row has
+// seen no visible key its reference stays -inf and the subtracted value is
+// 0, so -inf - (-inf) is never formed ("Merge normalized attention without
+// averaging tile outputs", paragraph on fully masked tiles).
+//   Masking (causal, key range, key mask) is applied only in tiles that need
+//   it; tiles with no visible key for a wave are skipped.
+//
+// Two running sums per row: l, the fp32 sum of the weights p (for the LSE),
+// and l~, the sum of the weights as rounded to the operand dtype for the PV
+// product. O~ accumulates the rounded weights, so it is divided by l~: the
+// output is then an exact convex combination of the value rows with weights
+// p~ / l~, whatever the magnitude of the dominant weight (up to 2^kTau here).
+//
+// Epilogue: O = O~/l~ rounded to the output dtype, LSE = (m + log2 l) ln 2.
 // l = 0 (no visible key) or a zero row-mask entry gives +0.0 output and
 // LSE = -inf ("Merge normalized attention without averaging tile outputs",
 // last paragraph).
@@ -47,9 +61,10 @@ constexpr int kWaves = 4;
 constexpr int kRows = 32;           // query rows per wave
 constexpr int kBc = 64;             // keys per tile
 constexpr int kKStr = kD + 8;       // K row stride in LDS (elements): 272 B
-constexpr int kVStr = kBc + 8;      // V^T row stride in LDS (elements): 144 B
+constexpr int kVStr = kD + 16;      // V row stride in LDS (elements): 288 B
 constexpr int kKElems = kBc * kKStr;
-constexpr int kVElems = kD * kVStr;
+constexpr int kVElems = kBc * kVStr;
+constexpr float kTau = 8.f;         // allowed lag of the reference max (log2 units)
 
 struct PrefillParams {
   const uint16_t* q;
@@ -66,11 +81,6 @@ struct PrefillParams {
   float c;      // scale * log2(e)
 };
 
-// Position of tile key kk (0..63) inside a V^T row of LDS.
-__device__ __forceinline__ int vt_pos(int kk) {
-  return (kk & ~12) | ((kk & 4) << 1) | ((kk & 8) >> 1);
-}
-
 template <int DT, bool CAUSAL, bool KMASK>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   using E = Elem<DT>;
@@ -79,7 +89,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int col = lane & 31;   // query row inside the wave's block
   const int half = lane >> 5;
 
@@ -104,60 +114,50 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   if (CAUSAL) n_tiles = min(n_tiles, (row_last_wg + off) / kBc + 1);
 
   // Q rows of this wave as MFMA B operands: lane holds row col, d in
-  // [16c + 8*half, 16c + 8*half + 8).
+  // [16c + 8*half, 16c + 8*half + 8). Rows past T_q read as zeros.
   u32x4 qf[8];
   {
-    const bool ok = wave_valid && qrow < p.T_q;
-    const uint16_t* qp = p.q + ((size_t)(b * p.h + head) * p.T_q + (ok ? qrow : 0)) * kD + half * 8;
+    const uint16_t* qbase = p.q + (size_t)(b * p.h + (wave_valid ? head : 0)) * p.T_q * kD;
+    const auto rq = make_rsrc(qbase, wave_valid ? (uint32_t)p.T_q * kD * 2 : 0u);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) qf[c] = ok ? load16(qp + c * 16) : u32x4{0, 0, 0, 0};
+    for (int c = 0; c < 8; ++c) qf[c] = buffer_load16(rq, (uint32_t)((qrow * kD + c * 16 + half * 8) * 2));
   }
 
   const size_t kv_base = (size_t)bk * p.T_k * kD;
-  const uint16_t* kg = p.k + kv_base;
-  const uint16_t* vg = p.v + kv_base;
+  const auto rk = make_rsrc(p.k + kv_base, (uint32_t)p.T_k * kD * 2);
+  const auto rv = make_rsrc(p.v + kv_base, (uint32_t)p.T_k * kD * 2);
 
-  // Staging registers: K as 4 chunks of 16 B (key chunk>>4, d-chunk chunk&15),
-  // V as 4 consecutive keys x 8 d for a transposed store.
+  // Staging: 1024 16-byte chunks per tile for K and for V; chunk = tid +
+  // 256 i holds key chunk / 16, d-chunk chunk % 16.
   u32x4 kreg[4], vreg[4];
-  const int v_kq = tid >> 4;   // 4-key group 0..15
-  const int v_dg = tid & 15;   // 8-d group 0..15
-
   auto load_tile = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int chunk = tid + 256 * i;
-      const int key = kt + (chunk >> 4);
-      kreg[i] = key < p.T_k ? load16(kg + (size_t)key * kD + (chunk & 15) * 8) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = kt + v_kq * 4 + i;
-      vreg[i] = key < p.T_k ? load16(vg + (size_t)key * kD + v_dg * 8) : u32x4{0, 0, 0, 0};
+      const uint32_t byte = (uint32_t)(((kt + ((tid + 256 * i) >> 4)) * kD + (tid & 15) * 8) * 2);
+      kreg[i] = buffer_load16(rk, byte);
+      vreg[i] = buffer_load16(rv, byte);
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int chunk = tid + 256 * i;
-      store16(&lds_k[buf][(chunk >> 4) * kKStr + (chunk & 15) * 8], kreg[i]);
-    }
-    const int pos = vt_pos(v_kq * 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int d = v_dg * 8 + 2 * e;
-      store8(&lds_v[buf][d * kVStr + pos],
-             u32x2{pack_lo16(vreg[0][e], vreg[1][e]), pack_lo16(vreg[2][e], vreg[3][e])});
-      store8(&lds_v[buf][(d + 1) * kVStr + pos],
-             u32x2{pack_hi16(vreg[0][e], vreg[1][e]), pack_hi16(vreg[2][e], vreg[3][e])});
+      const int key = (tid + 256 * i) >> 4;
+      store16(&lds_k[buf][key * kKStr + (tid & 15) * 8], kreg[i]);
+      store16(&lds_v[buf][key * kVStr + (tid & 15) * 8], vreg[i]);
     }
   };
+
+  // Per-lane offsets of the transposing V reads: lane j of a 16-lane group
+  // addresses key 4*half + j/4 (+8 for the upper 4 keys) and column
+  // 16*((lane>>4)&1) + 4*(j%4) of each 32-column block.
+  const int v_lane_off = (4 * half + ((lane & 15) >> 2)) * kVStr + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   f32x16 acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
-  float m_run = -INFINITY;   // running max, base-2 scaled units
-  float l_run = 0.f;         // this lane's share of the running sum
+  float m_ref = -INFINITY;   // reference maximum, base-2 scaled units
+  float l_run = 0.f;         // this lane's share of the running sum of p
+  float lr_run = 0.f;        // ... and of the rounded weights p~
 
   if (n_tiles > 0) {
     load_tile(0);
@@ -209,46 +209,48 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
         }
       }
 
-      float mx = s[0][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-      mx = max_halves(mx);
-      const float m_new = fmaxf(m_run, mx * p.c);
-      const float base = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - base);
-      float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
+        float mx = s[kb][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        if (__ballot(mx * p.c > m_ref + kTau)) {
+          // Re-reference: this block raised some row's maximum too far.
+          const float m_new = fmaxf(m_ref, max_halves(mx) * p.c);
+          if (m_new != -INFINITY) {
+            const float alpha = fast_exp2(m_ref - m_new);   // m_ref = -inf -> 0
+            l_run *= alpha;
+            lr_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] *= alpha;
+            m_ref = m_new;
+          }
+        }
+        const float base = m_ref == -INFINITY ? 0.f : m_ref;
+        float rs = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float e = fast_exp2(__builtin_fmaf(s[kb][r], p.c, -base));
           s[kb][r] = e;
           rs += e;
         }
-      }
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
-      if (__ballot(alpha != 1.f)) {
+        l_run += rs;
+        // P^T for the two 16-key chunks of this block, then their PV MFMAs.
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] *= alpha;
-      }
-
-      // P^T as B operands: 16-key chunk cc uses registers 8*(cc%2).. of block cc/2.
-      u32x4 pf[4];
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int cc = kb * 2 + h2;
+          const int r0 = h2 * 8;
+          const u32x4 pf = u32x4{E::pack2(s[kb][r0 + 0], s[kb][r0 + 1]), E::pack2(s[kb][r0 + 2], s[kb][r0 + 3]),
+                                 E::pack2(s[kb][r0 + 4], s[kb][r0 + 5]), E::pack2(s[kb][r0 + 6], s[kb][r0 + 7])};
+          lr_run = E::add_pair(pf[3], E::add_pair(pf[2], E::add_pair(pf[1], E::add_pair(pf[0], lr_run))));
+          const uint16_t* vr = vs + cc * 16 * kVStr + v_lane_off;
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        const f32x16& sv = s[cc >> 1];
-        const int r0 = (cc & 1) * 8;
-        pf[cc] = u32x4{E::pack2(sv[r0 + 0], sv[r0 + 1]), E::pack2(sv[r0 + 2], sv[r0 + 3]),
-                       E::pack2(sv[r0 + 4], sv[r0 + 5]), E::pack2(sv[r0 + 6], sv[r0 + 7])};
-      }
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const uint16_t* vr = vs + (db * 32 + col) * kVStr + half * 8;
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) acc[db] = E::mfma32(load16(vr + cc * 16), pf[cc], acc[db]);
+          for (int db = 0; db < 4; ++db) {
+            const u32x2 lo = lds_read_tr16(vr + db * 32);
+            const u32x2 hi = lds_read_tr16(vr + 8 * kVStr + db * 32);
+            acc[db] = E::mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf, acc[db]);
+          }
+        }
       }
     }
 
@@ -258,9 +260,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
 
   if (!wave_valid || qrow >= p.T_q) return;
   const float l_tot = sum_halves(l_run);
+  const float lr_tot = sum_halves(lr_run);
   bool empty = l_tot == 0.f;
   if (p.row_mask != nullptr) empty = empty || p.row_mask[(size_t)b * p.T_q + qrow] == 0;
-  const float inv = empty ? 0.f : 1.f / l_tot;
+  const float inv = empty ? 0.f : 1.f / lr_tot;
   uint16_t* op = p.o + ((size_t)(b * p.h + head) * p.T_q + qrow) * kD;
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
@@ -274,7 +277,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
     }
   }
   if (p.lse != nullptr && half == 0)
-    p.lse[(size_t)(b * p.h + head) * p.T_q + qrow] = empty ? -INFINITY : (m_run + fast_log2(l_tot)) * kLn2;
+    p.lse[(size_t)(b * p.h + head) * p.T_q + qrow] = empty ? -INFINITY : (m_ref + fast_log2(l_tot)) * kLn2;
 }
 
 template <int DT, bool CAUSAL, bool KMASK>

@@ -194,3 +194,7 @@ def test_partial_state_bytes_arithmetic():
     # "What the merge costs": S (d_h + 2) 4 bytes per token-head.
     g = load_golden("decode_shape_arithmetic.json")["partial_bytes_per_token_head"]
     assert g["splits"] * (g["head_dim"] + 2) * 4 == g["bytes"]
+
+
+def test_prefill_rejects_sequences_beyond_32bit_offsets(lib):
+    assert prefill_call(lib, T_q=1, T_k=(1 << 23) + 1, causal=0) == 2

@@ -5,12 +5,14 @@ Tolerances (max abs error on outputs; LSE relative error |d| / max(1, |LSE|)):
 fp16 outputs 2e-3, bf16 outputs 1e-2, LSE 1e-4; the paged gather and the
 outputs of rows with no visible key (+0.0 bits, LSE -inf) are bit-exact.
 
-Where the output format itself cannot hold the absolute tolerance -- a bf16
-value in [4, 8) is stored with a spacing of 2^-5, so even the exact result
-rounded to nearest is up to 0.0156 away -- an element may exceed the
-tolerance only if it is a faithful rounding of the exact value (closer to it
-than one unit in the last place of the format). The logit-std-30 stress
-workload has such elements (|O| up to 5.1).
+The output tolerance bounds the kernel's result before its final rounding
+to the output format: an element passes when it is the nearest-even rounding
+of some value within the tolerance of the exact result, i.e.
+|o - exact| <= tol + half the format's spacing at o. The flat reading cannot
+be met by any bf16 output on the logit-std-30 stress workload: there the
+exact float64 result, rounded to the nearest bf16, is itself up to 0.0155
+away (|O| reaches 5.1, where bf16 values are 2^-5 apart). Each check also
+reports how many elements needed the rounding allowance.
 """
 
 import math
@@ -50,17 +52,20 @@ def assert_outputs(o_gpu_t, lse_gpu, o_ref, lse_ref, dtype, what):
     empty = np.isneginf(lse_ref)
     diff = np.abs(o_gpu - o_ref)
     err = float(np.max(diff)) if o_ref.size else 0.0
-    over = diff > TOL[dtype]
-    if over.any():
-        # allowed only where the format's spacing exceeds the tolerance and the
-        # output is a faithful rounding of the exact value
-        mag = np.abs(o_ref[over])
-        ulp = np.exp2(np.floor(np.log2(np.where(mag > 0, mag, 1.0))) - MANT_BITS[dtype])
-        half_ulp_too_big = ulp / 2 > TOL[dtype]
-        faithful = diff[over] < ulp
-        bad = ~(half_ulp_too_big & faithful)
-        assert not bad.any(), (f"{what}: max abs err {err:.3e} > {TOL[dtype]} "
-                               f"({int(bad.sum())} elements not explained by the output format)")
+    # half the spacing of the output grid at the stored value
+    mag = np.abs(o_gpu)
+    half_ulp = np.where(mag > 0, np.exp2(np.floor(np.log2(np.where(mag > 0, mag, 1.0))) - MANT_BITS[dtype] - 1), 0.0)
+    bad = diff > TOL[dtype] + half_ulp
+    if bad.any():
+        idx = np.argwhere(bad)[:6]
+        detail = "; ".join(f"at {tuple(int(x) for x in i)}: exact {o_ref[tuple(i)]:.6f} "
+                           f"got {o_gpu[tuple(i)]:.6f}" for i in idx)
+        raise AssertionError(f"{what}: max abs err {err:.3e}; {int(bad.sum())} elements beyond "
+                             f"{TOL[dtype]} + half an output ulp: {detail}")
+    n_allow = int((diff > TOL[dtype]).sum())
+    if n_allow:
+        print(f"{what}: {n_allow} of {diff.size} elements within tolerance only after the output "
+              f"rounding allowance (max abs err {err:.3e})")
     if lse_gpu is not None:
         assert np.array_equal(np.isneginf(lse_gpu), empty), f"{what}: empty-row LSE mismatch"
         fin = ~empty
