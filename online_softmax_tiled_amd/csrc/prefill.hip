@@ -184,12 +184,20 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
       const uint16_t* ks = lds_k[buf];
       const uint16_t* vs = lds_v[buf];
       f32x16 s[2];
+      // QK: the 8 K fragments of a 32-key block are read before its MFMAs.
+      // MFMA bursts run at raised wave priority so the other wave on the
+      // SIMD fills the gaps with its softmax work instead of delaying them.
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
         const uint16_t* kr = ks + (kb * 32 + col) * kKStr + half * 8;
+        u32x4 kf[8];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) s[kb] = E::mfma32(load16(kr + c * 16), qf[c], s[kb]);
+        for (int c = 0; c < 8; ++c) kf[c] = load16(kr + c * 16);
+        s[kb] = f32x16{};
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) s[kb] = E::mfma32(kf[c], qf[c], s[kb]);
+        __builtin_amdgcn_s_setprio(0);
       }
 
       bool need_mask = kt + kBc > p.T_k;
@@ -209,24 +217,26 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
         }
       }
 
+      // One re-reference check for the whole tile, so that the rest of the
+      // tile is a single straight-line block in which the exponentials of
+      // block 1 can be scheduled between the PV MFMAs of block 0.
+      float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+      if (__ballot(mx * p.c > m_ref + kTau)) {
+        const float m_new = fmaxf(m_ref, max_halves(mx) * p.c);
+        if (m_new != -INFINITY) {
+          const float alpha = fast_exp2(m_ref - m_new);   // m_ref = -inf -> 0
+          l_run *= alpha;
+          lr_run *= alpha;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] *= alpha;
+          m_ref = m_new;
+        }
+      }
+      const float base = m_ref == -INFINITY ? 0.f : m_ref;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        float mx = s[kb][0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        if (__ballot(mx * p.c > m_ref + kTau)) {
-          // Re-reference: this block raised some row's maximum too far.
-          const float m_new = fmaxf(m_ref, max_halves(mx) * p.c);
-          if (m_new != -INFINITY) {
-            const float alpha = fast_exp2(m_ref - m_new);   // m_ref = -inf -> 0
-            l_run *= alpha;
-            lr_run *= alpha;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] *= alpha;
-            m_ref = m_new;
-          }
-        }
-        const float base = m_ref == -INFINITY ? 0.f : m_ref;
         float rs = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -244,12 +254,17 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
                                  E::pack2(s[kb][r0 + 4], s[kb][r0 + 5]), E::pack2(s[kb][r0 + 6], s[kb][r0 + 7])};
           lr_run = E::add_pair(pf[3], E::add_pair(pf[2], E::add_pair(pf[1], E::add_pair(pf[0], lr_run))));
           const uint16_t* vr = vs + cc * 16 * kVStr + v_lane_off;
+          u32x4 va[4];
 #pragma unroll
           for (int db = 0; db < 4; ++db) {
             const u32x2 lo = lds_read_tr16(vr + db * 32);
             const u32x2 hi = lds_read_tr16(vr + 8 * kVStr + db * 32);
-            acc[db] = E::mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf, acc[db]);
+            va[db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
           }
+          __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+          for (int db = 0; db < 4; ++db) acc[db] = E::mfma32(va[db], pf, acc[db]);
+          __builtin_amdgcn_s_setprio(0);
         }
       }
     }
