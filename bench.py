@@ -244,6 +244,29 @@ def cpu_baseline(inp, budget_s=15.0):
                        f"prefill, float64 numpy materialised attention, {spent:.1f} s of oracle time")
 
 
+def run_only(args, dev):
+    """One workload, for profiler counter runs: the prefill layer, a decode
+    workload, or a plain device copy of a known size (the calibration point
+    for the HBM byte counters)."""
+    import torch
+    if args.only == "prefill":
+        r = bench_prefill("llama3_8b_prefill_t8192", args.steps, args.warmup, dev)
+        print(json.dumps({"workload": "llama3_8b_prefill_t8192", "ms": r["ms"], "tflops": r["tflops"]}))
+    elif args.only == "decode_70b":
+        r = bench_decode_contiguous(args.steps, args.warmup, dev)
+        print(json.dumps(r))
+    elif args.only == "decode_paged":
+        from online_softmax_tiled_amd.workloads import make_config
+        r = bench_decode_paged(args.steps, args.warmup, dev, make_config("paged_decode_llama3_8b_b64"))
+        print(json.dumps(r))
+    else:
+        n = args.copy_mb * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        ms, _ = time_loop(lambda i=0: dst.copy_(src), args.steps, args.warmup)
+        print(json.dumps({"workload": "device copy", "bytes_read": n, "bytes_written": n, "ms": ms}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -251,6 +274,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="only the headline prefill")
+    ap.add_argument("--only", choices=["prefill", "decode_70b", "decode_paged", "copy"], default=None,
+                    help="run one workload only (for profiler counter runs) and print its timing")
+    ap.add_argument("--copy-mb", type=int, default=1024,
+                    help="bytes moved by the plain device copy of --only copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} requested); "
@@ -261,6 +288,9 @@ def main():
     from online_softmax_tiled_amd import api
     dev = torch.device("cuda:0")
     log(f"device: {torch.cuda.get_device_name(dev)}, {api.version()}")
+    if args.only is not None:
+        run_only(args, dev)
+        return
 
     res = bench_prefill("llama3_8b_prefill_t8192", args.steps, args.warmup, dev)
     log(f"prefill T=8192: {res['ms']:.3f} ms/step, {res['tflops']:.1f} TFLOP/s")
