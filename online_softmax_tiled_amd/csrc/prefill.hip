@@ -4,19 +4,17 @@
 // recurrence" and "Extending the recurrence to the output").
 //
 // Work decomposition
-//   A workgroup is 4 waves. Each wave owns one block of 32 query rows of one
-//   query head; the 4 blocks of a workgroup belong to query heads that share
-//   one KV head (row blocks are numbered query-block-major, head-minor inside
-//   a GQA group), so every K/V tile staged in LDS feeds all 4 waves.
-//   Workgroups are numbered with (batch, kv head) fastest so that consecutive
-//   workgroups -- which the hardware deals round-robin to the 8 XCDs -- put
-//   each KV head's workgroups on one XCD and its L2; the longest causal row
-//   blocks are numbered first.
+//   A workgroup is 8 waves (one per SIMD pair slot: 2 waves per SIMD, one
+//   workgroup per CU). Each wave owns one block of 32 query rows of one query
+//   head; the 8 blocks of a workgroup belong to query heads that share one KV
+//   head (row blocks are numbered query-block-major, head-minor inside a GQA
+//   group), so every K/V tile staged in LDS feeds all 8 waves. Workgroups are
+//   numbered with (batch, kv head) fastest so that consecutive workgroups --
+//   which the hardware deals round-robin to the 8 XCDs -- put each KV head's
+//   workgroups on one XCD and its L2; the longest causal row blocks are
+//   numbered first.
 //
-// Per 64-key tile and wave
-//   K and V tiles are staged into LDS in their natural row-major layout with
-//   range-checked buffer loads (rows past T_k read as zeros), double
-//   buffered, one barrier per tile.
+// Products, per 64-key tile and wave
 //   S^T = K Q^T on v_mfma_f32_32x32x16 (A = K rows from LDS, B = the wave's
 //   Q rows held in VGPRs for the whole kernel). In the accumulator layout
 //   lane l holds query row l%32 and, for register r of 32-key block kb, key
@@ -27,6 +25,19 @@
 //   the V^T A operand is two transposing LDS reads of 4 consecutive keys x 1
 //   column each from the natural V tile.
 //
+// Software pipeline
+//   Iteration j issues the MFMAs of PV(j-1) and QK(j+1) and, between them,
+//   the softmax of tile j, all in one straight-line block: the 32 MFMAs run
+//   on the matrix core while the exponentials, sums and packing of the other
+//   tile go through the VALU. The block is cut into 8 slices of 4 MFMAs, each
+//   with its share of the softmax work and the LDS operand reads of the next
+//   slice. Tiles stream through LDS with range-checked buffer loads (keys
+//   past T_k read as zeros): K of tile t sits in slot t % 2 (read in
+//   iteration t - 1), V of tile t in slot t % 3 (read in iteration t + 1);
+//   K(j+2) and V(j+1) are loaded during iteration j and stored before its
+//   barrier. Tiles past a wave's last visible key are fully masked, so the
+//   pipeline's fill and drain iterations add exact zeros.
+//
 // Online softmax in base 2, c = scale * log2(e): p = 2^(c*s - m) where m is
 // the row's reference maximum. The reference moves only when a score exceeds
 // it by more than kTau (then m <- the row's new maximum and l, O~ are
@@ -34,12 +45,12 @@
 // rescale is done. This is the recurrence of the pages with a reference that
 // is allowed to lag the running maximum: every term stays relative to the
 // same m in l and O~, so the result is unchanged in exact arithmetic, and
-// p <= 2^8 fits the fp32 state and the fp16/bf16 operands. While a row has
-// seen no visible key its reference stays -inf and the subtracted value is
-// 0, so -inf - (-inf) is never formed ("Merge normalized attention without
-// averaging tile outputs", paragraph on fully masked tiles).
-//   Masking (causal, key range, key mask) is applied only in tiles that need
-//   it; tiles with no visible key for a wave are skipped.
+// p <= 2^8 fits the fp32 state and the fp16/bf16 operands. The move is
+// decided per row without branches; the rescale of O~, which must wait for
+// PV(j-1), is applied at the start of the next iteration (rarely taken). While
+// a row has seen no visible key its reference stays -inf and the subtracted
+// value is 0, so -inf - (-inf) is never formed ("Merge normalized attention
+// without averaging tile outputs", paragraph on fully masked tiles).
 //
 // Two running sums per row: l, the fp32 sum of the weights p (for the LSE),
 // and l~, the sum of the weights as rounded to the operand dtype for the PV
@@ -57,7 +68,8 @@ namespace attn {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32;           // query rows per wave
 constexpr int kBc = 64;             // keys per tile
 // LDS row strides. K rows are read 16 B per lane along a row; 272 B rows put
@@ -83,15 +95,17 @@ struct PrefillParams {
   int B, h, h_kv, T_q, T_k;
   int g;        // h / h_kv
   int n_rb;     // row blocks per (batch, kv head) = g * ceil(T_q / 32)
-  int n_grp;    // workgroups per (batch, kv head) = ceil(n_rb / 4)
+  int n_grp;    // workgroups per (batch, kv head) = ceil(n_rb / kWaves)
   float c;      // scale * log2(e)
 };
 
 template <int DT, bool CAUSAL, bool KMASK>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   using E = Elem<DT>;
+  // K of tile t lives in slot t % 2 (read in iteration t - 1), V of tile t in
+  // slot t % 3 (read in iteration t + 1).
   __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kKElems];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][kVElems];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[3][kVElems];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -118,9 +132,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   const int row_last_wg = min(p.T_q - 1, (rb_last / p.g) * kRows + kRows - 1);
   int n_tiles = (p.T_k + kBc - 1) / kBc;
   if (CAUSAL) n_tiles = min(n_tiles, (row_last_wg + off) / kBc + 1);
+  // Last tile with a key this wave may see (-1: none).
+  int last = wave_valid ? n_tiles - 1 : -1;
+  if (CAUSAL && wave_valid) last = min(last, (row_last_w + off) / kBc);
 
-  // Q rows of this wave as MFMA B operands: lane holds row col, d in
-  // [16c + 8*half, 16c + 8*half + 8). Rows past T_q read as zeros.
   u32x4 qf[8];
   {
     const uint16_t* qbase = p.q + (size_t)(b * p.h + (wave_valid ? head : 0)) * p.T_q * kD;
@@ -133,149 +148,247 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   const auto rk = make_rsrc(p.k + kv_base, (uint32_t)p.T_k * kD * 2);
   const auto rv = make_rsrc(p.v + kv_base, (uint32_t)p.T_k * kD * 2);
 
-  // Staging: 1024 16-byte chunks per tile for K and for V; chunk = tid +
-  // 256 i holds key chunk / 16, d-chunk chunk % 16.
-  u32x4 kreg[4], vreg[4];
-  auto load_tile = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t byte = (uint32_t)(((kt + ((tid + 256 * i) >> 4)) * kD + (tid & 15) * 8) * 2);
-      kreg[i] = buffer_load16(rk, byte);
-      vreg[i] = buffer_load16(rv, byte);
-    }
+  // Staging: 1024 16-byte chunks per tile for K and for V; chunk tid + 512 i
+  // holds key chunk / 16, d-chunk chunk % 16.
+  u32x4 kreg[2], vreg[2];
+  auto tile_byte = [&](int t, int i) {
+    return (uint32_t)(((t * kBc + ((tid + kThreads * i) >> 4)) * kD + (tid & 15) * 8) * 2);
   };
-  auto store_tile = [&](int buf) {
+  auto load_k = [&](int t) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = (tid + 256 * i) >> 4;
-      store16(&lds_k[buf][key * kKStr + (tid & 15) * 8], kreg[i]);
-      store16(&lds_v[buf][key * kVStr + (tid & 15) * 8], vreg[i]);
-    }
+    for (int i = 0; i < 2; ++i) kreg[i] = buffer_load16(rk, tile_byte(t, i));
+  };
+  auto load_v = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) vreg[i] = buffer_load16(rv, tile_byte(t, i));
+  };
+  auto store_k = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) store16(&lds_k[slot][((tid + kThreads * i) >> 4) * kKStr + (tid & 15) * 8], kreg[i]);
+  };
+  auto store_v = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) store16(&lds_v[slot][((tid + kThreads * i) >> 4) * kVStr + (tid & 15) * 8], vreg[i]);
   };
 
-  // Per-lane offsets of the transposing V reads: lane j of a 16-lane group
-  // addresses key 4*half + j/4 (+8 for the upper 4 keys) and column
-  // 16*((lane>>4)&1) + 4*(j%4) of each 32-column block.
   const int v_lane_off = (4 * half + ((lane & 15) >> 2)) * kVStr + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   f32x16 acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
-  float m_ref = -INFINITY;   // reference maximum, base-2 scaled units
-  float l_run = 0.f;         // this lane's share of the running sum of p
-  float lr_run = 0.f;        // ... and of the rounded weights p~
+  float m_ref = -INFINITY;
+  float l_run = 0.f;
+  float lr_run = 0.f;
 
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int j = 0; j < n_tiles; ++j) {
-    const int kt = j * kBc;
-    const int buf = j & 1;
-    if (j + 1 < n_tiles) load_tile(kt + kBc);
-
-    uint64_t kbits = ~0ull;
-    if (KMASK) {
-      const int key = kt + lane;
-      const bool on = key < p.T_k && p.key_mask[(size_t)b * p.T_k + key] != 0;
-      kbits = __ballot(on);
+  // S^T of one tile into s (K tile from LDS, Q from registers).
+  auto qk = [&](const uint16_t* ks, f32x16 (&s)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint16_t* kr = ks + (kb * 32 + col) * kKStr + half * 8;
+      s[kb] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < 8; ++c) s[kb] = E::mfma32(load16(kr + c * 16), qf[c], s[kb]);
     }
-    bool skip = !wave_valid;
-    if (CAUSAL) skip = skip || kt > row_last_w + off;
-    if (KMASK) skip = skip || kbits == 0;
-
-    if (!skip) {
-      const uint16_t* ks = lds_k[buf];
-      const uint16_t* vs = lds_v[buf];
-      f32x16 s[2];
-      // QK: the 8 K fragments of a 32-key block are read before its MFMAs.
-      // MFMA bursts run at raised wave priority so the other wave on the
-      // SIMD fills the gaps with its softmax work instead of delaying them.
+  };
+  // Masking of tile t's scores where the tile needs it; every score of a
+  // tile past the wave's last visible tile is masked, which makes the extra
+  // pipeline iterations add exact zeros.
+  auto mask = [&](int t, uint64_t kbits, f32x16 (&s)[2]) {
+    const int kt = t * kBc;
+    bool need = kt + kBc > p.T_k || t > last;
+    if (CAUSAL) need = need || (kt + kBc - 1 > q0 + off);
+    if (KMASK) need = need || (kbits != ~0ull);
+    if (need) {
+      // key offset ko = kb*32 + 8*(r/4) + 4*half + r%4 is visible when
+      // ko - 4*half <= lim
+      int lim = p.T_k - kt - 1;
+      if (CAUSAL) lim = min(lim, qrow + off - kt);
+      lim = t > last ? -1000 : lim - 4 * half;
+      const uint32_t w0 = (uint32_t)kbits >> (4 * half);
+      const uint32_t w1 = (uint32_t)(kbits >> 32) >> (4 * half);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const uint16_t* kr = ks + (kb * 32 + col) * kKStr + half * 8;
-        u32x4 kf[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) kf[c] = load16(kr + c * 16);
-        s[kb] = f32x16{};
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) s[kb] = E::mfma32(kf[c], qf[c], s[kb]);
-        __builtin_amdgcn_s_setprio(0);
-      }
-
-      bool need_mask = kt + kBc > p.T_k;
-      if (CAUSAL) need_mask = need_mask || (kt + kBc - 1 > q0 + off);
-      if (KMASK) need_mask = need_mask || (kbits != ~0ull);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int ko = kb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-            bool vis = kt + ko < p.T_k;
-            if (CAUSAL) vis = vis && (kt + ko <= qrow + off);
-            if (KMASK) vis = vis && ((kbits >> ko) & 1ull);
-            s[kb][r] = vis ? s[kb][r] : -INFINITY;
-          }
-        }
-      }
-
-      // One re-reference check for the whole tile, so that the rest of the
-      // tile is a single straight-line block in which the exponentials of
-      // block 1 can be scheduled between the PV MFMAs of block 0.
-      float mx = fmaxf(s[0][0], s[1][0]);
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
-      if (__ballot(mx * p.c > m_ref + kTau)) {
-        const float m_new = fmaxf(m_ref, max_halves(mx) * p.c);
-        if (m_new != -INFINITY) {
-          const float alpha = fast_exp2(m_ref - m_new);   // m_ref = -inf -> 0
-          l_run *= alpha;
-          lr_run *= alpha;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i] *= alpha;
-          m_ref = m_new;
-        }
-      }
-      const float base = m_ref == -INFINITY ? 0.f : m_ref;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float rs = 0.f;
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(__builtin_fmaf(s[kb][r], p.c, -base));
-          s[kb][r] = e;
-          rs += e;
+          const int kc = kb * 32 + (r >> 2) * 8 + (r & 3);
+          bool vis = kc <= lim;
+          if (KMASK) vis = vis && (((kb ? w1 : w0) >> (kc - kb * 32)) & 1u);
+          s[kb][r] = vis ? s[kb][r] : -INFINITY;
         }
-        l_run += rs;
-        // P^T for the two 16-key chunks of this block, then their PV MFMAs.
+    }
+  };
+  auto key_bits = [&](int t) -> uint64_t {
+    const int key = t * kBc + lane;
+    return __ballot(key < p.T_k && p.key_mask[(size_t)b * p.T_k + key] != 0);
+  };
+
+  f32x16 sc[2];     // scores of tile j
+  u32x4 pp[4];      // P^T of tile j - 1
+  uint64_t kbits = ~0ull;
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int cc = kb * 2 + h2;
-          const int r0 = h2 * 8;
-          const u32x4 pf = u32x4{E::pack2(s[kb][r0 + 0], s[kb][r0 + 1]), E::pack2(s[kb][r0 + 2], s[kb][r0 + 3]),
-                                 E::pack2(s[kb][r0 + 4], s[kb][r0 + 5]), E::pack2(s[kb][r0 + 6], s[kb][r0 + 7])};
-          lr_run = E::add_pair(pf[3], E::add_pair(pf[2], E::add_pair(pf[1], E::add_pair(pf[0], lr_run))));
-          const uint16_t* vr = vs + cc * 16 * kVStr + v_lane_off;
-          u32x4 va[4];
+  for (int i = 0; i < 4; ++i) pp[i] = u32x4{};
+  sc[0] = f32x16{};
+  sc[1] = f32x16{};
+
+  if (n_tiles > 0) {
+    load_k(0);
+    load_v(0);
+    store_k(0);
+    store_v(0);
+    if (n_tiles > 1) {
+      load_k(1);
+      store_k(1);
+    }
+    if (KMASK) kbits = key_bits(0);
+  }
+  // V slot 2 is read (with P = 0) in the first iteration.
+  for (int i = tid; i < kVElems / 8; i += kThreads) store16(&lds_v[2][i * 8], u32x4{});
+  __syncthreads();
+  qk(lds_k[0], sc);
+
+  float alpha = 1.f;   // rescale of O~ decided by the previous softmax
+  for (int j = 0; j <= n_tiles; ++j) {
+    // Tiles past the end load as zeros; the slots they go to are free, so the
+    // loads and stores need no conditions and the iteration stays one block
+    // from the rescale below to the barrier.
+    load_k(j + 2);
+    load_v(j + 1);
+    uint64_t kbits_next = ~0ull;
+    if (KMASK) kbits_next = key_bits(j + 1);
+    // O~ still holds PV(j-2) at the old reference; PV(j-1) below uses the
+    // weights of the current one.
+    if (__ballot(alpha != 1.f)) {
 #pragma unroll
-          for (int db = 0; db < 4; ++db) {
-            const u32x2 lo = lds_read_tr16(vr + db * 32);
-            const u32x2 hi = lds_read_tr16(vr + 8 * kVStr + db * 32);
-            va[db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-          }
-          __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-          for (int db = 0; db < 4; ++db) acc[db] = E::mfma32(va[db], pf, acc[db]);
-          __builtin_amdgcn_s_setprio(0);
-        }
-      }
+      for (int i = 0; i < 4; ++i) acc[i] *= alpha;
     }
 
-    if (j + 1 < n_tiles) store_tile(buf ^ 1);
+    f32x16 sn[2];
+    u32x4 pn[4];
+    mask(j, kbits, sc);
+    {
+      // Steady state: the 32 MFMAs of PV(j-1) and QK(j+1) in 8 slices of 4,
+      // each slice carrying a share of the softmax VALU work of tile j, with
+      // the MFMA operands of a slice read from LDS one slice ahead.
+      const uint16_t* vs = lds_v[(j + 2) % 3];
+      const uint16_t* ks = lds_k[(j + 1) & 1];
+      auto read_v = [&](int cc, u32x4 (&va)[4]) {
+        const uint16_t* vr = vs + cc * 16 * kVStr + v_lane_off;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const u32x2 lo = lds_read_tr16(vr + db * 32);
+          const u32x2 hi = lds_read_tr16(vr + 8 * kVStr + db * 32);
+          va[db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+      };
+      auto read_k = [&](int c2, u32x4 (&kf)[4]) {
+        // fragments c = 2*c2, 2*c2+1 of both 32-key blocks
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          kf[i] = load16(ks + ((i & 1) * 32 + col) * kKStr + half * 8 + (2 * c2 + (i >> 1)) * 16);
+      };
+      u32x4 fa[4], fb[4];
+      float mx, base, rs = 0.f;
+      // slice 0: PV chunk 0 | row maxima
+      read_v(0, fa);
+      mx = fmaxf(sc[0][0], sc[1][0]);
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(sc[0][r], sc[1][r]));
+      read_v(1, fb);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) acc[db] = E::mfma32(fa[db], pp[0], acc[db]);
+      __builtin_amdgcn_sched_barrier(0);
+      // slice 1: PV chunk 1 | reference update, exps of block 0 rows 0-7
+      read_v(2, fa);
+      {
+        const float mr = max_halves(mx) * p.c;
+        const bool move = mr > m_ref + kTau;
+        alpha = move ? fast_exp2(m_ref - mr) : 1.f;
+        m_ref = move ? mr : m_ref;
+        l_run *= alpha;
+        lr_run *= alpha;
+        base = m_ref == -INFINITY ? 0.f : m_ref;
+      }
+#pragma unroll
+      for (int db = 0; db < 4; ++db) acc[db] = E::mfma32(fb[db], pp[1], acc[db]);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        sc[0][r] = fast_exp2(__builtin_fmaf(sc[0][r], p.c, -base));
+        rs += sc[0][r];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // slice 2: PV chunk 2 | exps of block 0 rows 8-15
+      read_v(3, fb);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) acc[db] = E::mfma32(fa[db], pp[2], acc[db]);
+#pragma unroll
+      for (int r = 8; r < 16; ++r) {
+        sc[0][r] = fast_exp2(__builtin_fmaf(sc[0][r], p.c, -base));
+        rs += sc[0][r];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // slice 3: PV chunk 3 | exps of block 1 rows 0-7
+      read_k(0, fa);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) acc[db] = E::mfma32(fb[db], pp[3], acc[db]);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        sc[1][r] = fast_exp2(__builtin_fmaf(sc[1][r], p.c, -base));
+        rs += sc[1][r];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // slice 4: QK fragments 0-1 | exps of block 1 rows 8-15
+      read_k(1, fb);
+      sn[0] = E::mfma32(fa[0], qf[0], f32x16{});
+      sn[1] = E::mfma32(fa[1], qf[0], f32x16{});
+      sn[0] = E::mfma32(fa[2], qf[1], sn[0]);
+      sn[1] = E::mfma32(fa[3], qf[1], sn[1]);
+#pragma unroll
+      for (int r = 8; r < 16; ++r) {
+        sc[1][r] = fast_exp2(__builtin_fmaf(sc[1][r], p.c, -base));
+        rs += sc[1][r];
+      }
+      l_run += rs;
+      __builtin_amdgcn_sched_barrier(0);
+      // slices 5-7: QK fragments 2-7 | packing of P^T and the sum of p~
+#pragma unroll
+      for (int c2 = 1; c2 < 4; ++c2) {
+        u32x4 (&cur)[4] = (c2 & 1) ? fb : fa;
+        u32x4 (&nxt)[4] = (c2 & 1) ? fa : fb;
+        if (c2 < 3) read_k(c2 + 1, nxt);
+        sn[0] = E::mfma32(cur[0], qf[2 * c2], sn[0]);
+        sn[1] = E::mfma32(cur[1], qf[2 * c2], sn[1]);
+        sn[0] = E::mfma32(cur[2], qf[2 * c2 + 1], sn[0]);
+        sn[1] = E::mfma32(cur[3], qf[2 * c2 + 1], sn[1]);
+        if (c2 == 1) {
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) {
+            const int r0 = cc * 8;
+            pn[cc] = u32x4{E::pack2(sc[0][r0 + 0], sc[0][r0 + 1]), E::pack2(sc[0][r0 + 2], sc[0][r0 + 3]),
+                           E::pack2(sc[0][r0 + 4], sc[0][r0 + 5]), E::pack2(sc[0][r0 + 6], sc[0][r0 + 7])};
+          }
+        } else if (c2 == 2) {
+#pragma unroll
+          for (int cc = 2; cc < 4; ++cc) {
+            const int r0 = (cc - 2) * 8;
+            pn[cc] = u32x4{E::pack2(sc[1][r0 + 0], sc[1][r0 + 1]), E::pack2(sc[1][r0 + 2], sc[1][r0 + 3]),
+                           E::pack2(sc[1][r0 + 4], sc[1][r0 + 5]), E::pack2(sc[1][r0 + 6], sc[1][r0 + 7])};
+          }
+        } else {
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc)
+            lr_run = E::add_pair(pn[cc][3], E::add_pair(pn[cc][2], E::add_pair(pn[cc][1], E::add_pair(pn[cc][0], lr_run))));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pp[i] = pn[i];
+    sc[0] = sn[0];
+    sc[1] = sn[1];
+    kbits = kbits_next;
+
+    store_k(j & 1);
+    store_v((j + 1) % 3);
     __syncthreads();
   }
 
@@ -304,7 +417,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
 template <int DT, bool CAUSAL, bool KMASK>
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.n_grp * p.B * p.h_kv));
-  hipLaunchKernelGGL((prefill_kernel<DT, CAUSAL, KMASK>), grid, dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((prefill_kernel<DT, CAUSAL, KMASK>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
