@@ -25,6 +25,7 @@ exits with a message.
 """
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -40,6 +41,33 @@ if ROOT not in sys.path:
 METRIC = "prefill TFLOP/s (% MFMA peak); decode KV GB/s (% HBM peak) on 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, published
+
+# HBM bytes per prefill launch, from two rocprofv3 counter passes (FETCH_SIZE,
+# WRITE_SIZE) scaled by what the same counters read for a plain device copy of
+# known size. Valid only for the kernel source they were taken on.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_llama3_8b_t8192_traffic.json")
+KERNEL_SOURCES = ("online_softmax_tiled_amd/csrc/prefill.hip", "online_softmax_tiled_amd/csrc/common.h")
+
+
+def kernel_source_sha256():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the prefill kernel as recorded by the counter
+    passes, or None when there is no record or the kernel source changed."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_sha256():
+        return None
+    return int(rec["hbm_bytes_per_launch"])
 HEAD_DIM = 128
 
 
@@ -311,7 +339,8 @@ def main():
         "config": {"workload": "llama3_8b_prefill_t8192", "B": 1, "h": 32, "h_kv": 8, "T": 8192,
                    "d_h": 128, "causal": True, "flop_per_step": res["flop"]},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": recorded_traffic()},
     }
     inp = res.pop("inp")
     if not args.no_extras:
