@@ -16,6 +16,8 @@ Also reported, on the same line:
   64-sequence paged Llama-3-8B shape, as KV GB/s against 8 TB/s; the paged
   gather as GB/s moved;
 * ``prefill_other``: the tiny and the numerics-stress prefill shapes;
+* ``merge_lse``: the two-operand (O, LSE) merge on the Llama-3-8B prefill
+  output shape, as GB/s against 8 TB/s;
 * ``cpu_baseline``: the float64 oracle timed on the host CPU on a bounded
   sample of the same prefill workload (blocks of random query rows, about
   15 s of oracle time).
@@ -164,6 +166,35 @@ def bench_prefill(name, steps, warmup, dev):
     return dict(inp=inp, flop=flop, ms=ms, wall=wall, tflops=flop / (ms * 1e-3) / 1e12)
 
 
+def bench_merge_lse(steps, warmup, dev, copies=3):
+    """attn_merge_lse on the Llama-3-8B prefill output shape (two [1, 32, 8192,
+    128] bf16 outputs with their LSEs, e.g. a cascade's prefix and suffix).
+    ``copies`` input sets (3 x 268 MB) are rotated so each call reads HBM,
+    not the 256 MB last-level cache. GB/s = bytes moved / call time."""
+    import torch
+    from online_softmax_tiled_amd import api
+    g = torch.Generator(device="cpu").manual_seed(2024)
+    shape, lead = (1, 32, 8192, 128), (1, 32, 8192)
+    sets = []
+    for _ in range(copies):
+        sets.append(tuple(t.to(dev) for t in (
+            torch.randn(shape, generator=g).to(torch.bfloat16), (torch.randn(lead, generator=g) * 4).float(),
+            torch.randn(shape, generator=g).to(torch.bfloat16), (torch.randn(lead, generator=g) * 4).float())))
+    o = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(lead, dtype=torch.float32, device=dev)
+    rows = 32 * 8192
+    nbytes = rows * (2 * 128 * 2 + 2 * 4 + 128 * 2 + 4)
+
+    def step(i=0):
+        oa, la, ob, lb = sets[i % copies]
+        api.merge_lse(oa, la, ob, lb, out=o, lse=lse)
+
+    ms, _ = time_loop(step, steps, warmup)
+    return dict(workload="merge_lse_llama3_8b_t8192", rows=rows, bytes=nbytes, us=ms * 1e3,
+                gbs=nbytes / (ms * 1e-3) / 1e9, frac_hbm=nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                rotated_input_sets=copies)
+
+
 def bench_decode_contiguous(steps, warmup, dev, copies=40):
     import torch
     from online_softmax_tiled_amd import api
@@ -283,6 +314,8 @@ def run_only(args, dev):
     elif args.only == "decode_70b":
         r = bench_decode_contiguous(args.steps, args.warmup, dev)
         print(json.dumps(r))
+    elif args.only == "merge_lse":
+        print(json.dumps(bench_merge_lse(args.steps, args.warmup, dev)))
     elif args.only == "decode_paged":
         from online_softmax_tiled_amd.workloads import make_config
         r = bench_decode_paged(args.steps, args.warmup, dev, make_config("paged_decode_llama3_8b_b64"))
@@ -302,7 +335,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="only the headline prefill")
-    ap.add_argument("--only", choices=["prefill", "decode_70b", "decode_paged", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode_70b", "decode_paged", "merge_lse", "copy"], default=None,
                     help="run one workload only (for profiler counter runs) and print its timing")
     ap.add_argument("--copy-mb", type=int, default=1024,
                     help="bytes moved by the plain device copy of --only copy (counter calibration)")
@@ -367,6 +400,10 @@ def main():
                 if isinstance(v[key], float):
                     v[key] = round(v[key], 4)
         line["decode"] = decode
+        rm = bench_merge_lse(max(30, args.steps), 5, dev)
+        log(f"merge_lse llama3-8b t8192: {rm['us']:.1f} us, {rm['gbs']:.0f} GB/s")
+        line["merge_lse"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in rm.items()
+                             if k != "workload"}
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on the host CPU ...")
         line["cpu_baseline"] = cpu_baseline(inp)

@@ -163,6 +163,28 @@ int attn_merge_states(const float* part_o, const float* part_m, const float* par
                       void* o, float* lse, int dtype, void* stream);
 
 /*
+ * Two-operand merge in (O, LSE) form: the output over the union of two
+ * disjoint key ranges of the same query rows, from each range's normalised
+ * output and LSE (a cascade's shared prefix and per-request suffix, or two
+ * context-parallel shards). [NA] sections "The state that gets passed around
+ * is the log-sum-exp" (O = w_a O_a + w_b O_b with w = exp(LSE - M) / sum,
+ * LSE = M + ln(sum exp(LSE - M)), M the larger LSE) and "Scale first, then
+ * multiply" (the weights are normalised before they touch O, so the result
+ * is a convex combination); section "The base case is a NaN factory" (an
+ * LSE of +inf, the empty-row value of some producers, is read as -inf).
+ *
+ *   o_a, o_b    [rows, d_h] dtype, normalised outputs of the two ranges.
+ *   lse_a, lse_b [rows] fp32 natural-log LSE; -inf or +inf = empty range.
+ *   rows        number of (batch, head, query) rows, e.g. B * h * T.
+ *   o           [rows, d_h] dtype (written); may alias o_a or o_b.
+ *   lse         [rows] fp32 (written) or NULL; may alias lse_a or lse_b.
+ * The O of an empty side is never read. Both sides empty: o = +0.0 bits,
+ * lse = -inf ([MI], last paragraph).
+ */
+int attn_merge_lse(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                   int rows, int d_h, void* o, float* lse, int dtype, void* stream);
+
+/*
  * Paged-KV gather: copy each sequence's keys (or values) out of a paged pool
  * into a contiguous tensor, bit for bit. [DA] paged addressing after section
  * "What the merge costs": position p lives in page block_table[b][p / P] at

@@ -27,6 +27,7 @@ _SIGNATURES = {
     "attn_decode_split": [_c_void_p] * 4 + [_c_int] * 3 + [_c_void_p] + [_c_int] * 8 + [_c_float]
                          + [_c_void_p] * 4,
     "attn_merge_states": [_c_void_p] * 4 + [_c_int] * 5 + [_c_void_p, _c_void_p, _c_int, _c_void_p],
+    "attn_merge_lse": [_c_void_p] * 4 + [_c_int] * 2 + [_c_void_p, _c_void_p, _c_int, _c_void_p],
     "attn_paged_gather": [_c_void_p] * 3 + [_c_int] * 8 + [_c_void_p, _c_void_p],
     "attn_last_error": [],
     "attn_version": [],
@@ -220,6 +221,29 @@ def decode(q, k, v, seq_lens, seq_lens_host=None, block_table=None, page_size=16
     po, pm, pl = decode_split(q, k, v, seq_lens, chunk, splits, block_table, page_size, scale)
     o, lse = merge_states(po, pm, pl, seq_lens, chunk, q.dtype)
     return o, lse, plan
+
+
+def merge_lse(o_a, lse_a, o_b, lse_b, out=None, lse=None):
+    """(O, LSE) of the union of two disjoint key ranges via attn_merge_lse.
+    o_* [..., 128] and lse_* [...] over the same leading shape; ``out`` / ``lse``
+    may be o_a / lse_a (in place)."""
+    lib = load()
+    _want(o_a, "o_a")
+    dev, dt = o_a.device, o_a.dtype
+    lead = tuple(o_a.shape[:-1])
+    d = o_a.shape[-1]
+    _want(o_b, "o_b", dt, tuple(o_a.shape), dev)
+    _want(lse_a, "lse_a", torch.float32, lead, dev)
+    _want(lse_b, "lse_b", torch.float32, lead, dev)
+    out = torch.empty_like(o_a) if out is None else out
+    _want(out, "out", dt, tuple(o_a.shape), dev)
+    lse = torch.empty(lead, dtype=torch.float32, device=dev) if lse is None else lse
+    _want(lse, "lse", torch.float32, lead, dev)
+    rows = int(np.prod(lead)) if lead else 1
+    _check("attn_merge_lse", lib.attn_merge_lse(
+        _ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), rows, d, _ptr(out), _ptr(lse),
+        _dtype_code(out), _stream(dev)))
+    return out, lse
 
 
 def paged_gather(pool, block_table, seq_lens, s_max, out=None):

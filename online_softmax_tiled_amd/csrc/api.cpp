@@ -31,6 +31,8 @@ hipError_t merge_states(const float* part_o, const float* part_m, const float* p
 hipError_t paged_gather(const void* pool, const int32_t* block_table, const int32_t* seq_lens,
                         int B, int h_kv, int page_size, int max_pages, int num_pages, int s_max,
                         void* out, hipStream_t stream);
+hipError_t merge_lse(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, void* o,
+                     float* lse, int rows, int dtype, hipStream_t stream);
 int decode_plan(int B, const int32_t* seq_lens, int h_kv, int num_cus, int32_t* chunk_keys,
                 int32_t* max_splits);
 }  // namespace attn
@@ -178,6 +180,16 @@ int attn_merge_states(const float* part_o, const float* part_m, const float* par
   return from_hip(attn::merge_states(part_o, part_m, part_l, seq_lens, chunk_keys, B, h, max_splits, o, lse, dtype,
                                      static_cast<hipStream_t>(stream)),
                   fn);
+}
+
+int attn_merge_lse(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, int rows, int d_h,
+                   void* o, float* lse, int dtype, void* stream) {
+  const char* fn = "attn_merge_lse";
+  if (int e = check_common(fn, dtype, d_h)) return e;
+  REQUIRE(rows >= 0, ATTN_ERR_INVALID, "%s: rows must be non-negative (got %d)", fn, rows);
+  if (rows == 0) return ok();
+  REQUIRE(o_a && lse_a && o_b && lse_b && o, ATTN_ERR_INVALID, "%s: a required pointer is NULL", fn);
+  return from_hip(attn::merge_lse(o_a, lse_a, o_b, lse_b, o, lse, rows, dtype, static_cast<hipStream_t>(stream)), fn);
 }
 
 int attn_paged_gather(const void* pool, const int32_t* block_table, const int32_t* seq_lens, int B, int h_kv,

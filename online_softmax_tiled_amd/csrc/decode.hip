@@ -304,9 +304,12 @@ hipError_t decode_split(const void* q, const void* k, const void* v, const int32
 // first fills the machine is ceil(num_cus / (B * h_kv)) ("Decode attention:
 // FlashDecoding, split-K, paged kernels", section "The grid"). Here the key
 // slice length is chosen instead, so ragged batches are balanced too: aim at
-// about 16 workgroups per CU of total work (several per CU keep enough loads
-// in flight and even out ragged lengths), never below 128 keys per slice
-// unless that is needed to reach one workgroup per CU, never below 64.
+// about 12 workgroups per CU of total work (several per CU keep enough loads
+// in flight and even out ragged lengths; fewer, longer slices spend less on
+// each workgroup's start and final merge -- on the 64-sequence Llama-3-8B
+// shape 1280-key slices read 5.5 TB/s where 960-key slices read 5.2), never
+// below 128 keys per slice unless that is needed to reach one workgroup per
+// CU, never below 64.
 int decode_plan(int B, const int32_t* seq_lens, int h_kv, int num_cus, int32_t* chunk_keys,
                 int32_t* max_splits) {
   long total = 0;
@@ -320,7 +323,7 @@ int decode_plan(int B, const int32_t* seq_lens, int h_kv, int num_cus, int32_t* 
     for (int b = 0; b < B; ++b) u += (seq_lens[b] + chunk - 1) / chunk;
     return u * h_kv;
   };
-  const long target = 16L * num_cus;
+  const long target = 12L * num_cus;
   long chunk = (total * h_kv + target - 1) / target;
   chunk = ((chunk + 63) / 64) * 64;
   if (chunk < 128) chunk = 128;

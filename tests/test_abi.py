@@ -123,6 +123,11 @@ def test_decode_split_rejects_before_launch(lib, kw, code):
 
 def test_merge_and_gather_reject_before_launch(lib):
     p = ctypes.c_void_p
+    assert lib.attn_merge_lse(p(1), p(1), p(1), p(1), -1, 128, p(1), None, 1, None) == 1
+    assert lib.attn_merge_lse(p(1), None, p(1), p(1), 8, 128, p(1), None, 1, None) == 1
+    assert lib.attn_merge_lse(p(1), p(1), p(1), p(1), 8, 64, p(1), None, 1, None) == 2
+    assert lib.attn_merge_lse(p(1), p(1), p(1), p(1), 8, 128, p(1), None, 7, None) == 2
+    assert lib.attn_merge_lse(None, None, None, None, 0, 128, None, None, 1, None) == 0
     assert lib.attn_merge_states(p(1), p(1), p(1), p(1), 0, 1, 8, 4, 128, p(1), None, 1, None) == 1
     assert lib.attn_merge_states(p(1), p(1), p(1), p(1), 64, 1, 8, 0, 128, p(1), None, 1, None) == 1
     assert lib.attn_merge_states(p(1), None, p(1), p(1), 64, 1, 8, 4, 128, p(1), None, 1, None) == 1
@@ -172,12 +177,12 @@ def test_plan_properties(lib):
 def test_plan_on_the_measured_workloads(lib):
     # 70B TP8 shard, batch 1, 32768 keys on 256 CUs: one slice per CU.
     assert plan([32768], 8, 1, 256) == (128, 256)
-    # 64 ragged sequences at Llama-3-8B shape: thousands of slices, <=16 per sequence.
+    # 64 ragged sequences at Llama-3-8B shape: about 12 slices per CU, <=16 per sequence.
     rng = np.random.default_rng(1004)
     lens = rng.integers(512, 16384, size=64, endpoint=True)
     chunk, splits = plan(lens, 32, 8, 256)
     units = 8 * sum(math.ceil(int(s) / chunk) for s in lens)
-    assert units >= 16 * 256 * 0.9 and splits <= 16
+    assert units >= 12 * 256 * 0.9 and splits <= 16
 
 
 def test_plan_rejects_bad_input(lib):

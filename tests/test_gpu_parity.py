@@ -365,3 +365,103 @@ def test_decode_graph_replay_matches_eager():
         torch.cuda.synchronize()
     o_ref, lse_ref = decode_ref(dec["q"], dec["k_seqs"], dec["v_seqs"], dec["seq_lens"], dec["scale"])
     assert_outputs(o, lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16", "graph decode")
+
+
+# ------------------------------------------------------------------ (O, LSE) merge
+
+@pytest.mark.parametrize("dtype,T_k,split", [("bf16", 300, 128), ("f16", 257, 1), ("bf16", 200, 199)])
+def test_merge_lse_cascade_prefix_suffix(dtype, T_k, split):
+    # A shared prefix and a suffix of the keys attended separately (key
+    # masks), then combined in (O, LSE) form: the result is attention over
+    # all keys, checked against the oracle at the prefill tolerances.
+    inp = make_prefill(2, 8, 2, 96, T_k, 128, dtype, seed=T_k * 3 + split, causal=False)
+    km_a = np.zeros((2, T_k), dtype=np.uint8)
+    km_a[:, :split] = 1
+    km_b = (1 - km_a).astype(np.uint8)
+    q, k, v = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
+    oa, la = api.prefill(q, k, v, causal=False, scale=inp["scale"], key_mask=to_dev(km_a))
+    ob, lb = api.prefill(q, k, v, causal=False, scale=inp["scale"], key_mask=to_dev(km_b))
+    o, lse = api.merge_lse(oa, la, ob, lb)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = attention_ref(inp["q"], inp["k"], inp["v"], inp["scale"], False)
+    assert_outputs(o, lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, dtype,
+                   f"cascade merge {dtype} split {split}/{T_k}")
+
+
+def _merge_lse_case(dtype, rows, seed):
+    """Random (O, LSE) pairs with every kind of empty side. O of an empty side
+    is NaN on the device (it must never be read) and zero for the oracle."""
+    rng = np.random.default_rng(seed)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+    oa = torch.from_numpy(rng.standard_normal((rows, 128)).astype(np.float32)).to(tdt)
+    ob = torch.from_numpy(rng.standard_normal((rows, 128)).astype(np.float32)).to(tdt)
+    la = rng.normal(0.0, 6.0, rows).astype(np.float32)
+    lb = rng.normal(0.0, 6.0, rows).astype(np.float32)
+    la[0:10] = -np.inf                       # a empty
+    lb[10:20] = np.inf                       # b empty, +inf convention
+    la[20:30], lb[20:30] = np.inf, -np.inf   # both empty
+    la[30:40], lb[30:40] = -np.inf, -np.inf  # both empty
+    la[40:50] = np.inf                       # a empty, +inf convention
+    la[50:60], lb[50:60] = 80.0, -80.0       # one side dominates
+    la[60:70] = lb[60:70]                    # equal masses
+    empty_a = np.isinf(la)
+    empty_b = np.isinf(lb)
+    oa_ref = oa.float().numpy().astype(np.float64)
+    ob_ref = ob.float().numpy().astype(np.float64)
+    oa_ref[empty_a] = 0.0
+    ob_ref[empty_b] = 0.0
+    oa_dev, ob_dev = oa.clone(), ob.clone()
+    oa_dev[torch.from_numpy(empty_a)] = float("nan")
+    ob_dev[torch.from_numpy(empty_b)] = float("nan")
+    return (to_dev(oa_dev), to_dev(la), to_dev(ob_dev), to_dev(lb)), (oa_ref, la.astype(np.float64),
+                                                                       ob_ref, lb.astype(np.float64))
+
+
+def _check_merge_lse(o, lse, o_ref, lse_ref, dtype, what):
+    # fp32 arithmetic then one rounding: within half an output ulp plus 1e-5
+    o_gpu = o.float().cpu().numpy().astype(np.float64)
+    mag = np.abs(o_gpu)
+    half_ulp = np.where(mag > 0, np.exp2(np.floor(np.log2(np.where(mag > 0, mag, 1.0))) - MANT_BITS[dtype] - 1), 0.0)
+    diff = np.abs(o_gpu - o_ref)
+    assert np.all(diff <= half_ulp + 1e-5 * np.maximum(1.0, np.abs(o_ref))), f"{what}: max err {diff.max():.3e}"
+    lse_g = lse.cpu().numpy().astype(np.float64)
+    empty = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(lse_g), empty), f"{what}: empty rows differ"
+    assert float(lse_rel(lse_g[~empty], lse_ref[~empty]).max()) <= 1e-5, f"{what}: LSE"
+    assert np.all(o.view(torch.int16).cpu().numpy()[empty] == 0), f"{what}: empty rows are not +0.0 bits"
+
+
+@pytest.mark.parametrize("dtype,rows", [("bf16", 1000), ("f16", 1000), ("bf16", 17), ("bf16", 1)])
+def test_merge_lse_against_oracle_with_empty_sides(dtype, rows):
+    from oracle import merge_lse_ref
+    rows = max(rows, 70) if rows > 1 else rows
+    (oa, la, ob, lb), (oa_r, la_r, ob_r, lb_r) = _merge_lse_case(dtype, rows, seed=rows)
+    o, lse = api.merge_lse(oa, la, ob, lb)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = merge_lse_ref(oa_r, la_r, ob_r, lb_r)
+    _check_merge_lse(o, lse, o_ref, lse_ref, dtype, f"merge_lse {dtype} rows {rows}")
+    # in place over the first operand gives the same bits
+    o2, lse2 = api.merge_lse(oa, la, ob, lb, out=oa, lse=la)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.view(torch.int16), o.view(torch.int16)) and torch.equal(lse2, lse)
+
+
+def test_merge_lse_llama3_8b_shape_sampled():
+    # Full prefill-output shape [1, 32, 8192, 128], in the launch configuration
+    # the bench times; checked on 4096 sampled rows.
+    from oracle import merge_lse_ref
+    g = torch.Generator().manual_seed(7)
+    oa = torch.randn((1, 32, 8192, 128), generator=g).to(torch.bfloat16)
+    ob = torch.randn((1, 32, 8192, 128), generator=g).to(torch.bfloat16)
+    la = (torch.randn((1, 32, 8192), generator=g) * 4).float()
+    lb = (torch.randn((1, 32, 8192), generator=g) * 4).float()
+    o, lse = api.merge_lse(to_dev(oa), to_dev(la), to_dev(ob), to_dev(lb))
+    torch.cuda.synchronize()
+    idx = np.random.default_rng(8).choice(32 * 8192, size=4096, replace=False)
+    flat = lambda t: t.reshape(32 * 8192, *t.shape[3:])
+    o_ref, lse_ref = merge_lse_ref(flat(oa).float().numpy()[idx].astype(np.float64),
+                                   flat(la).numpy()[idx].astype(np.float64),
+                                   flat(ob).float().numpy()[idx].astype(np.float64),
+                                   flat(lb).numpy()[idx].astype(np.float64))
+    sel = torch.from_numpy(idx).to(DEV)
+    _check_merge_lse(flat(o)[sel], flat(lse)[sel], o_ref, lse_ref, "bf16", "merge_lse llama3-8b sampled")
