@@ -99,6 +99,11 @@ __device__ __forceinline__ float max_halves(float x) { return fmaxf(x, __shfl_xo
 __device__ __forceinline__ float sum_halves(float x) { return x + __shfl_xor(x, 32); }
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+// Streaming load: non-temporal hint, for data read exactly once (decode K/V),
+// so it does not displace reused lines from the caches.
+__device__ __forceinline__ u32x4 load16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 
 // Buffer resource over [base, base + bytes): a raw buffer load past the end
 // returns zeros instead of touching memory, so tile loads need no branches.
@@ -119,6 +124,10 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
 }
 __device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+// Streaming store: non-temporal hint, for output written once and not reread.
+__device__ __forceinline__ void store16_nt(void* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
 __device__ __forceinline__ void store8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
 
 }  // namespace attn
