@@ -15,7 +15,8 @@ Also reported, on the same line:
   step reads from HBM, not from the 256 MB last-level cache) and on the
   64-sequence paged Llama-3-8B shape, as KV GB/s against 8 TB/s; the paged
   gather as GB/s moved;
-* ``prefill_other``: the tiny and the numerics-stress prefill shapes;
+* ``prefill_other``: the tiny and the numerics-stress prefill shapes, and
+  the chunked prefill of 8 sequences against a paged cache;
 * ``merge_lse``: the two-operand (O, LSE) merge on the Llama-3-8B prefill
   output shape, as GB/s against 8 TB/s;
 * ``cpu_baseline``: the float64 oracle timed on the host CPU on a bounded
@@ -164,6 +165,32 @@ def bench_prefill(name, steps, warmup, dev):
 
     ms, wall = time_loop(step, steps, warmup)
     return dict(inp=inp, flop=flop, ms=ms, wall=wall, tflops=flop / (ms * 1e-3) / 1e12)
+
+
+def bench_chunked_prefill(steps, warmup, dev):
+    """attn_prefill_paged on the chunked-prefill workload: 8 sequences with
+    1024..8192 cached keys each, 256..1024 of them new (the query rows),
+    16-token pages. Useful FLOP = 4 d h x visible (query, key) pairs."""
+    import torch
+    from online_softmax_tiled_amd import api
+    from online_softmax_tiled_amd.workloads import make_config
+    c = make_config("chunked_prefill_llama3_8b_b8")
+    args = [t.to(dev) if isinstance(t, torch.Tensor) else torch.from_numpy(t).to(dev)
+            for t in (c["q"], c["cu_seqlens_q"], c["k_pool"], c["v_pool"], c["block_table"], c["seq_lens_k"])]
+    q, cu, kp, vp, bt, sk = args
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    tq = c["q_lens"].astype(np.int64)
+    tk = c["seq_lens_k"].astype(np.int64)
+    pairs = int((tq * (tk - tq) + tq * (tq + 1) // 2).sum())
+    flop = 4.0 * c["d"] * c["h"] * pairs
+
+    def step(i=0):
+        api.prefill_paged(q, cu, c["max_q"], kp, vp, bt, sk, causal=True, scale=c["scale"], out=o, lse=lse)
+
+    ms, _ = time_loop(step, steps, warmup)
+    return dict(ms=ms, tflops=flop / (ms * 1e-3) / 1e12, flop=flop, new_tokens=int(tq.sum()),
+                cached_keys=int(tk.sum()))
 
 
 def bench_merge_lse(steps, warmup, dev, copies=3):
@@ -383,6 +410,11 @@ def main():
             other[name] = {"ms": round(r["ms"], 4), "tflops": round(r["tflops"], 2),
                            "frac_mfma": round(r["tflops"] / PEAK_BF16_TFLOPS, 4)}
             log(f"prefill {name}: {r['ms']:.4f} ms, {r['tflops']:.1f} TFLOP/s")
+        rc = bench_chunked_prefill(max(10, args.steps), 3, dev)
+        other["chunked_prefill_llama3_8b_b8"] = {"ms": round(rc["ms"], 4), "tflops": round(rc["tflops"], 2),
+                                                  "frac_mfma": round(rc["tflops"] / PEAK_BF16_TFLOPS, 4),
+                                                  "new_tokens": rc["new_tokens"], "cached_keys": rc["cached_keys"]}
+        log(f"chunked prefill b8 (paged): {rc['ms']:.4f} ms, {rc['tflops']:.1f} TFLOP/s")
         line["prefill_other"] = other
         decode = {}
         r3 = bench_decode_contiguous(max(200, args.steps), 20, dev)

@@ -83,6 +83,40 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v,
                      int dtype, float scale, int causal, void* stream);
 
 /*
+ * Prefill of new tokens against a paged KV cache, variable length (chunked
+ * prefill in a serving batch): sequence b has T_q,b new query tokens, which
+ * are the last T_q,b positions of its T_k,b-token context; query t attends
+ * to keys j <= t + T_k,b - T_q,b when causal (bottom-right alignment), to
+ * all T_k,b keys otherwise. [DA] opening section (the launcher packs the
+ * query tokens of many sequences, with the g heads of a KV head, into
+ * query-parallel blocks) and section "Where GQA enters" (a chunked-prefill
+ * request in a mixed batch runs the query-parallel path over the paged
+ * cache; the block-table addressing); the arithmetic is that of
+ * attn_prefill_fwd ([NA] section "The online recurrence").
+ *
+ *   q            [total_q, h, d_h] dtype, token-major: the rows of sequence b
+ *                are cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1.
+ *   cu_seqlens_q [B + 1] int32 device, non-decreasing, cu_seqlens_q[0] = 0.
+ *   max_q        host upper bound of every T_q,b; it sizes the grid. Rows
+ *                past max_q of a longer sequence are not computed.
+ *   k_pool, v_pool  [num_pages, page_size, h_kv, d_h] dtype.
+ *   block_table  [B, max_pages] int32 device; key j of sequence b is slot
+ *                j % page_size of page block_table[b][j / page_size]. A page
+ *                id outside [0, num_pages) excludes its keys.
+ *   seq_lens_k   [B] int32 device, T_k,b (at most max_pages * page_size; at
+ *                least T_q,b when causal, else the first rows have no key).
+ *   page_size    a power of two in [16, 65536].
+ *   o            [total_q, h, d_h] dtype (written).
+ *   lse          [total_q, h] fp32 (written) or NULL.
+ * Rows with no visible key get +0.0 and LSE -inf. No key or row masks here.
+ */
+int attn_prefill_paged(const void* q, const int32_t* cu_seqlens_q, int max_q,
+                       const void* k_pool, const void* v_pool, const int32_t* block_table,
+                       const int32_t* seq_lens_k, int B, int h, int h_kv, int d_h,
+                       int page_size, int max_pages, int num_pages, int dtype, float scale,
+                       int causal, void* o, float* lse, void* stream);
+
+/*
  * Decode plan (host only, pure): choose the split-KV chunk length so the
  * stage-1 grid fills the GPU. [DA] sections "The grid" (the smallest split
  * count that fills the machine in one wave) and "SGLang: a split count

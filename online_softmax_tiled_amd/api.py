@@ -9,6 +9,7 @@ fails to load, every call raises.
 """
 
 import ctypes
+import math
 import os
 
 import numpy as np
@@ -23,6 +24,8 @@ HEAD_DIM = 128
 _c_int, _c_float, _c_void_p = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
 _SIGNATURES = {
     "attn_prefill_fwd": [_c_void_p] * 7 + [_c_int] * 7 + [_c_float, _c_int, _c_void_p],
+    "attn_prefill_paged": [_c_void_p, _c_void_p, _c_int] + [_c_void_p] * 4 + [_c_int] * 8 + [_c_float, _c_int]
+                          + [_c_void_p] * 3,
     "attn_decode_plan": [_c_int, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_void_p],
     "attn_decode_split": [_c_void_p] * 4 + [_c_int] * 3 + [_c_void_p] + [_c_int] * 8 + [_c_float]
                          + [_c_void_p] * 4,
@@ -132,6 +135,37 @@ def prefill(q, k, v, causal=True, scale=None, key_mask=None, row_mask=None, out=
     _check("attn_prefill_fwd", lib.attn_prefill_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(key_mask), _ptr(row_mask), _ptr(out), _ptr(lse),
         B, h, h_kv, T_q, T_k, d, _dtype_code(q), scale, 1 if causal else 0, _stream(dev)))
+    return out, lse
+
+
+def prefill_paged(q, cu_seqlens_q, max_q, k_pool, v_pool, block_table, seq_lens_k, causal=True, scale=None,
+                  out=None, lse=None):
+    """Variable-length prefill against a paged KV cache via attn_prefill_paged.
+
+    q [total_q, h, 128] token-major, cu_seqlens_q [B+1] int32 (device),
+    max_q >= every sequence's query count (host int), pools
+    [num_pages, page_size, h_kv, 128], block_table [B, max_pages] int32,
+    seq_lens_k [B] int32. Returns (o [total_q, h, 128], lse [total_q, h])."""
+    lib = load()
+    _want(q, "q")
+    dev, dt = q.device, q.dtype
+    total_q, h, d = q.shape
+    _want(k_pool, "k_pool", dt, None, dev)
+    num_pages, page_size, h_kv, _ = k_pool.shape
+    _want(v_pool, "v_pool", dt, tuple(k_pool.shape), dev)
+    _want(block_table, "block_table", torch.int32, None, dev)
+    B, max_pages = block_table.shape
+    _want(cu_seqlens_q, "cu_seqlens_q", torch.int32, (B + 1,), dev)
+    _want(seq_lens_k, "seq_lens_k", torch.int32, (B,), dev)
+    scale = float(np.float32(1.0 / np.sqrt(d))) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    _want(out, "out", dt, tuple(q.shape), dev)
+    lse = torch.empty((total_q, h), dtype=torch.float32, device=dev) if lse is None else lse
+    _want(lse, "lse", torch.float32, (total_q, h), dev)
+    _check("attn_prefill_paged", lib.attn_prefill_paged(
+        _ptr(q), _ptr(cu_seqlens_q), int(max_q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+        _ptr(seq_lens_k), B, h, h_kv, d, page_size, max_pages, num_pages, _dtype_code(q), float(scale),
+        int(bool(causal)), _ptr(out), _ptr(lse), _stream(dev)))
     return out, lse
 
 

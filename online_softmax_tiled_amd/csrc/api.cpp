@@ -31,6 +31,10 @@ hipError_t merge_states(const float* part_o, const float* part_m, const float* p
 hipError_t paged_gather(const void* pool, const int32_t* block_table, const int32_t* seq_lens,
                         int B, int h_kv, int page_size, int max_pages, int num_pages, int s_max,
                         void* out, hipStream_t stream);
+hipError_t prefill_paged(const void* q, const int32_t* cu_seqlens_q, int max_q, const void* k_pool,
+                         const void* v_pool, const int32_t* block_table, const int32_t* seq_lens_k, int B, int h,
+                         int h_kv, int page_shift, int max_pages, int num_pages, void* o, float* lse, int dtype,
+                         float scale, int causal, hipStream_t stream);
 hipError_t merge_lse(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, void* o,
                      float* lse, int rows, int dtype, hipStream_t stream);
 int decode_plan(int B, const int32_t* seq_lens, int h_kv, int num_cus, int32_t* chunk_keys,
@@ -115,6 +119,35 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, const uint8_t*
   REQUIRE(T_k == 0 || (k && v), ATTN_ERR_INVALID, "%s: k and v must not be NULL", fn);
   return from_hip(attn::prefill_fwd(q, k, v, key_mask, row_mask, o, lse, B, h, h_kv, T_q, T_k, dtype, scale,
                                     causal, static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+int attn_prefill_paged(const void* q, const int32_t* cu_seqlens_q, int max_q, const void* k_pool,
+                       const void* v_pool, const int32_t* block_table, const int32_t* seq_lens_k, int B, int h,
+                       int h_kv, int d_h, int page_size, int max_pages, int num_pages, int dtype, float scale,
+                       int causal, void* o, float* lse, void* stream) {
+  const char* fn = "attn_prefill_paged";
+  if (int e = check_common(fn, dtype, d_h)) return e;
+  if (int e = check_heads(fn, h, h_kv)) return e;
+  if (int e = check_scale(fn, scale)) return e;
+  REQUIRE(B >= 0 && max_q >= 0, ATTN_ERR_INVALID, "%s: negative size (B=%d, max_q=%d)", fn, B, max_q);
+  REQUIRE(page_size >= 16 && page_size <= (1 << 16) && (page_size & (page_size - 1)) == 0, ATTN_ERR_UNSUPPORTED,
+          "%s: page_size must be a power of two in [16, 65536] (got %d)", fn, page_size);
+  REQUIRE(max_pages > 0 && num_pages > 0, ATTN_ERR_INVALID, "%s: max_pages and num_pages must be positive", fn);
+  REQUIRE((long)max_pages * page_size <= kMaxSeq, ATTN_ERR_UNSUPPORTED, "%s: more than %d keys per sequence", fn,
+          kMaxSeq);
+  // Q rows of one head are addressed with 32-bit byte offsets (stride h * d).
+  REQUIRE((long)max_q * h * kHeadDim * 2 < (1L << 32), ATTN_ERR_UNSUPPORTED, "%s: max_q * h too large", fn);
+  const long n_grp = ((long)(h / h_kv) * ((max_q + 31) / 32) + 7) / 8;
+  REQUIRE(n_grp * B * h_kv < (1L << 31), ATTN_ERR_UNSUPPORTED, "%s: grid too large", fn);
+  if (B == 0 || max_q == 0) return ok();
+  REQUIRE(q && cu_seqlens_q && k_pool && v_pool && block_table && seq_lens_k && o, ATTN_ERR_INVALID,
+          "%s: a required pointer is NULL", fn);
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  return from_hip(attn::prefill_paged(q, cu_seqlens_q, max_q, k_pool, v_pool, block_table, seq_lens_k, B, h, h_kv,
+                                      shift, max_pages, num_pages, o, lse, dtype, scale, causal,
+                                      static_cast<hipStream_t>(stream)),
                   fn);
 }
 

@@ -97,9 +97,18 @@ struct PrefillParams {
   int n_rb;     // row blocks per (batch, kv head) = g * ceil(T_q / 32)
   int n_grp;    // workgroups per (batch, kv head) = ceil(n_rb / kWaves)
   float c;      // scale * log2(e)
+  // Paged, variable-length form (PAGED): Q and O token-major [total_q, h, d]
+  // with sequence b at rows cu_q[b] .. cu_q[b+1]; LSE [total_q, h]; K/V in
+  // pools [num_pages, page_size, h_kv, d] addressed through the block table;
+  // T_q, T_k, n_rb, n_grp above are then upper bounds over the batch and the
+  // per-sequence values are read on the device.
+  const int32_t* cu_q;
+  const int32_t* seq_k;
+  const int32_t* bt;
+  int max_pages, num_pages, page_shift;   // page_size = 1 << page_shift
 };
 
-template <int DT, bool CAUSAL, bool KMASK>
+template <int DT, bool CAUSAL, bool KMASK, bool PAGED>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   using E = Elem<DT>;
   // K of tile t lives in slot t % 2 (read in iteration t - 1), V of tile t in
@@ -119,34 +128,48 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   const int b = bk / p.h_kv;
   const int kvh = bk - b * p.h_kv;
 
+  // Lengths of this sequence (uniform over the workgroup).
+  int T_q = p.T_q, T_k = p.T_k, n_rb = p.n_rb, q_start = 0;
+  if (PAGED) {
+    q_start = p.cu_q[b];
+    T_q = min(p.cu_q[b + 1] - q_start, p.T_q);
+    T_k = min(p.seq_k[b], p.max_pages << p.page_shift);
+    n_rb = p.g * ((T_q + kRows - 1) / kRows);
+    if (grp * kWaves >= n_rb) return;   // whole workgroup past this sequence's rows
+  }
+
   const int rb = grp * kWaves + wave;
-  const bool wave_valid = rb < p.n_rb;
+  const bool wave_valid = rb < n_rb;
   const int qblk = rb / p.g;
   const int head = kvh * p.g + (rb - qblk * p.g);
   const int q0 = qblk * kRows;
-  const int off = p.T_k - p.T_q;   // >= 0 when causal
+  const int off = T_k - T_q;   // >= 0 when causal (bottom-right alignment)
   const int qrow = q0 + col;
-  const int row_last_w = min(p.T_q - 1, q0 + kRows - 1);
+  const int row_last_w = min(T_q - 1, q0 + kRows - 1);
 
-  const int rb_last = min(grp * kWaves + kWaves - 1, p.n_rb - 1);
-  const int row_last_wg = min(p.T_q - 1, (rb_last / p.g) * kRows + kRows - 1);
-  int n_tiles = (p.T_k + kBc - 1) / kBc;
+  const int rb_last = min(grp * kWaves + kWaves - 1, n_rb - 1);
+  const int row_last_wg = min(T_q - 1, (rb_last / p.g) * kRows + kRows - 1);
+  int n_tiles = (T_k + kBc - 1) / kBc;
   if (CAUSAL) n_tiles = min(n_tiles, (row_last_wg + off) / kBc + 1);
   // Last tile with a key this wave may see (-1: none).
   int last = wave_valid ? n_tiles - 1 : -1;
   if (CAUSAL && wave_valid) last = min(last, (row_last_w + off) / kBc);
 
+  // Q row qrow of this wave's head: [B, h, T_q, d], or token-major
+  // [total_q, h, d] when PAGED (row stride h * d).
+  const int q_rstride = PAGED ? p.h * kD : kD;
   u32x4 qf[8];
   {
-    const uint16_t* qbase = p.q + (size_t)(b * p.h + (wave_valid ? head : 0)) * p.T_q * kD;
-    const auto rq = make_rsrc(qbase, wave_valid ? (uint32_t)p.T_q * kD * 2 : 0u);
+    const int hq = wave_valid ? head : 0;
+    const uint16_t* qbase = PAGED ? p.q + ((size_t)q_start * p.h + hq) * kD : p.q + (size_t)(b * p.h + hq) * T_q * kD;
+    const auto rq = make_rsrc(qbase, wave_valid ? (uint32_t)T_q * q_rstride * 2 : 0u);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) qf[c] = buffer_load16(rq, (uint32_t)((qrow * kD + c * 16 + half * 8) * 2));
+    for (int c = 0; c < 8; ++c) qf[c] = buffer_load16(rq, (uint32_t)((qrow * q_rstride + c * 16 + half * 8) * 2));
   }
 
-  const size_t kv_base = (size_t)bk * p.T_k * kD;
-  const auto rk = make_rsrc(p.k + kv_base, (uint32_t)p.T_k * kD * 2);
-  const auto rv = make_rsrc(p.v + kv_base, (uint32_t)p.T_k * kD * 2);
+  const size_t kv_base = PAGED ? 0 : (size_t)bk * T_k * kD;
+  const auto rk = make_rsrc(p.k + kv_base, PAGED ? 0u : (uint32_t)T_k * kD * 2);
+  const auto rv = make_rsrc(p.v + kv_base, PAGED ? 0u : (uint32_t)T_k * kD * 2);
 
   // Staging: 1024 16-byte chunks per tile for K and for V; chunk tid + 512 i
   // holds key chunk / 16, d-chunk chunk % 16.
@@ -154,13 +177,35 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   auto tile_byte = [&](int t, int i) {
     return (uint32_t)(((t * kBc + ((tid + kThreads * i) >> 4)) * kD + (tid & 15) * 8) * 2);
   };
+  // Paged: key row of chunk i of tile t, through the block table; keys past
+  // T_k or on a page id outside the pool read as zeros.
+  auto paged_row = [&](int t, int i) -> long {
+    const int key = t * kBc + ((tid + kThreads * i) >> 4);
+    int page = key < T_k ? p.bt[(size_t)b * p.max_pages + (key >> p.page_shift)] : -1;
+    if (page < 0 || page >= p.num_pages) return -1;
+    return (((long)page << p.page_shift) + (key & ((1 << p.page_shift) - 1))) * p.h_kv + kvh;
+  };
   auto load_k = [&](int t) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) kreg[i] = buffer_load16(rk, tile_byte(t, i));
+    for (int i = 0; i < 2; ++i) {
+      if (PAGED) {
+        const long r = paged_row(t, i);
+        kreg[i] = r >= 0 ? load16(p.k + r * kD + (tid & 15) * 8) : u32x4{0u, 0u, 0u, 0u};
+      } else {
+        kreg[i] = buffer_load16(rk, tile_byte(t, i));
+      }
+    }
   };
   auto load_v = [&](int t) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) vreg[i] = buffer_load16(rv, tile_byte(t, i));
+    for (int i = 0; i < 2; ++i) {
+      if (PAGED) {
+        const long r = paged_row(t, i);
+        vreg[i] = r >= 0 ? load16(p.v + r * kD + (tid & 15) * 8) : u32x4{0u, 0u, 0u, 0u};
+      } else {
+        vreg[i] = buffer_load16(rv, tile_byte(t, i));
+      }
+    }
   };
   auto store_k = [&](int slot) {
 #pragma unroll
@@ -195,13 +240,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   // pipeline iterations add exact zeros.
   auto mask = [&](int t, uint64_t kbits, f32x16 (&s)[2]) {
     const int kt = t * kBc;
-    bool need = kt + kBc > p.T_k || t > last;
+    bool need = kt + kBc > T_k || t > last;
     if (CAUSAL) need = need || (kt + kBc - 1 > q0 + off);
     if (KMASK) need = need || (kbits != ~0ull);
     if (need) {
       // key offset ko = kb*32 + 8*(r/4) + 4*half + r%4 is visible when
       // ko - 4*half <= lim
-      int lim = p.T_k - kt - 1;
+      int lim = T_k - kt - 1;
       if (CAUSAL) lim = min(lim, qrow + off - kt);
       lim = t > last ? -1000 : lim - 4 * half;
       const uint32_t w0 = (uint32_t)kbits >> (4 * half);
@@ -217,9 +262,19 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
         }
     }
   };
+  // Visible-key bits of tile t (KMASK): the key mask, or with PAGED the keys
+  // whose block-table entry names a page of the pool.
   auto key_bits = [&](int t) -> uint64_t {
     const int key = t * kBc + lane;
-    return __ballot(key < p.T_k && p.key_mask[(size_t)b * p.T_k + key] != 0);
+    if (PAGED) {
+      bool on = key < T_k;
+      if (on) {
+        const int page = p.bt[(size_t)b * p.max_pages + (key >> p.page_shift)];
+        on = page >= 0 && page < p.num_pages;
+      }
+      return __ballot(on);
+    }
+    return __ballot(key < T_k && p.key_mask[(size_t)b * T_k + key] != 0);
   };
 
   f32x16 sc[2];     // scores of tile j
@@ -392,13 +447,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     __syncthreads();
   }
 
-  if (!wave_valid || qrow >= p.T_q) return;
+  if (!wave_valid || qrow >= T_q) return;
   const float l_tot = sum_halves(l_run);
   const float lr_tot = sum_halves(lr_run);
   bool empty = l_tot == 0.f;
-  if (p.row_mask != nullptr) empty = empty || p.row_mask[(size_t)b * p.T_q + qrow] == 0;
+  if (!PAGED && p.row_mask != nullptr) empty = empty || p.row_mask[(size_t)b * T_q + qrow] == 0;
   const float inv = empty ? 0.f : 1.f / lr_tot;
-  uint16_t* op = p.o + ((size_t)(b * p.h + head) * p.T_q + qrow) * kD;
+  const size_t orow = PAGED ? (size_t)(q_start + qrow) * p.h + head : (size_t)(b * p.h + head) * T_q + qrow;
+  uint16_t* op = p.o + orow * kD;
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
 #pragma unroll
@@ -411,33 +467,35 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     }
   }
   if (p.lse != nullptr && half == 0)
-    p.lse[(size_t)(b * p.h + head) * p.T_q + qrow] = empty ? -INFINITY : (m_ref + fast_log2(l_tot)) * kLn2;
+    p.lse[orow] = empty ? -INFINITY : (m_ref + fast_log2(l_tot)) * kLn2;
 }
 
-template <int DT, bool CAUSAL, bool KMASK>
+template <int DT, bool CAUSAL, bool KMASK, bool PAGED>
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.n_grp * p.B * p.h_kv));
-  hipLaunchKernelGGL((prefill_kernel<DT, CAUSAL, KMASK>), grid, dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((prefill_kernel<DT, CAUSAL, KMASK, PAGED>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int DT>
 hipError_t dispatch_prefill(const PrefillParams& p, bool causal, bool kmask, hipStream_t s) {
-  if (causal) return kmask ? launch_prefill<DT, true, true>(p, s) : launch_prefill<DT, true, false>(p, s);
-  return kmask ? launch_prefill<DT, false, true>(p, s) : launch_prefill<DT, false, false>(p, s);
+  if (causal) return kmask ? launch_prefill<DT, true, true, false>(p, s) : launch_prefill<DT, true, false, false>(p, s);
+  return kmask ? launch_prefill<DT, false, true, false>(p, s) : launch_prefill<DT, false, false, false>(p, s);
 }
 
-}  // namespace
+// Paged launches take the key-bit path: keys on a page id outside the pool
+// are excluded (masked), not read as zeros.
+template <int DT>
+hipError_t dispatch_prefill_paged(const PrefillParams& p, bool causal, hipStream_t s) {
+  return causal ? launch_prefill<DT, true, true, true>(p, s) : launch_prefill<DT, false, true, true>(p, s);
+}
 
-hipError_t prefill_fwd(const void* q, const void* k, const void* v, const uint8_t* key_mask,
-                       const uint8_t* row_mask, void* o, float* lse, int B, int h, int h_kv,
-                       int T_q, int T_k, int dtype, float scale, int causal, hipStream_t stream) {
-  PrefillParams p;
+PrefillParams common_params(const void* q, const void* k, const void* v, void* o, float* lse, int B, int h,
+                            int h_kv, int T_q, int T_k, float scale) {
+  PrefillParams p = {};
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
   p.v = static_cast<const uint16_t*>(v);
-  p.key_mask = key_mask;
-  p.row_mask = row_mask;
   p.o = static_cast<uint16_t*>(o);
   p.lse = lse;
   p.B = B;
@@ -449,9 +507,39 @@ hipError_t prefill_fwd(const void* q, const void* k, const void* v, const uint8_
   p.n_rb = p.g * ((T_q + kRows - 1) / kRows);
   p.n_grp = (p.n_rb + kWaves - 1) / kWaves;
   p.c = scale * kLog2e;
+  return p;
+}
+
+}  // namespace
+
+hipError_t prefill_fwd(const void* q, const void* k, const void* v, const uint8_t* key_mask,
+                       const uint8_t* row_mask, void* o, float* lse, int B, int h, int h_kv,
+                       int T_q, int T_k, int dtype, float scale, int causal, hipStream_t stream) {
+  PrefillParams p = common_params(q, k, v, o, lse, B, h, h_kv, T_q, T_k, scale);
+  p.key_mask = key_mask;
+  p.row_mask = row_mask;
   if (B == 0 || T_q == 0 || h == 0) return hipSuccess;
   if (dtype == ATTN_DTYPE_BF16) return dispatch_prefill<ATTN_DTYPE_BF16>(p, causal != 0, key_mask != nullptr, stream);
   return dispatch_prefill<ATTN_DTYPE_F16>(p, causal != 0, key_mask != nullptr, stream);
+}
+
+// Variable-length prefill against a paged KV cache: T_q is the largest query
+// count of the batch (it sizes the grid; workgroups past a sequence's rows
+// exit at once), T_k the largest key count the block table can address.
+hipError_t prefill_paged(const void* q, const int32_t* cu_seqlens_q, int max_q, const void* k_pool,
+                         const void* v_pool, const int32_t* block_table, const int32_t* seq_lens_k, int B, int h,
+                         int h_kv, int page_shift, int max_pages, int num_pages, void* o, float* lse, int dtype,
+                         float scale, int causal, hipStream_t stream) {
+  PrefillParams p = common_params(q, k_pool, v_pool, o, lse, B, h, h_kv, max_q, max_pages << page_shift, scale);
+  p.cu_q = cu_seqlens_q;
+  p.seq_k = seq_lens_k;
+  p.bt = block_table;
+  p.max_pages = max_pages;
+  p.num_pages = num_pages;
+  p.page_shift = page_shift;
+  if (B == 0 || max_q == 0 || h == 0) return hipSuccess;
+  if (dtype == ATTN_DTYPE_BF16) return dispatch_prefill_paged<ATTN_DTYPE_BF16>(p, causal != 0, stream);
+  return dispatch_prefill_paged<ATTN_DTYPE_F16>(p, causal != 0, stream);
 }
 
 }  // namespace attn

@@ -170,7 +170,31 @@ def make_decode(B, h, h_kv, d, dtype, seed, seq_lens=None, len_range=None, paged
     return out
 
 
-# The five named workloads. Seeds are 1000 + their position (1-based).
+def make_chunked_prefill(B, h, h_kv, d, dtype, seed, ctx_range, new_range, page_size=16, spare_pages=0,
+                         poison=True):
+    """Chunked prefill against a paged cache: sequence b holds T_k,b context
+    tokens in the pools (drawn as by ``make_decode`` with ``ctx_range``), the
+    last T_q,b of which are new and are the query rows; T_q,b is drawn from
+    ``new_range`` (inclusive) and capped at T_k,b. Queries come from a second
+    pair of streams (root seed ``seed + 7919``) and are packed token-major.
+
+    Returns the paged decode dict plus q [total_q, h, d], cu_seqlens_q
+    int32 [B+1], q_lens int32 [B] and seq_lens_k (= seq_lens).
+    """
+    dec = make_decode(B, h, h_kv, d, dtype, seed, len_range=ctx_range, paged=True, page_size=page_size,
+                      spare_pages=spare_pages, poison=poison)
+    rv, ri = _streams(seed + 7919)
+    lo, hi = new_range
+    q_lens = np.minimum(ri.integers(lo, hi, size=B, endpoint=True), dec["seq_lens"]).astype(np.int32)
+    cu = np.concatenate([[0], np.cumsum(q_lens.astype(np.int64))]).astype(np.int32)
+    q = _normal(rv, (int(cu[-1]), h, d), dtype)
+    dec.update(kind="chunked_prefill", q=q, q_lens=q_lens, cu_seqlens_q=cu, seq_lens_k=dec["seq_lens"],
+               max_q=int(q_lens.max()) if B else 0)
+    return dec
+
+
+# The named workloads. Seeds are 1000 + their position (1-based); the sixth
+# is the chunked-prefill shape of the paged prefill entry point.
 CONFIGS = {
     "tiny_prefill": dict(
         kind="prefill", B=1, h=4, h_kv=1, T_q=256, T_k=256, d=128, dtype="f16",
@@ -188,6 +212,9 @@ CONFIGS = {
         kind="prefill", B=1, h=32, h_kv=8, T_q=4096, T_k=4096, d=128, dtype="bf16",
         causal=True, qk_std=math.sqrt(30.0), key_tile=64, key_tile_p=1.0 / 8.0,
         row_mask_frac=0.01, seed=1005),
+    "chunked_prefill_llama3_8b_b8": dict(
+        kind="chunked_prefill", B=8, h=32, h_kv=8, d=128, dtype="bf16", ctx_range=(1024, 8192),
+        new_range=(256, 1024), page_size=16, seed=1006),
 }
 
 
@@ -198,4 +225,6 @@ def make_config(name, **overrides):
     kind = cfg.pop("kind")
     if kind == "prefill":
         return make_prefill(**cfg)
+    if kind == "chunked_prefill":
+        return make_chunked_prefill(**cfg)
     return make_decode(**cfg)

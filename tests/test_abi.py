@@ -203,3 +203,37 @@ def test_partial_state_bytes_arithmetic():
 
 def test_prefill_rejects_sequences_beyond_32bit_offsets(lib):
     assert prefill_call(lib, T_q=1, T_k=(1 << 23) + 1, causal=0) == 2
+
+
+def paged_prefill_call(lib, **kw):
+    args = dict(q=1, cu=1, max_q=8, kp=1, vp=1, bt=1, sk=1, B=1, h=8, h_kv=2, d=128, page=16, max_pages=4,
+                num_pages=4, dtype=1, scale=0.088, causal=1, o=1, lse=NULL)
+    args.update(kw)
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.attn_prefill_paged(p(args["q"]), p(args["cu"]), args["max_q"], p(args["kp"]), p(args["vp"]),
+                                  p(args["bt"]), p(args["sk"]), args["B"], args["h"], args["h_kv"], args["d"],
+                                  args["page"], args["max_pages"], args["num_pages"], args["dtype"], args["scale"],
+                                  args["causal"], p(args["o"]), p(args["lse"]), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(page=24), 2),          # not a power of two
+    (dict(page=8), 2),           # below 16
+    (dict(d=64), 2),
+    (dict(dtype=3), 2),
+    (dict(h=6, h_kv=4), 1),
+    (dict(max_pages=0), 1),
+    (dict(num_pages=0), 1),
+    (dict(scale=-1.0), 1),
+    (dict(B=-1), 1),
+    (dict(bt=None), 1),
+    (dict(cu=None), 1),
+    (dict(max_pages=1 << 20, page=16), 2),   # more keys per sequence than supported
+])
+def test_paged_prefill_rejects_before_launch(lib, kw, code):
+    assert paged_prefill_call(lib, **kw) == code
+
+
+def test_paged_prefill_empty_is_ok_without_launch(lib):
+    assert paged_prefill_call(lib, B=0, q=None, o=None) == 0
+    assert paged_prefill_call(lib, max_q=0, q=None, o=None) == 0

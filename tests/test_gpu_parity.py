@@ -465,3 +465,92 @@ def test_merge_lse_llama3_8b_shape_sampled():
                                    flat(lb).numpy()[idx].astype(np.float64))
     sel = torch.from_numpy(idx).to(DEV)
     _check_merge_lse(flat(o)[sel], flat(lse)[sel], o_ref, lse_ref, "bf16", "merge_lse llama3-8b sampled")
+
+
+# ------------------------------------------------------------------ paged (chunked) prefill
+
+def _run_paged_prefill(c, causal, rows_per_seq=None):
+    """attn_prefill_paged on a chunked-prefill case; checks every sequence
+    against the oracle over its ground-truth contiguous K/V (optionally on a
+    sample of its query rows)."""
+    from online_softmax_tiled_amd.workloads import DTYPES
+    q = to_dev(c["q"])
+    o, lse = api.prefill_paged(q, to_dev(c["cu_seqlens_q"]), c["max_q"], to_dev(c["k_pool"]), to_dev(c["v_pool"]),
+                               to_dev(c["block_table"]), to_dev(c["seq_lens_k"]), causal=causal, scale=c["scale"])
+    torch.cuda.synchronize()
+    cu = c["cu_seqlens_q"]
+    excluded = c.get("excluded_keys", {})
+    for b in range(c["B"]):
+        tq, tk = int(cu[b + 1] - cu[b]), int(c["seq_lens_k"][b])
+        if tq == 0:
+            continue
+        qb = c["q"][cu[b]:cu[b + 1]].permute(1, 0, 2).unsqueeze(0)
+        kb = c["k_seqs"][b].unsqueeze(0)
+        vb = c["v_seqs"][b].unsqueeze(0)
+        km = None
+        if b in excluded:
+            km = np.ones((1, tk), dtype=np.uint8)
+            km[0, excluded[b]] = 0
+        rows = None
+        if rows_per_seq is not None and tq > rows_per_seq:
+            rows = np.sort(np.random.default_rng(b).choice(tq, size=rows_per_seq, replace=False))
+        o_ref, lse_ref = attention_ref(qb, kb, vb, c["scale"], causal, key_mask=km, rows=rows)
+        sel = np.arange(tq) if rows is None else rows
+        ob = o[cu[b]:cu[b + 1]][torch.from_numpy(sel).to(DEV)].permute(1, 0, 2).unsqueeze(0)
+        lb = lse[cu[b]:cu[b + 1]].cpu().numpy().astype(np.float64)[sel].T[None]
+        assert_outputs(ob, lb, o_ref, lse_ref, c["dtype"], f"paged prefill seq {b} ({tq} new / {tk} keys)")
+
+
+@pytest.mark.parametrize("dtype,page_size,causal", [("bf16", 16, True), ("f16", 32, True), ("bf16", 64, False),
+                                                    ("bf16", 16, False)])
+def test_paged_prefill_small(dtype, page_size, causal):
+    from online_softmax_tiled_amd.workloads import make_chunked_prefill
+    c = make_chunked_prefill(5, 8, 2, 128, dtype, seed=page_size + 3 * causal, ctx_range=(1, 300),
+                             new_range=(1, 120), page_size=page_size, spare_pages=3)
+    _run_paged_prefill(c, causal)
+
+
+def test_paged_prefill_edge_sequences():
+    # an empty sequence (no new tokens), a fully new one (T_q = T_k), a
+    # one-token one, and a block-table entry outside the pool (its keys are
+    # excluded, as the oracle's key mask says)
+    from online_softmax_tiled_amd.workloads import make_chunked_prefill
+    c = make_chunked_prefill(4, 8, 2, 128, "bf16", seed=11, ctx_range=(40, 200), new_range=(1, 60),
+                             page_size=16)
+    tk = c["seq_lens_k"]
+    q_lens = np.array([0, int(tk[1]), 1, min(37, int(tk[3]))], dtype=np.int32)
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    g = torch.Generator().manual_seed(12)
+    c["q"] = torch.randn((int(cu[-1]), 8, 128), generator=g).to(torch.bfloat16)
+    c.update(q_lens=q_lens, cu_seqlens_q=cu, max_q=int(q_lens.max()))
+    bt = c["block_table"].copy()
+    bt[3, 1] = -1                     # keys 16..31 of sequence 3 are not in the pool
+    c["block_table"] = bt
+    c["excluded_keys"] = {3: np.arange(16, 32)}
+    _run_paged_prefill(c, True)
+
+
+def test_paged_prefill_chunked_llama3_8b_b8():
+    # the measured chunked-prefill workload, in the bench's launch
+    # configuration, on 96 sampled query rows per sequence
+    c = make_config("chunked_prefill_llama3_8b_b8")
+    _run_paged_prefill(c, True, rows_per_seq=96)
+
+
+def test_paged_prefill_matches_contiguous_prefill():
+    # one sequence whose pages happen to be consecutive: bits equal to the
+    # contiguous kernel on the same keys (same tiling, same arithmetic)
+    inp = make_prefill(1, 8, 2, 70, 200, 128, "bf16", seed=5, causal=True)
+    k, v = inp["k"][0], inp["v"][0]                       # [h_kv, T_k, d]
+    pad = (-200) % 16                                     # 200 keys -> 13 pages, the last zero-padded
+    kt = torch.cat([k.permute(1, 0, 2), torch.zeros(pad, 2, 128, dtype=k.dtype)]).reshape(-1, 16, 2, 128)
+    vt = torch.cat([v.permute(1, 0, 2), torch.zeros(pad, 2, 128, dtype=v.dtype)]).reshape(-1, 16, 2, 128)
+    bt = torch.arange(kt.shape[0], dtype=torch.int32)[None]
+    q_tok = inp["q"][0].permute(1, 0, 2).contiguous()     # [T_q, h, d]
+    o_p, l_p = api.prefill_paged(to_dev(q_tok), to_dev(torch.tensor([0, 70], dtype=torch.int32)), 70,
+                                 to_dev(kt.contiguous()), to_dev(vt.contiguous()), to_dev(bt),
+                                 to_dev(torch.tensor([200], dtype=torch.int32)), causal=True, scale=inp["scale"])
+    o_c, l_c = api.prefill(to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"]), causal=True, scale=inp["scale"])
+    torch.cuda.synchronize()
+    assert torch.equal(o_p.permute(1, 0, 2).unsqueeze(0).contiguous().view(torch.int16), o_c.view(torch.int16))
+    assert torch.equal(l_p.T.unsqueeze(0).contiguous(), l_c)
