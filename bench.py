@@ -186,7 +186,8 @@ def bench_chunked_prefill(steps, warmup, dev):
     flop = 4.0 * c["d"] * c["h"] * pairs
 
     def step(i=0):
-        api.prefill_paged(q, cu, c["max_q"], kp, vp, bt, sk, causal=True, scale=c["scale"], out=o, lse=lse)
+        api.prefill_paged(q, cu, c["max_q"], kp, vp, bt, sk, causal=True, scale=c["scale"], out=o, lse=lse,
+                          seq_lens_k_host=c["seq_lens_k"])
 
     ms, _ = time_loop(step, steps, warmup)
     return dict(ms=ms, tflops=flop / (ms * 1e-3) / 1e12, flop=flop, new_tokens=int(tq.sum()),

@@ -105,6 +105,10 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v,
  *                id outside [0, num_pages) excludes its keys.
  *   seq_lens_k   [B] int32 device, T_k,b (at most max_pages * page_size; at
  *                least T_q,b when causal, else the first rows have no key).
+ *   seq_lens_k_host  NULL, or the same counts on the host: then (for B <= 512)
+ *                the sequences are launched longest context first, which
+ *                balances the GPU when the contexts differ; results do not
+ *                depend on it.
  *   page_size    a power of two in [16, 65536].
  *   o            [total_q, h, d_h] dtype (written).
  *   lse          [total_q, h] fp32 (written) or NULL.
@@ -112,7 +116,8 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v,
  */
 int attn_prefill_paged(const void* q, const int32_t* cu_seqlens_q, int max_q,
                        const void* k_pool, const void* v_pool, const int32_t* block_table,
-                       const int32_t* seq_lens_k, int B, int h, int h_kv, int d_h,
+                       const int32_t* seq_lens_k, const int32_t* seq_lens_k_host,
+                       int B, int h, int h_kv, int d_h,
                        int page_size, int max_pages, int num_pages, int dtype, float scale,
                        int causal, void* o, float* lse, void* stream);
 

@@ -24,7 +24,7 @@ HEAD_DIM = 128
 _c_int, _c_float, _c_void_p = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
 _SIGNATURES = {
     "attn_prefill_fwd": [_c_void_p] * 7 + [_c_int] * 7 + [_c_float, _c_int, _c_void_p],
-    "attn_prefill_paged": [_c_void_p, _c_void_p, _c_int] + [_c_void_p] * 4 + [_c_int] * 8 + [_c_float, _c_int]
+    "attn_prefill_paged": [_c_void_p, _c_void_p, _c_int] + [_c_void_p] * 5 + [_c_int] * 8 + [_c_float, _c_int]
                           + [_c_void_p] * 3,
     "attn_decode_plan": [_c_int, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_void_p],
     "attn_decode_split": [_c_void_p] * 4 + [_c_int] * 3 + [_c_void_p] + [_c_int] * 8 + [_c_float]
@@ -139,13 +139,15 @@ def prefill(q, k, v, causal=True, scale=None, key_mask=None, row_mask=None, out=
 
 
 def prefill_paged(q, cu_seqlens_q, max_q, k_pool, v_pool, block_table, seq_lens_k, causal=True, scale=None,
-                  out=None, lse=None):
+                  out=None, lse=None, seq_lens_k_host=None):
     """Variable-length prefill against a paged KV cache via attn_prefill_paged.
 
     q [total_q, h, 128] token-major, cu_seqlens_q [B+1] int32 (device),
     max_q >= every sequence's query count (host int), pools
     [num_pages, page_size, h_kv, 128], block_table [B, max_pages] int32,
-    seq_lens_k [B] int32. Returns (o [total_q, h, 128], lse [total_q, h])."""
+    seq_lens_k [B] int32. ``seq_lens_k_host`` (optional, host ints) lets the
+    library launch the longest contexts first. Returns (o [total_q, h, 128],
+    lse [total_q, h])."""
     lib = load()
     _want(q, "q")
     dev, dt = q.device, q.dtype
@@ -162,9 +164,15 @@ def prefill_paged(q, cu_seqlens_q, max_q, k_pool, v_pool, block_table, seq_lens_
     _want(out, "out", dt, tuple(q.shape), dev)
     lse = torch.empty((total_q, h), dtype=torch.float32, device=dev) if lse is None else lse
     _want(lse, "lse", torch.float32, (total_q, h), dev)
+    host = None
+    if seq_lens_k_host is not None:
+        host = np.ascontiguousarray(np.asarray(seq_lens_k_host, dtype=np.int32))
+        if host.shape != (B,):
+            raise ValueError(f"seq_lens_k_host has shape {host.shape}, expected ({B},)")
     _check("attn_prefill_paged", lib.attn_prefill_paged(
         _ptr(q), _ptr(cu_seqlens_q), int(max_q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
-        _ptr(seq_lens_k), B, h, h_kv, d, page_size, max_pages, num_pages, _dtype_code(q), float(scale),
+        _ptr(seq_lens_k), None if host is None else host.ctypes.data_as(_c_void_p), B, h, h_kv, d, page_size,
+        max_pages, num_pages, _dtype_code(q), float(scale),
         int(bool(causal)), _ptr(out), _ptr(lse), _stream(dev)))
     return out, lse
 

@@ -32,9 +32,10 @@ hipError_t paged_gather(const void* pool, const int32_t* block_table, const int3
                         int B, int h_kv, int page_size, int max_pages, int num_pages, int s_max,
                         void* out, hipStream_t stream);
 hipError_t prefill_paged(const void* q, const int32_t* cu_seqlens_q, int max_q, const void* k_pool,
-                         const void* v_pool, const int32_t* block_table, const int32_t* seq_lens_k, int B, int h,
-                         int h_kv, int page_shift, int max_pages, int num_pages, void* o, float* lse, int dtype,
-                         float scale, int causal, hipStream_t stream);
+                         const void* v_pool, const int32_t* block_table, const int32_t* seq_lens_k,
+                         const int32_t* seq_lens_k_host, int B, int h, int h_kv, int page_shift, int max_pages,
+                         int num_pages, void* o, float* lse, int dtype, float scale, int causal,
+                         hipStream_t stream);
 hipError_t merge_lse(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, void* o,
                      float* lse, int rows, int dtype, hipStream_t stream);
 int decode_plan(int B, const int32_t* seq_lens, int h_kv, int num_cus, int32_t* chunk_keys,
@@ -123,7 +124,8 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, const uint8_t*
 }
 
 int attn_prefill_paged(const void* q, const int32_t* cu_seqlens_q, int max_q, const void* k_pool,
-                       const void* v_pool, const int32_t* block_table, const int32_t* seq_lens_k, int B, int h,
+                       const void* v_pool, const int32_t* block_table, const int32_t* seq_lens_k,
+                       const int32_t* seq_lens_k_host, int B, int h,
                        int h_kv, int d_h, int page_size, int max_pages, int num_pages, int dtype, float scale,
                        int causal, void* o, float* lse, void* stream) {
   const char* fn = "attn_prefill_paged";
@@ -145,7 +147,8 @@ int attn_prefill_paged(const void* q, const int32_t* cu_seqlens_q, int max_q, co
           "%s: a required pointer is NULL", fn);
   int shift = 0;
   while ((1 << shift) < page_size) ++shift;
-  return from_hip(attn::prefill_paged(q, cu_seqlens_q, max_q, k_pool, v_pool, block_table, seq_lens_k, B, h, h_kv,
+  return from_hip(attn::prefill_paged(q, cu_seqlens_q, max_q, k_pool, v_pool, block_table, seq_lens_k,
+                                      seq_lens_k_host, B, h, h_kv,
                                       shift, max_pages, num_pages, o, lse, dtype, scale, causal,
                                       static_cast<hipStream_t>(stream)),
                   fn);

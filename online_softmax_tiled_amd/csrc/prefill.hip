@@ -62,6 +62,8 @@
 // l = 0 (no visible key) or a zero row-mask entry gives +0.0 output and
 // LSE = -inf ("Merge normalized attention without averaging tile outputs",
 // last paragraph).
+#include <algorithm>
+
 #include "common.h"
 
 namespace attn {
@@ -82,7 +84,8 @@ constexpr int kKStr = kD + 8;       // 272 B
 constexpr int kVStr = kD + 32;      // 320 B
 constexpr int kKElems = kBc * kKStr;
 constexpr int kVElems = kBc * kVStr;
-constexpr float kTau = 8.f;         // allowed lag of the reference max (log2 units)
+constexpr float kTau = 8.f;
+constexpr int kMaxOrder = 512;      // sequences a paged launch can reorder         // allowed lag of the reference max (log2 units)
 
 struct PrefillParams {
   const uint16_t* q;
@@ -106,6 +109,10 @@ struct PrefillParams {
   const int32_t* seq_k;
   const int32_t* bt;
   int max_pages, num_pages, page_shift;   // page_size = 1 << page_shift
+  // Optional launch order of the sequences (longest context first), given
+  // when the host knows the key counts; n_order = 0 means natural order.
+  int n_order;
+  uint16_t order[kMaxOrder];
 };
 
 template <int DT, bool CAUSAL, bool KMASK, bool PAGED>
@@ -123,8 +130,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   const int half = lane >> 5;
 
   const int n_bk = p.B * p.h_kv;
-  const int bk = blockIdx.x % n_bk;
-  const int grp = p.n_grp - 1 - (int)(blockIdx.x / n_bk);
+  int bk = blockIdx.x % n_bk;
+  int grp = p.n_grp - 1 - (int)(blockIdx.x / n_bk);
+  if (PAGED && p.n_order > 0) {
+    // Sequences in the given order (a workgroup's run time follows its
+    // sequence's key count, so the longest go first); inside a sequence the
+    // KV head varies fastest, as above, then the row group, heaviest first.
+    const int per_seq = p.n_grp * p.h_kv;
+    const int r = (int)(blockIdx.x / per_seq);
+    const int rem = (int)(blockIdx.x - r * per_seq);
+    bk = p.order[r] * p.h_kv + rem % p.h_kv;
+    grp = p.n_grp - 1 - rem / p.h_kv;
+  }
   const int b = bk / p.h_kv;
   const int kvh = bk - b * p.h_kv;
 
@@ -177,19 +194,26 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   auto tile_byte = [&](int t, int i) {
     return (uint32_t)(((t * kBc + ((tid + kThreads * i) >> 4)) * kD + (tid & 15) * 8) * 2);
   };
-  // Paged: key row of chunk i of tile t, through the block table; keys past
-  // T_k or on a page id outside the pool read as zeros.
-  auto paged_row = [&](int t, int i) -> long {
+  // Paged: the page id (block-table entry, -1 past T_k) of staging row i of
+  // tile t, and the pool row it gives; keys past T_k or on a page id outside
+  // the pool read as zeros. Page ids are fetched one iteration before the
+  // K tile that needs them and reused for the V tile one iteration later,
+  // so no tile load waits on a block-table load.
+  auto page_of = [&](int t, int i) -> int {
     const int key = t * kBc + ((tid + kThreads * i) >> 4);
-    int page = key < T_k ? p.bt[(size_t)b * p.max_pages + (key >> p.page_shift)] : -1;
+    return key < T_k ? p.bt[(size_t)b * p.max_pages + (key >> p.page_shift)] : -1;
+  };
+  auto paged_row = [&](int t, int i, int page) -> long {
     if (page < 0 || page >= p.num_pages) return -1;
+    const int key = t * kBc + ((tid + kThreads * i) >> 4);
     return (((long)page << p.page_shift) + (key & ((1 << p.page_shift) - 1))) * p.h_kv + kvh;
   };
+  int pg_k[2] = {-1, -1}, pg_v[2] = {-1, -1}, pg_n[2] = {-1, -1};
   auto load_k = [&](int t) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       if (PAGED) {
-        const long r = paged_row(t, i);
+        const long r = paged_row(t, i, pg_k[i]);
         kreg[i] = r >= 0 ? load16(p.k + r * kD + (tid & 15) * 8) : u32x4{0u, 0u, 0u, 0u};
       } else {
         kreg[i] = buffer_load16(rk, tile_byte(t, i));
@@ -200,7 +224,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       if (PAGED) {
-        const long r = paged_row(t, i);
+        const long r = paged_row(t, i, pg_v[i]);
         vreg[i] = r >= 0 ? load16(p.v + r * kD + (tid & 15) * 8) : u32x4{0u, 0u, 0u, 0u};
       } else {
         vreg[i] = buffer_load16(rv, tile_byte(t, i));
@@ -263,18 +287,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     }
   };
   // Visible-key bits of tile t (KMASK): the key mask, or with PAGED the keys
-  // whose block-table entry names a page of the pool.
-  auto key_bits = [&](int t) -> uint64_t {
+  // whose block-table entry names a page of the pool. The per-lane value is
+  // loaded early (key_raw) and turned into bits late (key_ballot), so the
+  // ballot's wait falls where the tile loads are awaited anyway.
+  auto key_raw = [&](int t) -> int {
     const int key = t * kBc + lane;
-    if (PAGED) {
-      bool on = key < T_k;
-      if (on) {
-        const int page = p.bt[(size_t)b * p.max_pages + (key >> p.page_shift)];
-        on = page >= 0 && page < p.num_pages;
-      }
-      return __ballot(on);
-    }
-    return __ballot(key < T_k && p.key_mask[(size_t)b * T_k + key] != 0);
+    if (key >= T_k) return PAGED ? -1 : 0;
+    return PAGED ? p.bt[(size_t)b * p.max_pages + (key >> p.page_shift)] : (int)p.key_mask[(size_t)b * T_k + key];
+  };
+  auto key_ballot = [&](int raw) -> uint64_t {
+    return __ballot(PAGED ? (raw >= 0 && raw < p.num_pages) : raw != 0);
   };
 
   f32x16 sc[2];     // scores of tile j
@@ -286,15 +308,32 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   sc[1] = f32x16{};
 
   if (n_tiles > 0) {
+    if (PAGED) {
+      pg_k[0] = page_of(0, 0);
+      pg_k[1] = page_of(0, 1);
+      pg_v[0] = pg_k[0];
+      pg_v[1] = pg_k[1];
+    }
     load_k(0);
     load_v(0);
     store_k(0);
     store_v(0);
     if (n_tiles > 1) {
+      if (PAGED) {
+        pg_k[0] = page_of(1, 0);
+        pg_k[1] = page_of(1, 1);
+      }
       load_k(1);
       store_k(1);
     }
-    if (KMASK) kbits = key_bits(0);
+    if (KMASK) kbits = key_ballot(key_raw(0));
+  }
+  if (PAGED) {
+    // pages of tile 1 for V(1) and of tile 2 for K(2), used in iteration 0
+    pg_v[0] = page_of(1, 0);
+    pg_v[1] = page_of(1, 1);
+    pg_k[0] = page_of(2, 0);
+    pg_k[1] = page_of(2, 1);
   }
   // V slot 2 is read (with P = 0) in the first iteration.
   for (int i = tid; i < kVElems / 8; i += kThreads) store16(&lds_v[2][i * 8], u32x4{});
@@ -308,8 +347,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     // from the rescale below to the barrier.
     load_k(j + 2);
     load_v(j + 1);
-    uint64_t kbits_next = ~0ull;
-    if (KMASK) kbits_next = key_bits(j + 1);
+    if (PAGED) {
+      pg_n[0] = page_of(j + 3, 0);
+      pg_n[1] = page_of(j + 3, 1);
+    }
+    int kraw = 0;
+    if (KMASK) kraw = key_raw(j + 1);
     // O~ still holds PV(j-2) at the old reference; PV(j-1) below uses the
     // weights of the current one.
     if (__ballot(alpha != 1.f)) {
@@ -440,7 +483,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     for (int i = 0; i < 4; ++i) pp[i] = pn[i];
     sc[0] = sn[0];
     sc[1] = sn[1];
-    kbits = kbits_next;
+    if (KMASK) kbits = key_ballot(kraw);
+    if (PAGED) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        pg_v[i] = pg_k[i];
+        pg_k[i] = pg_n[i];
+      }
+    }
 
     store_k(j & 1);
     store_v((j + 1) % 3);
@@ -527,10 +577,19 @@ hipError_t prefill_fwd(const void* q, const void* k, const void* v, const uint8_
 // count of the batch (it sizes the grid; workgroups past a sequence's rows
 // exit at once), T_k the largest key count the block table can address.
 hipError_t prefill_paged(const void* q, const int32_t* cu_seqlens_q, int max_q, const void* k_pool,
-                         const void* v_pool, const int32_t* block_table, const int32_t* seq_lens_k, int B, int h,
-                         int h_kv, int page_shift, int max_pages, int num_pages, void* o, float* lse, int dtype,
-                         float scale, int causal, hipStream_t stream) {
+                         const void* v_pool, const int32_t* block_table, const int32_t* seq_lens_k,
+                         const int32_t* seq_lens_k_host, int B, int h, int h_kv, int page_shift, int max_pages,
+                         int num_pages, void* o, float* lse, int dtype, float scale, int causal,
+                         hipStream_t stream) {
   PrefillParams p = common_params(q, k_pool, v_pool, o, lse, B, h, h_kv, max_q, max_pages << page_shift, scale);
+  if (seq_lens_k_host != nullptr && B <= kMaxOrder) {
+    // Longest context first (stable), so the longest workgroups start first.
+    int idx[kMaxOrder];
+    for (int i = 0; i < B; ++i) idx[i] = i;
+    std::stable_sort(idx, idx + B, [&](int a, int c) { return seq_lens_k_host[a] > seq_lens_k_host[c]; });
+    for (int i = 0; i < B; ++i) p.order[i] = (uint16_t)idx[i];
+    p.n_order = B;
+  }
   p.cu_q = cu_seqlens_q;
   p.seq_k = seq_lens_k;
   p.bt = block_table;

@@ -211,7 +211,7 @@ def paged_prefill_call(lib, **kw):
     args.update(kw)
     p = lambda x: None if x is None else ctypes.c_void_p(x)
     return lib.attn_prefill_paged(p(args["q"]), p(args["cu"]), args["max_q"], p(args["kp"]), p(args["vp"]),
-                                  p(args["bt"]), p(args["sk"]), args["B"], args["h"], args["h_kv"], args["d"],
+                                  p(args["bt"]), p(args["sk"]), None, args["B"], args["h"], args["h_kv"], args["d"],
                                   args["page"], args["max_pages"], args["num_pages"], args["dtype"], args["scale"],
                                   args["causal"], p(args["o"]), p(args["lse"]), None)
 

@@ -469,14 +469,15 @@ def test_merge_lse_llama3_8b_shape_sampled():
 
 # ------------------------------------------------------------------ paged (chunked) prefill
 
-def _run_paged_prefill(c, causal, rows_per_seq=None):
+def _run_paged_prefill(c, causal, rows_per_seq=None, host_order=False):
     """attn_prefill_paged on a chunked-prefill case; checks every sequence
     against the oracle over its ground-truth contiguous K/V (optionally on a
     sample of its query rows)."""
     from online_softmax_tiled_amd.workloads import DTYPES
     q = to_dev(c["q"])
     o, lse = api.prefill_paged(q, to_dev(c["cu_seqlens_q"]), c["max_q"], to_dev(c["k_pool"]), to_dev(c["v_pool"]),
-                               to_dev(c["block_table"]), to_dev(c["seq_lens_k"]), causal=causal, scale=c["scale"])
+                               to_dev(c["block_table"]), to_dev(c["seq_lens_k"]), causal=causal, scale=c["scale"],
+                               seq_lens_k_host=c["seq_lens_k"] if host_order else None)
     torch.cuda.synchronize()
     cu = c["cu_seqlens_q"]
     excluded = c.get("excluded_keys", {})
@@ -501,13 +502,13 @@ def _run_paged_prefill(c, causal, rows_per_seq=None):
         assert_outputs(ob, lb, o_ref, lse_ref, c["dtype"], f"paged prefill seq {b} ({tq} new / {tk} keys)")
 
 
-@pytest.mark.parametrize("dtype,page_size,causal", [("bf16", 16, True), ("f16", 32, True), ("bf16", 64, False),
-                                                    ("bf16", 16, False)])
-def test_paged_prefill_small(dtype, page_size, causal):
+@pytest.mark.parametrize("dtype,page_size,causal,host_order", [("bf16", 16, True, False), ("f16", 32, True, True),
+                                                               ("bf16", 64, False, True), ("bf16", 16, False, False)])
+def test_paged_prefill_small(dtype, page_size, causal, host_order):
     from online_softmax_tiled_amd.workloads import make_chunked_prefill
     c = make_chunked_prefill(5, 8, 2, 128, dtype, seed=page_size + 3 * causal, ctx_range=(1, 300),
                              new_range=(1, 120), page_size=page_size, spare_pages=3)
-    _run_paged_prefill(c, causal)
+    _run_paged_prefill(c, causal, host_order=host_order)
 
 
 def test_paged_prefill_edge_sequences():
@@ -534,7 +535,7 @@ def test_paged_prefill_chunked_llama3_8b_b8():
     # the measured chunked-prefill workload, in the bench's launch
     # configuration, on 96 sampled query rows per sequence
     c = make_config("chunked_prefill_llama3_8b_b8")
-    _run_paged_prefill(c, True, rows_per_seq=96)
+    _run_paged_prefill(c, True, rows_per_seq=96, host_order=True)
 
 
 def test_paged_prefill_matches_contiguous_prefill():
