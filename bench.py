@@ -261,7 +261,9 @@ def bench_decode_contiguous(steps, warmup, dev, copies=40):
                 rotated_kv_copies=copies, timing="HIP graph of split+merge steps, replayed")
 
 
-def bench_decode_paged(steps, warmup, dev, dec):
+def bench_decode_paged(steps, warmup, dev, dec, fixed_split=None, gather=True):
+    """Paged split-KV decode on the 64-sequence workload, with the adaptive
+    plan or (``fixed_split``) a batch-invariant fixed split length."""
     import torch
     from online_softmax_tiled_amd import api
     q = dec["q"].to(dev)
@@ -270,7 +272,10 @@ def bench_decode_paged(steps, warmup, dev, dec):
     bt = torch.from_numpy(dec["block_table"]).to(dev)
     B, h, d = q.shape
     h_kv = kp.shape[2]
-    chunk, splits = api.decode_plan(dec["seq_lens"], h, h_kv, device=dev)
+    if fixed_split is None:
+        chunk, splits = api.decode_plan(dec["seq_lens"], h, h_kv, device=dev)
+    else:
+        chunk, splits = api.decode_plan_fixed(dec["seq_lens"], fixed_split)
     po = torch.empty((B, h, splits, d), dtype=torch.float32, device=dev)
     pm = torch.empty((B, h, splits), dtype=torch.float32, device=dev)
     pl = torch.empty_like(pm)
@@ -288,6 +293,10 @@ def bench_decode_paged(steps, warmup, dev, dec):
 
     ms_split, _ = time_loop(split_only, steps, warmup)
     ms, _ = time_loop(full, steps, warmup)
+    if not gather:
+        return dict(kv_bytes=kv_bytes, us_per_step=ms * 1e3, split_us=ms_split * 1e3,
+                    gbs=kv_bytes / (ms * 1e-3) / 1e9, frac_hbm=kv_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                    plan=[chunk, splits])
     ms_graph = time_graph(full, 10, reps=2)
     s_max = int(dec["seq_lens"].max())
     gout = torch.empty((B, h_kv, s_max, d), dtype=q.dtype, device=dev)
@@ -428,6 +437,9 @@ def main():
         log(f"decode paged b64: {r4['us_per_step']:.1f} us/step ({r4['split_us']:.1f} split), {r4['gbs']:.0f} GB/s; "
             f"gather {r4['gather_gbs']:.0f} GB/s")
         decode[r4.pop("workload")] = r4
+        r5 = bench_decode_paged(max(20, args.steps), 3, dev, dec, fixed_split=2048, gather=False)
+        log(f"decode paged b64, batch-invariant split 2048: {r5['us_per_step']:.1f} us/step, {r5['gbs']:.0f} GB/s")
+        decode["paged_decode_llama3_8b_b64_fixed_split_2048"] = r5
         for v in decode.values():
             for key in list(v):
                 if isinstance(v[key], float):

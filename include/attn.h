@@ -134,6 +134,15 @@ int attn_prefill_paged(const void* q, const int32_t* cu_seqlens_q, int max_q,
  *                 the split dimension of the partial buffers.
  * The split count of sequence b is n_b = ceil(seq_lens[b] / chunk_keys);
  * units = h_kv * sum_b n_b is at least num_cus whenever the keys allow it.
+ *
+ * The plan depends on the whole batch, so a sequence's output bits may change
+ * with its companions. For batch-invariant results ([DA] section "Split-K
+ * breaks bitwise reproducibility": fix the split tile so the split count is a
+ * function of the sequence length alone) skip this plan and pass a fixed
+ * chunk_keys (a multiple of 16, e.g. 2048) with max_splits = ceil(max_b
+ * seq_lens[b] / chunk_keys) to attn_decode_split and attn_merge_states: a
+ * row's splits and the merge's summation order then depend only on its own
+ * length.
  */
 int attn_decode_plan(int B, const int32_t* seq_lens_host, int h, int h_kv, int d_h,
                      int num_cus, int32_t* chunk_keys, int32_t* max_splits);

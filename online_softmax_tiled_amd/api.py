@@ -190,6 +190,19 @@ def decode_plan(seq_lens, h, h_kv, num_cus=None, d=HEAD_DIM, device=None):
     return chunk.value, splits.value
 
 
+def decode_plan_fixed(seq_lens, split_keys=2048):
+    """(chunk_keys, max_splits) for a split length that does not depend on the
+    batch: each sequence's output bits then depend only on its own query,
+    keys and ``split_keys`` (batch-invariant decode). ``split_keys`` must be a
+    positive multiple of 16."""
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    split_keys = int(split_keys)
+    if split_keys <= 0 or split_keys % 16:
+        raise ValueError(f"split_keys must be a positive multiple of 16 (got {split_keys})")
+    s_max = int(lens.max()) if lens.size else 0
+    return split_keys, max(1, -(-s_max // split_keys))
+
+
 def decode_split(q, k, v, seq_lens, chunk_keys, max_splits, block_table=None, page_size=16,
                  scale=None, part_o=None, part_m=None, part_l=None):
     """Stage 1 of split-KV decode via attn_decode_split.

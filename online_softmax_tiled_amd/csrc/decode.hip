@@ -77,9 +77,14 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
   using E = Elem<DT>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[kWaves * kWaveLds];
 
-  const int split = blockIdx.x;
+  // Consecutive workgroups (dealt round-robin to the 8 XCDs) take
+  // consecutive splits of one (sequence, head), rotated by (head + sequence)
+  // so that the split index does not follow the XCD: otherwise, with a
+  // multiple of 8 splits, one XCD would get every sequence's split 0 and
+  // another only the longest sequences' last splits.
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
+  const int split = (int)((blockIdx.x + blockIdx.y + blockIdx.z) % (unsigned)p.max_splits);
   const int s_raw = p.seq_lens[b];
   if (s_raw <= 0) return;
   const int n_split = min(p.max_splits, (s_raw + p.chunk - 1) / p.chunk);

@@ -13,12 +13,12 @@
 // attention without averaging tile outputs", paragraph on fully masked
 // tiles).
 //
-// Layout: one workgroup of 256 threads per (sequence, head, d-slice). With
-// many splits the head dimension is cut into ND = 4 slices so that more
-// workgroups share the partial traffic. Inside a workgroup, thread (s, f)
-// of SL split lanes x FL float4 lanes sums splits s, s + SL, ... for 4
-// consecutive d values, with the loads of 4 splits in flight at a time; the
-// SL partial sums are then added through LDS.
+// Layout: one workgroup per (sequence, head, d-slice). With many splits the
+// head dimension is cut into ND = 4 slices so that more workgroups share the
+// partial traffic. Inside a workgroup, thread (s, f) of 32 split lanes x FL
+// float4 lanes sums splits s, s + 32, ... for 4 consecutive d values, with
+// the loads of U splits in flight at a time; the 32 lane sums are then added
+// through LDS in lane order.
 #include "common.h"
 
 namespace attn {
@@ -43,16 +43,28 @@ __device__ __forceinline__ float wave_max(float x) {
 }
 
 // ND: d-slices per (sequence, head); each slice is kD / ND values, handled
-// by FL = kD / ND / 4 float4 lanes and SL = 256 / FL split lanes.
-template <int DT, int ND>
-__global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
+// by FL = kD / ND / 4 float4 lanes and kSL = 32 split lanes (FL * 32
+// threads: 1024 for one slice, 256 for four). Split lane s sums splits s,
+// s + 32, s + 64, ... in that order, with U partials in flight, and the 32
+// lane sums are added in lane order. The
+// summation order of a row therefore depends only on its own split count,
+// never on ND, on the batch or on max_splits: with a split length that does
+// not depend on the batch, every row's bits are batch-invariant ("Decode
+// attention: FlashDecoding, split-K, paged kernels", section "Split-K breaks
+// bitwise reproducibility": fix the split tile so the count is a function of
+// the sequence length alone).
+constexpr int kSL = 32;
+
+template <int DT, int ND, int U>
+__global__ __launch_bounds__(kD / ND / 4 * kSL) void merge_kernel(MergeParams p) {
   using E = Elem<DT>;
   constexpr int kSlice = kD / ND;
   constexpr int FL = kSlice / 4;
-  constexpr int SL = 256 / FL;
-  __shared__ float red_m[4];
-  __shared__ __attribute__((aligned(16))) float red_o[SL][kSlice];
-  __shared__ float red_l[SL];
+  constexpr int NT = FL * kSL;
+  constexpr int NW = NT / 64;
+  __shared__ float red_m[NW];
+  __shared__ __attribute__((aligned(16))) float red_o[kSL][kSlice];
+  __shared__ float red_l[kSL];
 
   const int bh = blockIdx.x;
   const int d0 = blockIdx.y * kSlice;
@@ -63,14 +75,16 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   const size_t base = (size_t)bh * p.max_splits;
 
   float mloc = -INFINITY;
-  for (int i = tid; i < n; i += 256) {
+  for (int i = tid; i < n; i += NT) {
     const float mi = p.part_m[base + i];
     if (p.part_l[base + i] > 0.f) mloc = fmaxf(mloc, mi);
   }
   mloc = wave_max(mloc);
   if ((tid & 63) == 0) red_m[tid >> 6] = mloc;
   __syncthreads();
-  const float big = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+  float big = red_m[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) big = fmaxf(big, red_m[w]);
 
   uint16_t* op = p.o + (size_t)bh * kD + d0;
   if (big == -INFINITY) {   // no visible key in any split: zero output
@@ -83,19 +97,19 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   const int d = (tid % FL) * 4;
   f32x4 acc = f32x4{};
   float lacc = 0.f;
-  for (int i0 = sl; i0 < n; i0 += 4 * SL) {
-    float li[4], mi[4];
-    f32x4 oi[4];
+  for (int i0 = sl; i0 < n; i0 += U * kSL) {
+    float li[U], mi[U];
+    f32x4 oi[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * SL;
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kSL;
       const bool ok = i < n;
       li[u] = ok ? p.part_l[base + i] : 0.f;
       mi[u] = ok ? p.part_m[base + i] : -INFINITY;
       oi[u] = ok ? *reinterpret_cast<const f32x4*>(&p.part_o[(base + i) * kD + d0 + d]) : f32x4{};
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       if (li[u] > 0.f) {
         const float w = fast_exp2((mi[u] - big) * kLog2e);
         lacc += w * li[u];
@@ -109,11 +123,11 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   if (tid < kSlice / 2) {
     float l_all = 0.f;
 #pragma unroll
-    for (int s = 0; s < SL; ++s) l_all += red_l[s];
+    for (int s = 0; s < kSL; ++s) l_all += red_l[s];
     const int dd = tid * 2;
     float o0 = 0.f, o1 = 0.f;
-#pragma unroll 8
-    for (int s = 0; s < SL; ++s) {
+#pragma unroll
+    for (int s = 0; s < kSL; ++s) {
       o0 += red_o[s][dd];
       o1 += red_o[s][dd + 1];
     }
@@ -125,11 +139,12 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
 
 template <int DT>
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
-  // Many splits and few (sequence, head) pairs: cut d into 4 slices.
+  // Many splits and few (sequence, head) pairs: cut d into 4 slices so that
+  // more workgroups share the partial traffic (same bits as one slice).
   if (p.max_splits >= 64 && (long)p.B * p.h < 1024) {
-    hipLaunchKernelGGL((merge_kernel<DT, 4>), dim3((unsigned)(p.B * p.h), 4), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((merge_kernel<DT, 4, 4>), dim3((unsigned)(p.B * p.h), 4), dim3(kD / 4 / 4 * kSL), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((merge_kernel<DT, 1>), dim3((unsigned)(p.B * p.h), 1), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((merge_kernel<DT, 1, 4>), dim3((unsigned)(p.B * p.h), 1), dim3(kD / 4 * kSL), 0, stream, p);
   }
   return hipGetLastError();
 }

@@ -555,3 +555,49 @@ def test_paged_prefill_matches_contiguous_prefill():
     torch.cuda.synchronize()
     assert torch.equal(o_p.permute(1, 0, 2).unsqueeze(0).contiguous().view(torch.int16), o_c.view(torch.int16))
     assert torch.equal(l_p.T.unsqueeze(0).contiguous(), l_c)
+
+
+# ------------------------------------------------------------------ batch-invariant decode
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_decode_batch_invariant_with_fixed_split(paged):
+    # One sequence decoded alone and inside a batch whose longest sequence
+    # needs >= 64 splits (the merge then runs its 4-slice layout): with the
+    # same fixed split length its output bits are identical.
+    h, h_kv, d, split = 8, 1, 128, 256
+    lens = [3000, 100, 20000, 777, 5000]
+    dec = make_decode(len(lens), h, h_kv, d, "bf16", seed=31, seq_lens=lens, paged=paged, page_size=16)
+    alone = make_decode(1, h, h_kv, d, "bf16", seed=32, seq_lens=[3000], paged=paged, page_size=16)
+    # sequence 0 of the batch gets the lone sequence's query, keys and values
+    dec["q"][0] = alone["q"][0]
+    if paged:
+        kp, vp, bt = dec["k_pool"], dec["v_pool"], dec["block_table"]
+        kp_a, vp_a, bt_a = alone["k_pool"], alone["v_pool"], alone["block_table"]
+        for p_log in range((3000 + 15) // 16):
+            kp[bt[0, p_log]] = kp_a[bt_a[0, p_log]]
+            vp[bt[0, p_log]] = vp_a[bt_a[0, p_log]]
+    else:
+        dec["k"][0, :, :3000] = alone["k"][0]
+        dec["v"][0, :, :3000] = alone["v"][0]
+
+    def run(c):
+        sl = to_dev(np.asarray(c["seq_lens"], dtype=np.int32))
+        plan = api.decode_plan_fixed(c["seq_lens"], split)
+        if paged:
+            o, lse, _ = api.decode(to_dev(c["q"]), to_dev(c["k_pool"]), to_dev(c["v_pool"]), sl,
+                                   block_table=to_dev(c["block_table"]), page_size=16, scale=c["scale"], plan=plan)
+        else:
+            o, lse, _ = api.decode(to_dev(c["q"]), to_dev(c["k"]), to_dev(c["v"]), sl, scale=c["scale"], plan=plan)
+        torch.cuda.synchronize()
+        return o, lse, plan
+
+    o_b, lse_b, plan_b = run(dec)
+    o_a, lse_a, plan_a = run(alone)
+    assert plan_b[1] >= 64 and plan_a[1] < 64     # the two merges take different layouts
+    assert torch.equal(o_b[0].view(torch.int16), o_a[0].view(torch.int16))
+    assert torch.equal(lse_b[0], lse_a[0])
+    o_ref, lse_ref = decode_ref(alone["q"], alone["k_seqs"], alone["v_seqs"], alone["seq_lens"], alone["scale"])
+    assert_outputs(o_a, lse_a.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16", "batch-invariant decode")
+    # and run to run
+    o_b2, _, _ = run(dec)
+    assert torch.equal(o_b2.view(torch.int16), o_b.view(torch.int16))
