@@ -223,6 +223,38 @@ def bench_merge_lse(steps, warmup, dev, copies=3):
                 rotated_input_sets=copies)
 
 
+def bench_decode_large_group(steps, warmup, dev):
+    """Decode with a 128-head group on one KV head (g = 128, tiled in blocks
+    of 16 heads): 32 sequences of 32768 contiguous keys, 537 MB of K+V (more
+    than the 256 MB last-level cache), synthetic N(0,1) drawn on the device.
+    GB/s = K+V bytes / (split + merge time)."""
+    import torch
+    from online_softmax_tiled_amd import api
+    B, h, h_kv, s, d = 32, 128, 1, 32768, 128
+    g = torch.Generator(device=dev).manual_seed(1007)
+    q = torch.randn((B, h, d), generator=g, device=dev).to(torch.bfloat16)
+    k = torch.randn((B, h_kv, s, d), generator=g, device=dev).to(torch.bfloat16)
+    v = torch.randn((B, h_kv, s, d), generator=g, device=dev).to(torch.bfloat16)
+    lens = np.full(B, s, dtype=np.int32)
+    sl = torch.from_numpy(lens).to(dev)
+    chunk, splits = api.decode_plan(lens, h, h_kv, device=dev)
+    po = torch.empty((B, h, splits, d), dtype=torch.float32, device=dev)
+    pm = torch.empty((B, h, splits), dtype=torch.float32, device=dev)
+    pl = torch.empty_like(pm)
+    o = torch.empty((B, h, d), dtype=q.dtype, device=dev)
+    lse = torch.empty((B, h), dtype=torch.float32, device=dev)
+    kv_bytes = 2 * B * h_kv * s * d * 2
+
+    def full(i=0):
+        api.decode_split(q, k, v, sl, chunk, splits, part_o=po, part_m=pm, part_l=pl)
+        api.merge_states(po, pm, pl, sl, chunk, q.dtype, out=o, lse=lse)
+
+    ms, _ = time_loop(full, steps, warmup)
+    return dict(kv_bytes=kv_bytes, us_per_step=ms * 1e3, gbs=kv_bytes / (ms * 1e-3) / 1e9,
+                frac_hbm=kv_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, plan=[chunk, splits],
+                shape="B=32 h=128 h_kv=1 s=32768 d=128 bf16")
+
+
 def bench_decode_contiguous(steps, warmup, dev, copies=40):
     import torch
     from online_softmax_tiled_amd import api
@@ -440,6 +472,9 @@ def main():
         r5 = bench_decode_paged(max(20, args.steps), 3, dev, dec, fixed_split=2048, gather=False)
         log(f"decode paged b64, batch-invariant split 2048: {r5['us_per_step']:.1f} us/step, {r5['gbs']:.0f} GB/s")
         decode["paged_decode_llama3_8b_b64_fixed_split_2048"] = r5
+        r6 = bench_decode_large_group(max(20, args.steps), 3, dev)
+        log(f"decode g=128 b32 s32768: {r6['us_per_step']:.1f} us/step, {r6['gbs']:.0f} GB/s, plan {r6['plan']}")
+        decode["decode_g128_b32_s32768"] = r6
         for v in decode.values():
             for key in list(v):
                 if isinstance(v[key], float):

@@ -38,14 +38,14 @@ hipError_t prefill_paged(const void* q, const int32_t* cu_seqlens_q, int max_q, 
                          hipStream_t stream);
 hipError_t merge_lse(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, void* o,
                      float* lse, int rows, int dtype, hipStream_t stream);
-int decode_plan(int B, const int32_t* seq_lens, int h_kv, int num_cus, int32_t* chunk_keys,
+int decode_plan(int B, const int32_t* seq_lens, int units_per_split, int num_cus, int32_t* chunk_keys,
                 int32_t* max_splits);
 }  // namespace attn
 
 namespace {
 
 constexpr int kHeadDim = 128;
-constexpr int kMaxGroup = 16;   // decode: query heads per KV head
+constexpr int kMaxGroup = 256;  // decode: query heads per KV head (tiled in blocks of 16)
 constexpr int kMaxSeq = 1 << 23;  // prefill: keys or queries per (batch, head)
 
 thread_local std::string g_last_error;
@@ -166,7 +166,8 @@ int attn_decode_plan(int B, const int32_t* seq_lens_host, int h, int h_kv, int d
   REQUIRE(B == 0 || seq_lens_host, ATTN_ERR_INVALID, "%s: seq_lens_host must not be NULL", fn);
   for (int b = 0; b < B; ++b)
     REQUIRE(seq_lens_host[b] >= 0, ATTN_ERR_INVALID, "%s: seq_lens[%d] = %d is negative", fn, b, seq_lens_host[b]);
-  attn::decode_plan(B, seq_lens_host, h_kv, num_cus, chunk_keys, max_splits);
+  // Workgroups per split: one per KV head and head block of 16 query heads.
+  attn::decode_plan(B, seq_lens_host, h_kv * ((h / h_kv + 15) / 16), num_cus, chunk_keys, max_splits);
   return ok();
 }
 
@@ -180,6 +181,8 @@ int attn_decode_split(const void* q, const void* k, const void* v, const int32_t
   if (int e = check_scale(fn, scale)) return e;
   REQUIRE(h / h_kv <= kMaxGroup, ATTN_ERR_UNSUPPORTED, "%s: %d query heads per KV head (at most %d supported)",
           fn, h / h_kv, kMaxGroup);
+  REQUIRE((((long)max_splits * h_kv * B + 7) / 8) * 8 * ((h / h_kv + 15) / 16) < (1L << 31), ATTN_ERR_UNSUPPORTED,
+          "%s: grid too large", fn);
   REQUIRE(B >= 0, ATTN_ERR_INVALID, "%s: negative batch %d", fn, B);
   REQUIRE(chunk_keys > 0 && chunk_keys % 16 == 0, ATTN_ERR_INVALID,
           "%s: chunk_keys must be a positive multiple of 16 (got %d)", fn, chunk_keys);

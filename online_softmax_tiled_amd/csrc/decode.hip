@@ -15,8 +15,15 @@
 // the split round-robin, each with its own state, and merge the four states
 // through LDS at the end.
 //
-// Per 32-key tile and wave (v_mfma_f32_16x16x32, the g <= 16 query heads of
-// the group as the 16 columns, unused columns zero):
+// Groups of more than 16 query heads (g up to 128 for MLA-style models) are
+// tiled into ceil(g / 16) head blocks, one workgroup each, as the pages'
+// grouped-head decode does ("Decode attention: FlashDecoding, split-K, paged
+// kernels", section "SGLang: a split count computed per sequence, on
+// device": 16 heads per block, the group tiled across blocks); the blocks of
+// one split read the same keys, which the shared last-level cache serves.
+//
+// Per 32-key tile and wave (v_mfma_f32_16x16x32, the up to 16 query heads of
+// the head block as the 16 columns, unused columns zero):
 // K and V are read exactly once, with non-temporal loads (on the 64-sequence
 // paged workload 5.69 TB/s against 5.34-5.50 with ordinary loads).
 //   S^T = K Q^T: A = K rows loaded straight from global memory (lane l: key
@@ -53,6 +60,7 @@ struct DecodeParams {
   int max_pages, page_size, num_pages;
   int s_max;
   int B, h, h_kv, g;
+  int n_hb;    // head blocks of 16 per KV head = ceil(g / 16)
   int chunk, max_splits;
   float c;     // scale * log2(e)
 };
@@ -72,7 +80,10 @@ __device__ __forceinline__ float sum_rows16(float x) {
 // group a covers keys 4a..4a+3 and 16+4a..16+4a+3, stored contiguously.
 __device__ __forceinline__ int vt_pos(int kk) { return ((kk & 12) << 1) | ((kk & 16) >> 2) | (kk & 3); }
 
-template <int DT, bool PAGED>
+// STREAM: K/V loads carry the non-temporal hint (each byte read once). With
+// several head blocks the same keys are read by several workgroups, and the
+// loads must leave them in the caches.
+template <int DT, bool PAGED, bool STREAM>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
   using E = Elem<DT>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[kWaves * kWaveLds];
@@ -82,9 +93,25 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
   // so that the split index does not follow the XCD: otherwise, with a
   // multiple of 8 splits, one XCD would get every sequence's split 0 and
   // another only the longest sequences' last splits.
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
-  const int split = (int)((blockIdx.x + blockIdx.y + blockIdx.z) % (unsigned)p.max_splits);
+  unsigned gx = blockIdx.x, gy = blockIdx.y, gz = blockIdx.z;
+  int hb = 0;
+  if (p.n_hb > 1) {
+    // 1-D grid: the n_hb head blocks of one (split, KV head, sequence) unit
+    // sit 8 apart in launch order, so they land on the same XCD close in
+    // time and re-read the unit's keys from that XCD's L2.
+    const unsigned L = blockIdx.x;
+    hb = (int)((L >> 3) % (unsigned)p.n_hb);
+    const unsigned u = (L & 7u) + 8u * (L / (8u * (unsigned)p.n_hb));
+    if (u >= (unsigned)(p.max_splits * p.h_kv * p.B)) return;
+    gx = u % (unsigned)p.max_splits;
+    gy = (u / (unsigned)p.max_splits) % (unsigned)p.h_kv;
+    gz = u / ((unsigned)p.max_splits * (unsigned)p.h_kv);
+  }
+  const int kvh = (int)gy;
+  const int hb0 = hb * 16;               // first head of this block in the group
+  const int hn = min(16, p.g - hb0);     // heads in this block
+  const int b = (int)gz;
+  const int split = (int)((gx + gy + gz) % (unsigned)p.max_splits);
   const int s_raw = p.seq_lens[b];
   if (s_raw <= 0) return;
   const int n_split = min(p.max_splits, (s_raw + p.chunk - 1) / p.chunk);
@@ -103,8 +130,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
   // Q^T as B operands: lane holds head col, d in [8*row + 32c, +8).
   u32x4 qf[4];
   {
-    const bool ok = col < p.g;
-    const uint16_t* qp = p.q + ((size_t)b * p.h + kvh * p.g + (ok ? col : 0)) * kD + row * 8;
+    const bool ok = col < hn;
+    const uint16_t* qp = p.q + ((size_t)b * p.h + kvh * p.g + hb0 + (ok ? col : 0)) * kD + row * 8;
 #pragma unroll
     for (int c = 0; c < 4; ++c) qf[c] = ok ? load16(qp + c * 32) : u32x4{0, 0, 0, 0};
   }
@@ -146,7 +173,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
       const bool ok = bok[kb] && kt + kb * 16 + col < k_hi;
       const uint16_t* kp = p.k + (rbase[kb] + (ok ? col : 0) * kstride) * kD + row * 8;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) kf[kb][c] = ok ? load16_nt(kp + c * 32) : u32x4{0, 0, 0, 0};
+      for (int c = 0; c < 4; ++c)
+        kf[kb][c] = ok ? (STREAM ? load16_nt(kp + c * 32) : load16(kp + c * 32)) : u32x4{0, 0, 0, 0};
     }
     // V: lane (d-chunk col, key group row) loads keys 4*row+i and 16+4*row+i.
     u32x4 vf[8];
@@ -155,7 +183,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
       const int kb = i >> 2;
       const int ko = row * 4 + (i & 3);
       const bool ok = bok[kb] && kt + kb * 16 + ko < k_hi;
-      vf[i] = ok ? load16_nt(p.v + (rbase[kb] + ko * kstride) * kD + col * 8) : u32x4{0, 0, 0, 0};
+      const uint16_t* vp = p.v + (rbase[kb] + ko * kstride) * kD + col * 8;
+      vf[i] = ok ? (STREAM ? load16_nt(vp) : load16(vp)) : u32x4{0, 0, 0, 0};
     }
 
     f32x4 s[2];
@@ -238,7 +267,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
   __syncthreads();
 
   // 256 threads: head j = tid / 32 (+8 per pass), 4 d-values each.
-  for (int j = tid >> 5; j < p.g; j += 8) {
+  for (int j = tid >> 5; j < hn; j += 8) {
     const int d = (tid & 31) * 4;
     float mw[kWaves], m_all = -INFINITY;
 #pragma unroll
@@ -256,7 +285,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
         o += wt * *reinterpret_cast<const f32x4*>(&red[(w * 16 + j) * kD + d]);
       }
     }
-    const size_t hs = (size_t)b * p.h + kvh * p.g + j;
+    const size_t hs = (size_t)b * p.h + kvh * p.g + hb0 + j;
     *reinterpret_cast<f32x4*>(&p.part_o[(hs * p.max_splits + split) * kD + d]) = o;
     if ((tid & 31) == 0) {
       p.part_m[hs * p.max_splits + split] = m_all == -INFINITY ? -INFINITY : m_all * kLn2;
@@ -267,11 +296,17 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
 
 template <int DT>
 hipError_t dispatch_decode(const DecodeParams& p, bool paged, hipStream_t stream) {
-  const dim3 grid((unsigned)p.max_splits, (unsigned)p.h_kv, (unsigned)p.B);
-  if (paged)
-    hipLaunchKernelGGL((decode_split_kernel<DT, true>), grid, dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL((decode_split_kernel<DT, false>), grid, dim3(256), 0, stream, p);
+  const long units = (long)p.max_splits * p.h_kv * p.B;
+  const dim3 grid = p.n_hb == 1 ? dim3((unsigned)p.max_splits, (unsigned)p.h_kv, (unsigned)p.B)
+                                : dim3((unsigned)(((units + 7) / 8) * 8 * p.n_hb));
+  const bool stream_kv = p.n_hb == 1;
+  if (paged) {
+    if (stream_kv) hipLaunchKernelGGL((decode_split_kernel<DT, true, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((decode_split_kernel<DT, true, false>), grid, dim3(256), 0, stream, p);
+  } else {
+    if (stream_kv) hipLaunchKernelGGL((decode_split_kernel<DT, false, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((decode_split_kernel<DT, false, false>), grid, dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
@@ -299,6 +334,7 @@ hipError_t decode_split(const void* q, const void* k, const void* v, const int32
   p.h = h;
   p.h_kv = h_kv;
   p.g = h / h_kv;
+  p.n_hb = (p.g + 15) / 16;
   p.chunk = chunk_keys;
   p.max_splits = max_splits;
   p.c = scale * kLog2e;
@@ -317,7 +353,8 @@ hipError_t decode_split(const void* q, const void* k, const void* v, const int32
 // shape 1280-key slices read 5.5 TB/s where 960-key slices read 5.2), never
 // below 128 keys per slice unless that is needed to reach one workgroup per
 // CU, never below 64.
-int decode_plan(int B, const int32_t* seq_lens, int h_kv, int num_cus, int32_t* chunk_keys,
+// units_per_split: workgroups one split launches (KV heads x head blocks).
+int decode_plan(int B, const int32_t* seq_lens, int units_per_split, int num_cus, int32_t* chunk_keys,
                 int32_t* max_splits) {
   long total = 0;
   int s_max = 0;
@@ -328,10 +365,10 @@ int decode_plan(int B, const int32_t* seq_lens, int h_kv, int num_cus, int32_t* 
   auto units = [&](long chunk) {
     long u = 0;
     for (int b = 0; b < B; ++b) u += (seq_lens[b] + chunk - 1) / chunk;
-    return u * h_kv;
+    return u * units_per_split;
   };
   const long target = 12L * num_cus;
-  long chunk = (total * h_kv + target - 1) / target;
+  long chunk = (total * units_per_split + target - 1) / target;
   chunk = ((chunk + 63) / 64) * 64;
   if (chunk < 128) chunk = 128;
   while (chunk > 64 && units(chunk) < num_cus) chunk -= 64;

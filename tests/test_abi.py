@@ -108,7 +108,7 @@ def split_call(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(h=34, h_kv=2), 2),               # 17 query heads per KV head
+    (dict(h=514, h_kv=2), 2),              # 257 query heads per KV head
     (dict(chunk=40), 1),                   # not a multiple of 16
     (dict(chunk=0), 1),
     (dict(splits=0), 1),

@@ -601,3 +601,23 @@ def test_decode_batch_invariant_with_fixed_split(paged):
     # and run to run
     o_b2, _, _ = run(dec)
     assert torch.equal(o_b2.view(torch.int16), o_b.view(torch.int16))
+
+
+
+# ------------------------------------------------------------------ large head groups (decode)
+
+@pytest.mark.parametrize("h,h_kv,paged", [(32, 1, False), (48, 2, True), (128, 1, False), (128, 1, True),
+                                          (17, 1, False)])
+def test_decode_large_groups(h, h_kv, paged):
+    # g = 32, 24, 128 (MLA-style), 17: the group is tiled in blocks of 16 heads
+    dec = make_decode(3, h, h_kv, 128, "bf16", seed=h + h_kv, len_range=(1, 700), paged=paged, page_size=16)
+    sl = to_dev(np.asarray(dec["seq_lens"], dtype=np.int32))
+    if paged:
+        o, lse, plan = api.decode(to_dev(dec["q"]), to_dev(dec["k_pool"]), to_dev(dec["v_pool"]), sl,
+                                  block_table=to_dev(dec["block_table"]), page_size=16, scale=dec["scale"])
+    else:
+        o, lse, plan = api.decode(to_dev(dec["q"]), to_dev(dec["k"]), to_dev(dec["v"]), sl, scale=dec["scale"])
+    torch.cuda.synchronize()
+    o_ref, lse_ref = decode_ref(dec["q"], dec["k_seqs"], dec["v_seqs"], dec["seq_lens"], dec["scale"])
+    assert_outputs(o, lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16",
+                   f"decode g={h // h_kv} paged={paged} plan={plan}")
