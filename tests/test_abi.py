@@ -237,3 +237,12 @@ def test_paged_prefill_rejects_before_launch(lib, kw, code):
 def test_paged_prefill_empty_is_ok_without_launch(lib):
     assert paged_prefill_call(lib, B=0, q=None, o=None) == 0
     assert paged_prefill_call(lib, max_q=0, q=None, o=None) == 0
+
+
+def test_fixed_decode_plan_is_batch_independent():
+    from online_softmax_tiled_amd import api
+    assert api.decode_plan_fixed([3000], 256) == (256, 12)
+    assert api.decode_plan_fixed([3000, 20000, 5], 256) == (256, 79)
+    assert api.decode_plan_fixed([], 2048) == (2048, 1)
+    with pytest.raises(ValueError):
+        api.decode_plan_fixed([10], 100)
