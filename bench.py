@@ -53,10 +53,16 @@ KERNEL_SOURCES = ("online_softmax_tiled_amd/csrc/prefill.hip", "online_softmax_t
 
 
 def kernel_source_sha256():
+    """SHA-256 of the prefill kernel's code: the sources with comments and
+    blank space removed, so that only a code change invalidates the record."""
+    import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

@@ -4,8 +4,8 @@
 // recurrence" and "Extending the recurrence to the output").
 //
 // Work decomposition
-//   A workgroup is 8 waves (one per SIMD pair slot: 2 waves per SIMD, one
-//   workgroup per CU). Each wave owns one block of 32 query rows of one query
+//   A workgroup is 8 waves, two per SIMD, one workgroup per CU. Each wave
+//   owns one block of 32 query rows of one query
 //   head; the 8 blocks of a workgroup belong to query heads that share one KV
 //   head (row blocks are numbered query-block-major, head-minor inside a GQA
 //   group), so every K/V tile staged in LDS feeds all 8 waves. Workgroups are
@@ -52,6 +52,15 @@
 // value is 0, so -inf - (-inf) is never formed ("Merge normalized attention
 // without averaging tile outputs", paragraph on fully masked tiles).
 //
+// Paged, variable-length form (PAGED)
+//   The same kernel serves prefill against a paged KV cache: Q and O are
+//   token-major with per-sequence offsets, T_q and T_k are read per sequence
+//   on the device (bottom-right causal alignment), and K/V tiles are staged
+//   through the block table, with each row's page id fetched one iteration
+//   ahead. Keys on a page id outside the pool are masked through the same
+//   per-tile key bits as the key mask. The host may pass a launch order of
+//   the sequences (longest context first).
+//
 // Two running sums per row: l, the fp32 sum of the weights p (for the LSE),
 // and l~, the sum of the weights as rounded to the operand dtype for the PV
 // product. O~ accumulates the rounded weights, so it is divided by l~: the
@@ -84,8 +93,8 @@ constexpr int kKStr = kD + 8;       // 272 B
 constexpr int kVStr = kD + 32;      // 320 B
 constexpr int kKElems = kBc * kKStr;
 constexpr int kVElems = kBc * kVStr;
-constexpr float kTau = 8.f;
-constexpr int kMaxOrder = 512;      // sequences a paged launch can reorder         // allowed lag of the reference max (log2 units)
+constexpr float kTau = 8.f;         // allowed lag of the reference max (log2 units)
+constexpr int kMaxOrder = 512;      // sequences a paged launch can reorder
 
 struct PrefillParams {
   const uint16_t* q;
