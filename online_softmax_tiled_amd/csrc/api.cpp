@@ -166,8 +166,10 @@ int attn_decode_plan(int B, const int32_t* seq_lens_host, int h, int h_kv, int d
   REQUIRE(B == 0 || seq_lens_host, ATTN_ERR_INVALID, "%s: seq_lens_host must not be NULL", fn);
   for (int b = 0; b < B; ++b)
     REQUIRE(seq_lens_host[b] >= 0, ATTN_ERR_INVALID, "%s: seq_lens[%d] = %d is negative", fn, b, seq_lens_host[b]);
-  // Workgroups per split: one per KV head and head block of 16 query heads.
-  attn::decode_plan(B, seq_lens_host, h_kv * ((h / h_kv + 15) / 16), num_cus, chunk_keys, max_splits);
+  // Workgroups per split: one per KV head, or with more than 16 query heads
+  // per KV head one per KV head and group of 4 head blocks of 16.
+  const int n_hb = (h / h_kv + 15) / 16;
+  attn::decode_plan(B, seq_lens_host, h_kv * (n_hb == 1 ? 1 : (n_hb + 3) / 4), num_cus, chunk_keys, max_splits);
   return ok();
 }
 
@@ -181,8 +183,8 @@ int attn_decode_split(const void* q, const void* k, const void* v, const int32_t
   if (int e = check_scale(fn, scale)) return e;
   REQUIRE(h / h_kv <= kMaxGroup, ATTN_ERR_UNSUPPORTED, "%s: %d query heads per KV head (at most %d supported)",
           fn, h / h_kv, kMaxGroup);
-  REQUIRE((((long)max_splits * h_kv * B + 7) / 8) * 8 * ((h / h_kv + 15) / 16) < (1L << 31), ATTN_ERR_UNSUPPORTED,
-          "%s: grid too large", fn);
+  REQUIRE((((long)max_splits * h_kv * B + 7) / 8) * 8 * (((h / h_kv + 15) / 16 + 3) / 4) < (1L << 31),
+          ATTN_ERR_UNSUPPORTED, "%s: grid too large", fn);
   REQUIRE(B >= 0, ATTN_ERR_INVALID, "%s: negative batch %d", fn, B);
   REQUIRE(chunk_keys > 0 && chunk_keys % 16 == 0, ATTN_ERR_INVALID,
           "%s: chunk_keys must be a positive multiple of 16 (got %d)", fn, chunk_keys);

@@ -11,16 +11,19 @@
 // b is slot p % P of page table[b][p / P] (the paged addressing after
 // section "What the merge costs").
 //
-// Workgroup = one (sequence b, KV head, split); 4 waves take 32-key tiles of
-// the split round-robin, each with its own state, and merge the four states
-// through LDS at the end.
+// Workgroup = one (sequence b, KV head, split); with up to 16 query heads
+// per KV head (key mode) its 4 waves take 32-key tiles of the split
+// round-robin, each with its own state, and merge the four states through
+// LDS at the end.
 //
-// Groups of more than 16 query heads (g up to 128 for MLA-style models) are
-// tiled into ceil(g / 16) head blocks, one workgroup each, as the pages'
-// grouped-head decode does ("Decode attention: FlashDecoding, split-K, paged
-// kernels", section "SGLang: a split count computed per sequence, on
-// device": 16 heads per block, the group tiled across blocks); the blocks of
-// one split read the same keys, which the shared last-level cache serves.
+// Groups of more than 16 query heads (g up to 256; 128 for MLA-style models)
+// are tiled into ceil(g / 16) head blocks, as the pages' grouped-head decode
+// does ("Decode attention: FlashDecoding, split-K, paged kernels", section
+// "SGLang: a split count computed per sequence, on device": 16 heads per
+// block, the group tiled across blocks). Then each wave of a workgroup takes
+// one head block and walks every tile of the split (head mode), so the four
+// waves read the same keys at the same time and each ends with a complete
+// state; a group of more than 4 head blocks spreads over several workgroups.
 //
 // Per 32-key tile and wave (v_mfma_f32_16x16x32, the up to 16 query heads of
 // the head block as the 16 columns, unused columns zero):
@@ -93,16 +96,26 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
   // so that the split index does not follow the XCD: otherwise, with a
   // multiple of 8 splits, one XCD would get every sequence's split 0 and
   // another only the longest sequences' last splits.
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  // Head mode (more than one head block of 16): the 4 waves of a workgroup
+  // take 4 head blocks of the group and each walks every tile of the split,
+  // so the four read the same keys together (one fetch, three L1 hits) and
+  // each ends with the complete state of its 16 heads. Otherwise (key mode)
+  // the 4 waves share one head block and take the tiles round-robin.
+  const bool head_mode = p.n_hb > 1;
   unsigned gx = blockIdx.x, gy = blockIdx.y, gz = blockIdx.z;
   int hb = 0;
-  if (p.n_hb > 1) {
-    // 1-D grid: the n_hb head blocks of one (split, KV head, sequence) unit
+  if (head_mode) {
+    // 1-D grid: the n_hg head groups of one (split, KV head, sequence) unit
     // sit 8 apart in launch order, so they land on the same XCD close in
     // time and re-read the unit's keys from that XCD's L2.
+    const unsigned n_hg = (unsigned)(p.n_hb + kWaves - 1) / kWaves;
     const unsigned L = blockIdx.x;
-    hb = (int)((L >> 3) % (unsigned)p.n_hb);
-    const unsigned u = (L & 7u) + 8u * (L / (8u * (unsigned)p.n_hb));
-    if (u >= (unsigned)(p.max_splits * p.h_kv * p.B)) return;
+    hb = (int)((L >> 3) % n_hg) * kWaves + __builtin_amdgcn_readfirstlane(wave);
+    const unsigned u = (L & 7u) + 8u * (L / (8u * n_hg));
+    if (u >= (unsigned)(p.max_splits * p.h_kv * p.B) || hb >= p.n_hb) return;   // no barrier in head mode
     gx = u % (unsigned)p.max_splits;
     gy = (u / (unsigned)p.max_splits) % (unsigned)p.h_kv;
     gz = u / ((unsigned)p.max_splits * (unsigned)p.h_kv);
@@ -121,9 +134,6 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
   const int k_lo = split * p.chunk;
   const int k_hi = split == p.max_splits - 1 ? s_len : min(s_len, k_lo + p.chunk);
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
   const int col = lane & 15;   // query head inside the group
   const int row = lane >> 4;   // 16-lane row 0..3
 
@@ -147,7 +157,9 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
 
   const int n_tiles = (k_hi - k_lo + kTile - 1) / kTile;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  for (int t = wave_u; t < n_tiles; t += kWaves) {
+  const int t0 = head_mode ? 0 : wave_u;
+  const int dt = head_mode ? 1 : kWaves;
+  for (int t = t0; t < n_tiles; t += dt) {
     const int kt = k_lo + t * kTile;
     // Each 16-key block lies inside one page (pages hold a multiple of 16
     // keys and blocks start at multiples of 16): resolve its row once.
@@ -252,6 +264,22 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
+  if (head_mode) {
+    // This wave's state is complete: write its 16 heads' partials.
+    // acc[db] lane (col, row) reg r: head col, d = 16db + 4row + r
+    if (col < hn) {
+      const size_t hs = (size_t)b * p.h + kvh * p.g + hb0 + col;
+      float* po = p.part_o + (hs * p.max_splits + split) * kD;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(&po[db * 16 + row * 4]) = acc[db];
+      if (row == 0) {
+        p.part_m[hs * p.max_splits + split] = m_run == -INFINITY ? -INFINITY : m_run * kLn2;
+        p.part_l[hs * p.max_splits + split] = l_run;
+      }
+    }
+    return;
+  }
+
   // Merge the 4 wave states through LDS (reusing the V^T regions).
   __syncthreads();
   float* red = reinterpret_cast<float*>(lds);            // [wave][16 heads][128 d]
@@ -297,8 +325,9 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
 template <int DT>
 hipError_t dispatch_decode(const DecodeParams& p, bool paged, hipStream_t stream) {
   const long units = (long)p.max_splits * p.h_kv * p.B;
+  const long n_hg = (p.n_hb + kWaves - 1) / kWaves;
   const dim3 grid = p.n_hb == 1 ? dim3((unsigned)p.max_splits, (unsigned)p.h_kv, (unsigned)p.B)
-                                : dim3((unsigned)(((units + 7) / 8) * 8 * p.n_hb));
+                                : dim3((unsigned)(((units + 7) / 8) * 8 * n_hg));
   const bool stream_kv = p.n_hb == 1;
   if (paged) {
     if (stream_kv) hipLaunchKernelGGL((decode_split_kernel<DT, true, true>), grid, dim3(256), 0, stream, p);
