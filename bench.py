@@ -230,10 +230,10 @@ def bench_merge_lse(steps, warmup, dev, copies=3):
 
 
 def bench_decode_large_group(steps, warmup, dev):
-    """Decode with a 128-head group on one KV head (g = 128, tiled in blocks
-    of 16 heads): 32 sequences of 32768 contiguous keys, 537 MB of K+V (more
-    than the 256 MB last-level cache), synthetic N(0,1) drawn on the device.
-    GB/s = K+V bytes / (split + merge time)."""
+    """Decode with a 128-head group on one KV head (g = 128, the heads as
+    the rows of the prefill kernel): 32 sequences of 32768 contiguous keys,
+    537 MB of K+V (more than the 256 MB last-level cache), synthetic N(0,1)
+    drawn on the device. GB/s = K+V bytes / (split + merge time)."""
     import torch
     from online_softmax_tiled_amd import api
     B, h, h_kv, s, d = 32, 128, 1, 32768, 128

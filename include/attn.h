@@ -166,7 +166,9 @@ int attn_decode_plan(int B, const int32_t* seq_lens_host, int h, int h_kv, int d
  *                outside [0, num_pages) is excluded, never dereferenced.
  *   seq_lens     [B] int32 device, KV length of each sequence. Must not
  *                exceed s_max (contiguous) or max_pages * page_size (paged);
- *                keys past that bound are never read.
+ *                keys past that bound are never read. s_max and
+ *                max_pages * page_size are at most 2^23 (else
+ *                ATTN_ERR_UNSUPPORTED).
  *   chunk_keys   positive multiple of 16 (attn_decode_plan returns a
  *                multiple of 64).
  *   max_splits   split dimension of the partial buffers.
@@ -179,8 +181,11 @@ int attn_decode_plan(int B, const int32_t* seq_lens_host, int h, int h_kv, int d
  * i < n_b = min(max_splits, ceil(seq_lens[b]/chunk_keys)) are written; the
  * others are left untouched and never read by attn_merge_states.
  * (m_i, l_i, O~_i) is a state in the sense of [OR] section "The recurrence":
- * m_i is its reference point (this library stores the largest logit of the
- * split), and any reference gives the same merged result.
+ * m_i is its reference point, and any reference gives the same merged
+ * result. With up to 16 query heads per KV head this library stores the
+ * largest logit of the split; with more (the heads then form the MFMA rows
+ * of the prefill kernel, 32 per wave, contiguous K/V or power-of-two pages)
+ * it stores a reference at most 8 ln 2 below that logit.
  */
 int attn_decode_split(const void* q, const void* k, const void* v,
                       const int32_t* block_table, int max_pages, int page_size, int num_pages,

@@ -24,6 +24,9 @@
 // one head block and walks every tile of the split (head mode), so the four
 // waves read the same keys at the same time and each ends with a complete
 // state; a group of more than 4 head blocks spreads over several workgroups.
+// The library sends groups of more than 32 heads to the prefill kernel
+// instead (the heads as its MFMA rows), except on a paged cache whose page
+// size is not a power of two.
 //
 // Per 32-key tile and wave (v_mfma_f32_16x16x32, the up to 16 query heads of
 // the head block as the 16 columns, unused columns zero):
@@ -376,14 +379,15 @@ hipError_t decode_split(const void* q, const void* k, const void* v, const int32
 // first fills the machine is ceil(num_cus / (B * h_kv)) ("Decode attention:
 // FlashDecoding, split-K, paged kernels", section "The grid"). Here the key
 // slice length is chosen instead, so ragged batches are balanced too: aim at
-// about 12 workgroups per CU of total work (several per CU keep enough loads
-// in flight and even out ragged lengths; fewer, longer slices spend less on
-// each workgroup's start and final merge -- on the 64-sequence Llama-3-8B
-// shape 1280-key slices read 5.5 TB/s where 960-key slices read 5.2), never
-// below 128 keys per slice unless that is needed to reach one workgroup per
-// CU, never below 64.
-// units_per_split: workgroups one split launches (KV heads x head blocks).
-int decode_plan(int B, const int32_t* seq_lens, int units_per_split, int num_cus, int32_t* chunk_keys,
+// wgs_per_cu workgroups per CU of total work. For this file's kernel, 12
+// (several per CU keep enough loads in flight and even out ragged lengths;
+// fewer, longer slices spend less on each workgroup's start and final merge
+// -- on the 64-sequence Llama-3-8B shape 1280-key slices read 5.5 TB/s where
+// 960-key slices read 5.2); for the prefill kernel's row form, which runs one
+// workgroup per CU, 1. Never below 128 keys per slice unless that is needed
+// to reach one workgroup per CU, never below 64.
+// units_per_split: workgroups one split launches (one per KV head).
+int decode_plan(int B, const int32_t* seq_lens, int units_per_split, int wgs_per_cu, int num_cus, int32_t* chunk_keys,
                 int32_t* max_splits) {
   long total = 0;
   int s_max = 0;
@@ -396,7 +400,7 @@ int decode_plan(int B, const int32_t* seq_lens, int units_per_split, int num_cus
     for (int b = 0; b < B; ++b) u += (seq_lens[b] + chunk - 1) / chunk;
     return u * units_per_split;
   };
-  const long target = 12L * num_cus;
+  const long target = (long)wgs_per_cu * num_cus;
   long chunk = (total * units_per_split + target - 1) / target;
   chunk = ((chunk + 63) / 64) * 64;
   if (chunk < 128) chunk = 128;

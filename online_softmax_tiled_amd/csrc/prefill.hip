@@ -118,13 +118,23 @@ struct PrefillParams {
   const int32_t* seq_k;
   const int32_t* bt;
   int max_pages, num_pages, page_shift;   // page_size = 1 << page_shift
+  // Split-KV decode form (DEC): one query token per sequence, q [B, h, d];
+  // the g query heads of a KV head are the rows, one workgroup per
+  // (sequence, KV head, split of chunk keys), K/V contiguous [B, h_kv, s_max,
+  // d] or paged; the unnormalised state goes to part_o [B, h, max_splits, d],
+  // part_m, part_l [B, h, max_splits] (natural-log units); seq_k holds the
+  // key counts.
+  float* part_o;
+  float* part_m;
+  float* part_l;
+  int chunk, max_splits, s_max;
   // Optional launch order of the sequences (longest context first), given
   // when the host knows the key counts; n_order = 0 means natural order.
   int n_order;
   uint16_t order[kMaxOrder];
 };
 
-template <int DT, bool CAUSAL, bool KMASK, bool PAGED>
+template <int DT, bool CAUSAL, bool KMASK, bool PAGED, bool DEC>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   using E = Elem<DT>;
   // K of tile t lives in slot t % 2 (read in iteration t - 1), V of tile t in
@@ -141,7 +151,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   const int n_bk = p.B * p.h_kv;
   int bk = blockIdx.x % n_bk;
   int grp = p.n_grp - 1 - (int)(blockIdx.x / n_bk);
-  if (PAGED && p.n_order > 0) {
+  int split = 0;
+  if (DEC) {
+    split = (int)(blockIdx.x % (unsigned)p.max_splits);
+    bk = (int)(blockIdx.x / (unsigned)p.max_splits);
+    grp = 0;
+  } else if (PAGED && p.n_order > 0) {
     // Sequences in the given order (a workgroup's run time follows its
     // sequence's key count, so the longest go first); inside a sequence the
     // KV head varies fastest, as above, then the row group, heaviest first.
@@ -156,7 +171,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
 
   // Lengths of this sequence (uniform over the workgroup).
   int T_q = p.T_q, T_k = p.T_k, n_rb = p.n_rb, q_start = 0;
-  if (PAGED) {
+  int k_lo = 0;   // first key of the workgroup's range (DEC)
+  if (DEC) {
+    // Splits past the sequence write nothing; the merge counts the valid
+    // ones from the same key count.
+    const int s_raw = p.seq_k[b];
+    if (s_raw <= 0) return;
+    if (split >= min(p.max_splits, (s_raw + p.chunk - 1) / p.chunk)) return;
+    const int s_len = min(s_raw, PAGED ? p.max_pages << p.page_shift : p.s_max);
+    k_lo = split * p.chunk;
+    const int k_hi = split == p.max_splits - 1 ? s_len : min(s_len, k_lo + p.chunk);
+    T_k = max(0, k_hi - k_lo);   // keys counted from k_lo
+  } else if (PAGED) {
     q_start = p.cu_q[b];
     T_q = min(p.cu_q[b + 1] - q_start, p.T_q);
     T_k = min(p.seq_k[b], p.max_pages << p.page_shift);
@@ -166,8 +192,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
 
   const int rb = grp * kWaves + wave;
   const bool wave_valid = rb < n_rb;
-  const int qblk = rb / p.g;
-  const int head = kvh * p.g + (rb - qblk * p.g);
+  // DEC: the rows are the group's heads (T_q = g), head = the first of them.
+  const int qblk = DEC ? rb : rb / p.g;
+  const int head = DEC ? kvh * p.g : kvh * p.g + (rb - qblk * p.g);
   const int q0 = qblk * kRows;
   const int off = T_k - T_q;   // >= 0 when causal (bottom-right alignment)
   const int qrow = q0 + col;
@@ -182,18 +209,21 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   if (CAUSAL && wave_valid) last = min(last, (row_last_w + off) / kBc);
 
   // Q row qrow of this wave's head: [B, h, T_q, d], or token-major
-  // [total_q, h, d] when PAGED (row stride h * d).
-  const int q_rstride = PAGED ? p.h * kD : kD;
+  // [total_q, h, d] when PAGED (row stride h * d); DEC: head + qrow of
+  // [B, h, d].
+  const int q_rstride = PAGED && !DEC ? p.h * kD : kD;
   u32x4 qf[8];
   {
     const int hq = wave_valid ? head : 0;
-    const uint16_t* qbase = PAGED ? p.q + ((size_t)q_start * p.h + hq) * kD : p.q + (size_t)(b * p.h + hq) * T_q * kD;
+    const uint16_t* qbase = DEC     ? p.q + ((size_t)b * p.h + hq) * kD
+                            : PAGED ? p.q + ((size_t)q_start * p.h + hq) * kD
+                                    : p.q + (size_t)(b * p.h + hq) * T_q * kD;
     const auto rq = make_rsrc(qbase, wave_valid ? (uint32_t)T_q * q_rstride * 2 : 0u);
 #pragma unroll
     for (int c = 0; c < 8; ++c) qf[c] = buffer_load16(rq, (uint32_t)((qrow * q_rstride + c * 16 + half * 8) * 2));
   }
 
-  const size_t kv_base = PAGED ? 0 : (size_t)bk * T_k * kD;
+  const size_t kv_base = PAGED ? 0 : DEC ? ((size_t)bk * p.s_max + k_lo) * kD : (size_t)bk * T_k * kD;
   const auto rk = make_rsrc(p.k + kv_base, PAGED ? 0u : (uint32_t)T_k * kD * 2);
   const auto rv = make_rsrc(p.v + kv_base, PAGED ? 0u : (uint32_t)T_k * kD * 2);
 
@@ -210,11 +240,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   // so no tile load waits on a block-table load.
   auto page_of = [&](int t, int i) -> int {
     const int key = t * kBc + ((tid + kThreads * i) >> 4);
-    return key < T_k ? p.bt[(size_t)b * p.max_pages + (key >> p.page_shift)] : -1;
+    return key < T_k ? p.bt[(size_t)b * p.max_pages + ((k_lo + key) >> p.page_shift)] : -1;
   };
   auto paged_row = [&](int t, int i, int page) -> long {
     if (page < 0 || page >= p.num_pages) return -1;
-    const int key = t * kBc + ((tid + kThreads * i) >> 4);
+    const int key = k_lo + t * kBc + ((tid + kThreads * i) >> 4);
     return (((long)page << p.page_shift) + (key & ((1 << p.page_shift) - 1))) * p.h_kv + kvh;
   };
   int pg_k[2] = {-1, -1}, pg_v[2] = {-1, -1}, pg_n[2] = {-1, -1};
@@ -302,7 +332,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   auto key_raw = [&](int t) -> int {
     const int key = t * kBc + lane;
     if (key >= T_k) return PAGED ? -1 : 0;
-    return PAGED ? p.bt[(size_t)b * p.max_pages + (key >> p.page_shift)] : (int)p.key_mask[(size_t)b * T_k + key];
+    return PAGED ? p.bt[(size_t)b * p.max_pages + ((k_lo + key) >> p.page_shift)]
+                 : (int)p.key_mask[(size_t)b * T_k + key];
   };
   auto key_ballot = [&](int raw) -> uint64_t {
     return __ballot(PAGED ? (raw >= 0 && raw < p.num_pages) : raw != 0);
@@ -509,6 +540,28 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   if (!wave_valid || qrow >= T_q) return;
   const float l_tot = sum_halves(l_run);
   const float lr_tot = sum_halves(lr_run);
+  if (DEC) {
+    // Partial state of the split at the reference m: O~ accumulated the
+    // rounded weights, so it is scaled by l / l~ to pair with l (the merge
+    // divides the combined O~ by the combined l). No visible key: m = -inf,
+    // l = 0, O~ = 0.
+    const bool none = l_tot == 0.f;
+    const float rs = none ? 0.f : l_tot / lr_tot;
+    const size_t hs = ((size_t)b * p.h + head + qrow) * p.max_splits + split;
+    float* po = p.part_o + hs * kD;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<f32x4*>(po + db * 32 + g4 * 8 + half * 4) =
+            f32x4{acc[db][g4 * 4 + 0] * rs, acc[db][g4 * 4 + 1] * rs, acc[db][g4 * 4 + 2] * rs,
+                  acc[db][g4 * 4 + 3] * rs};
+    if (half == 0) {
+      p.part_m[hs] = none ? -INFINITY : m_ref * kLn2;
+      p.part_l[hs] = l_tot;
+    }
+    return;
+  }
   bool empty = l_tot == 0.f;
   if (!PAGED && p.row_mask != nullptr) empty = empty || p.row_mask[(size_t)b * T_q + qrow] == 0;
   const float inv = empty ? 0.f : 1.f / lr_tot;
@@ -532,7 +585,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
 template <int DT, bool CAUSAL, bool KMASK, bool PAGED>
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.n_grp * p.B * p.h_kv));
-  hipLaunchKernelGGL((prefill_kernel<DT, CAUSAL, KMASK, PAGED>), grid, dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((prefill_kernel<DT, CAUSAL, KMASK, PAGED, false>), grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+// Split-KV decode on the prefill kernel (paged launches take the key-bit
+// path for page ids outside the pool).
+template <int DT, bool PAGED>
+hipError_t launch_decode_rows(const PrefillParams& p, hipStream_t stream) {
+  const dim3 grid((unsigned)((long)p.B * p.h_kv * p.max_splits));
+  hipLaunchKernelGGL((prefill_kernel<DT, false, PAGED, PAGED, true>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -608,6 +670,34 @@ hipError_t prefill_paged(const void* q, const int32_t* cu_seqlens_q, int max_q, 
   if (B == 0 || max_q == 0 || h == 0) return hipSuccess;
   if (dtype == ATTN_DTYPE_BF16) return dispatch_prefill_paged<ATTN_DTYPE_BF16>(p, causal != 0, stream);
   return dispatch_prefill_paged<ATTN_DTYPE_F16>(p, causal != 0, stream);
+}
+
+// Split-KV decode with the query heads of a group as the MFMA rows: the
+// stage-1 producer for groups of more than 16 heads (up to 256, one wave per
+// 32 heads). page_shift < 0 means contiguous K/V [B, h_kv, s_max, d].
+hipError_t decode_split_rows(const void* q, const void* k, const void* v, const int32_t* block_table,
+                             int max_pages, int page_shift, int num_pages, const int32_t* seq_lens, int s_max,
+                             int B, int h, int h_kv, int chunk_keys, int max_splits, int dtype, float scale,
+                             float* part_o, float* part_m, float* part_l, hipStream_t stream) {
+  PrefillParams p = common_params(q, k, v, nullptr, nullptr, B, h, h_kv, h / h_kv, 0, scale);
+  p.n_rb = (p.g + kRows - 1) / kRows;
+  p.n_grp = 1;
+  p.seq_k = seq_lens;
+  p.bt = block_table;
+  p.max_pages = max_pages;
+  p.num_pages = num_pages;
+  p.page_shift = page_shift;
+  p.part_o = part_o;
+  p.part_m = part_m;
+  p.part_l = part_l;
+  p.chunk = chunk_keys;
+  p.max_splits = max_splits;
+  p.s_max = s_max;
+  if (B == 0 || h == 0) return hipSuccess;
+  const bool paged = block_table != nullptr;
+  if (dtype == ATTN_DTYPE_BF16)
+    return paged ? launch_decode_rows<ATTN_DTYPE_BF16, true>(p, stream) : launch_decode_rows<ATTN_DTYPE_BF16, false>(p, stream);
+  return paged ? launch_decode_rows<ATTN_DTYPE_F16, true>(p, stream) : launch_decode_rows<ATTN_DTYPE_F16, false>(p, stream);
 }
 
 }  // namespace attn

@@ -606,6 +606,72 @@ def test_decode_batch_invariant_with_fixed_split(paged):
 
 # ------------------------------------------------------------------ large head groups (decode)
 
+@pytest.mark.parametrize("dtype,paged,page_size,plans", [
+    ("bf16", False, 16, [None, (80, 19), (1504, 1), (64, 2)]),   # split ends inside 64-key tiles; last takes the rest
+    ("f16", False, 16, [None, (992, 2)]),
+    ("bf16", True, 32, [None, (208, 8)]),
+    ("f16", True, 16, [(64, 24), (400, 2)]),
+    ("bf16", True, 48, [None, (96, 16)]),    # page size not a power of two: the 16-head block kernel
+])
+def test_decode_head_rows(dtype, paged, page_size, plans):
+    # g = 40 on two KV heads: the heads of a group are the rows of two waves,
+    # the second one part-filled; empty, one-key and tile-edge sequences
+    lens = [0, 1, 63, 64, 65, 700, 1500]
+    dec = make_decode(B=len(lens), h=80, h_kv=2, d=128, dtype=dtype, seed=31 + page_size, seq_lens=lens,
+                      paged=paged, page_size=page_size, spare_pages=3)
+    o_ref, lse_ref = decode_ref(dec["q"], dec["k_seqs"], dec["v_seqs"], dec["seq_lens"], dec["scale"])
+    for plan in plans:
+        o, lse, used = run_decode(dec, plan)
+        assert_outputs(o, lse, o_ref, lse_ref, dtype, f"decode g=40 paged={paged} P={page_size} plan={used}")
+
+
+def test_decode_head_rows_page_outside_pool():
+    # a block-table entry outside the pool: its 16 keys are excluded, so the
+    # exact result is attention over the remaining keys
+    lens = [300, 90]
+    dec = make_decode(B=2, h=128, h_kv=1, d=128, dtype="bf16", seed=41, seq_lens=lens, paged=True, page_size=16)
+    bt = dec["block_table"].copy()
+    bt[0, 2] = dec["k_pool"].shape[0] + 5      # keys 32..47 of sequence 0
+    bt[1, 5] = -7                              # keys 80..89 of sequence 1
+    keep0 = np.r_[0:32, 48:300]
+    keep1 = np.arange(80)
+    k_seqs = [dec["k_seqs"][0][:, keep0], dec["k_seqs"][1][:, keep1]]
+    v_seqs = [dec["v_seqs"][0][:, keep0], dec["v_seqs"][1][:, keep1]]
+    o_ref, lse_ref = decode_ref(dec["q"], k_seqs, v_seqs, np.array([keep0.size, keep1.size]), dec["scale"])
+    sl = to_dev(dec["seq_lens"])
+    for plan in (None, (64, 5)):
+        o, lse, used = api.decode(to_dev(dec["q"]), to_dev(dec["k_pool"]), to_dev(dec["v_pool"]), sl,
+                                  seq_lens_host=dec["seq_lens"], block_table=to_dev(bt), page_size=16,
+                                  scale=dec["scale"], plan=plan)
+        torch.cuda.synchronize()
+        assert_outputs(o, lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16",
+                       f"decode g=128 pages outside the pool plan={used}")
+
+
+def test_decode_head_rows_partials_match_slices():
+    # the row kernel's stage-1 states, finalised one by one, against the
+    # oracle on each key slice (m in natural-log units, l the sum of weights)
+    dec = make_decode(B=2, h=40, h_kv=1, d=128, dtype="bf16", seed=13, seq_lens=[700, 129], paged=False)
+    chunk, S = 144, 5
+    po, pm, pl = api.decode_split(to_dev(dec["q"]), to_dev(dec["k"]), to_dev(dec["v"]), to_dev(dec["seq_lens"]),
+                                  chunk, S, scale=dec["scale"])
+    torch.cuda.synchronize()
+    po, pm, pl = po.cpu().numpy(), pm.cpu().numpy(), pl.cpu().numpy()
+    for b in range(2):
+        s = int(dec["seq_lens"][b])
+        qb = dec["q"][b].double().numpy()
+        kb = dec["k_seqs"][b].double().numpy()
+        vb = dec["v_seqs"][b].double().numpy()
+        m, l, a = split_states_ref(qb, kb, vb, s, dec["scale"], chunk)
+        n = min(S, math.ceil(s / chunk))
+        for i in range(40):
+            for sp in range(n):
+                o_g, lse_g = finalize_ref((float(pm[b, i, sp]), float(pl[b, i, sp]), po[b, i, sp].astype(np.float64)))
+                o_r, lse_r = finalize_ref((m[i, sp], l[i, sp], a[i, sp]))
+                assert np.max(np.abs(o_g - o_r)) < 1e-2
+                assert abs(lse_g - lse_r) / max(1.0, abs(lse_r)) < LSE_TOL
+
+
 @pytest.mark.parametrize("h,h_kv,paged", [(32, 1, False), (48, 2, True), (128, 1, False), (128, 1, True),
                                           (17, 1, False)])
 def test_decode_large_groups(h, h_kv, paged):
