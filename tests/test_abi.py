@@ -116,6 +116,9 @@ def split_call(lib, **kw):
     (dict(bt=1, page_size=16, max_pages=0, num_pages=4), 1),
     (dict(pm=None), 1),
     (dict(d=96), 2),
+    (dict(s_max=(1 << 23) + 1), 2),        # more keys per sequence than supported
+    (dict(bt=1, page_size=1 << 16, max_pages=1 << 16, num_pages=4), 2),   # 2^32 addressable keys
+    (dict(bt=1, page_size=16, max_pages=(1 << 19) + 1, num_pages=4), 2),
 ])
 def test_decode_split_rejects_before_launch(lib, kw, code):
     assert split_call(lib, **kw) == code
