@@ -179,7 +179,9 @@ int attn_decode_plan(int B, const int32_t* seq_lens_host, int h, int h_kv, int d
  * Split i of sequence b covers keys [i*chunk_keys, (i+1)*chunk_keys), the
  * last split (i = max_splits-1) also takes any keys beyond. Exactly the splits
  * i < n_b = min(max_splits, ceil(seq_lens[b]/chunk_keys)) are written; the
- * others are left untouched and never read by attn_merge_states.
+ * others are left untouched, and attn_merge_states never uses their contents
+ * (it may load them, inside the [B, h, max_splits] buffers, before it knows
+ * n_b).
  * (m_i, l_i, O~_i) is a state in the sense of [OR] section "The recurrence":
  * m_i is its reference point, and any reference gives the same merged
  * result. With up to 16 query heads per KV head this library stores the

@@ -17,8 +17,8 @@
 // head dimension is cut into ND = 4 slices so that more workgroups share the
 // partial traffic. Inside a workgroup, thread (s, f) of 32 split lanes x FL
 // float4 lanes sums splits s, s + 32, ... for 4 consecutive d values, with
-// the loads of U splits in flight at a time; the 32 lane sums are then added
-// through LDS in lane order.
+// the loads of U splits in flight at a time (the first U before the maximum
+// is known); the 32 lane sums are then added through LDS in lane order.
 #include "common.h"
 
 namespace attn {
@@ -74,10 +74,28 @@ __global__ __launch_bounds__(kD / ND / 4 * kSL) void merge_kernel(MergeParams p)
   const int n = s_len <= 0 ? 0 : min(p.max_splits, (s_len + p.chunk - 1) / p.chunk);
   const size_t base = (size_t)bh * p.max_splits;
 
+  // Every load that does not need the split count or the maximum is issued
+  // before them: rows up to max_splits lie inside the partial buffers, and
+  // the rows past the valid count are masked once it is known (their
+  // contents are never used). The first round of partials is in registers
+  // when the maximum arrives, so the merge waits for one round trip, not
+  // three.
+  const int sl = tid / FL;
+  const int d = (tid % FL) * 4;
+  float li0[U], mi0[U];
+  f32x4 oi0[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int i = sl + u * kSL;
+    const bool in = i < p.max_splits;
+    li0[u] = in ? p.part_l[base + i] : 0.f;
+    mi0[u] = in ? p.part_m[base + i] : -INFINITY;
+    oi0[u] = in ? *reinterpret_cast<const f32x4*>(&p.part_o[(base + i) * kD + d0 + d]) : f32x4{};
+  }
   float mloc = -INFINITY;
-  for (int i = tid; i < n; i += NT) {
+  for (int i = tid; i < p.max_splits; i += NT) {
     const float mi = p.part_m[base + i];
-    if (p.part_l[base + i] > 0.f) mloc = fmaxf(mloc, mi);
+    if (i < n && p.part_l[base + i] > 0.f) mloc = fmaxf(mloc, mi);
   }
   mloc = wave_max(mloc);
   if ((tid & 63) == 0) red_m[tid >> 6] = mloc;
@@ -93,11 +111,17 @@ __global__ __launch_bounds__(kD / ND / 4 * kSL) void merge_kernel(MergeParams p)
     return;
   }
 
-  const int sl = tid / FL;
-  const int d = (tid % FL) * 4;
   f32x4 acc = f32x4{};
   float lacc = 0.f;
-  for (int i0 = sl; i0 < n; i0 += U * kSL) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (sl + u * kSL < n && li0[u] > 0.f) {
+      const float w = fast_exp2((mi0[u] - big) * kLog2e);
+      lacc += w * li0[u];
+      acc += w * oi0[u];
+    }
+  }
+  for (int i0 = sl + U * kSL; i0 < n; i0 += U * kSL) {
     float li[U], mi[U];
     f32x4 oi[U];
 #pragma unroll
@@ -142,7 +166,7 @@ hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
   // Many splits and few (sequence, head) pairs: cut d into 4 slices so that
   // more workgroups share the partial traffic (same bits as one slice).
   if (p.max_splits >= 64 && (long)p.B * p.h < 1024) {
-    hipLaunchKernelGGL((merge_kernel<DT, 4, 4>), dim3((unsigned)(p.B * p.h), 4), dim3(kD / 4 / 4 * kSL), 0, stream, p);
+    hipLaunchKernelGGL((merge_kernel<DT, 4, 8>), dim3((unsigned)(p.B * p.h), 4), dim3(kD / 4 / 4 * kSL), 0, stream, p);
   } else {
     hipLaunchKernelGGL((merge_kernel<DT, 1, 4>), dim3((unsigned)(p.B * p.h), 1), dim3(kD / 4 * kSL), 0, stream, p);
   }
