@@ -95,6 +95,7 @@ constexpr int kKElems = kBc * kKStr;
 constexpr int kVElems = kBc * kVStr;
 constexpr float kTau = 8.f;         // allowed lag of the reference max (log2 units)
 constexpr int kMaxOrder = 512;      // sequences a paged launch can reorder
+constexpr int kPfAhead = 3;         // DEC: tiles between a prefetch and its iteration
 
 struct PrefillParams {
   const uint16_t* q;
@@ -378,7 +379,44 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   // V slot 2 is read (with P = 0) in the first iteration.
   for (int i = tid; i < kVElems / 8; i += kThreads) store16(&lds_v[2][i * 8], u32x4{});
   __syncthreads();
+  if (DEC && !PAGED && n_rb <= 4 && wave >= 4) {
+    // Contiguous decode with at most 128 heads: waves 4-7 have no rows. They
+    // do their share of the staging and, each iteration, one load per
+    // 128-byte line of K (waves 4, 5) or V (waves 6, 7) of the tile kPfAhead
+    // ahead. That tile is then on its way through the L2 when the staging
+    // loads reach it, so each CU keeps about twice the bytes in flight of
+    // the staging alone (a streaming workgroup holds only one tile of loads
+    // in registers). The loaded values are discarded. Loads retire in order,
+    // so each one is consumed one iteration after its issue, where the wait
+    // for that iteration's staging loads has already covered it; the loop is
+    // unrolled by two so that the two values have fixed registers.
+    const auto rs = wave < 6 ? rk : rv;
+    const uint32_t loff = (uint32_t)(((tid - 4 * 64) & 127) * 128);
+    __syncthreads();   // the other waves' reads of K(0), below
+    uint32_t pf[2] = {0u, 0u};
+    auto step = [&](int j, int u) {
+      load_k(j + 2);
+      load_v(j + 1);
+      pf[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)((uint32_t)(j + kPfAhead) * (kBc * kD * 2) + loff), 0, 0);
+      store_k(j & 1);
+      store_v((j + 1) % 3);
+      asm volatile("" ::"v"(pf[u ^ 1]));
+      __syncthreads();
+    };
+    // One barrier per iteration j = 0 .. n_tiles, as in the main loop.
+    int j = 0;
+    for (; j + 1 <= n_tiles; j += 2) {
+      step(j, 0);
+      step(j + 1, 1);
+    }
+    if (j <= n_tiles) step(j, 0);
+    asm volatile("" ::"v"(pf[0]), "v"(pf[1]));
+    return;
+  }
   qk(lds_k[0], sc);
+  // Iteration 0 overwrites K(0)'s slot with K(2) before its barrier: every
+  // wave's reads of K(0) must be done first.
+  __syncthreads();
 
   float alpha = 1.f;   // rescale of O~ decided by the previous softmax
   for (int j = 0; j <= n_tiles; ++j) {
