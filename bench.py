@@ -391,6 +391,8 @@ def run_only(args, dev):
         print(json.dumps(r))
     elif args.only == "merge_lse":
         print(json.dumps(bench_merge_lse(args.steps, args.warmup, dev)))
+    elif args.only == "decode_g128":
+        print(json.dumps(bench_decode_large_group(args.steps, args.warmup, dev)))
     elif args.only == "decode_paged":
         from online_softmax_tiled_amd.workloads import make_config
         r = bench_decode_paged(args.steps, args.warmup, dev, make_config("paged_decode_llama3_8b_b64"))
@@ -410,7 +412,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="only the headline prefill")
-    ap.add_argument("--only", choices=["prefill", "decode_70b", "decode_paged", "merge_lse", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode_70b", "decode_paged", "decode_g128", "merge_lse", "copy"],
+                    default=None,
                     help="run one workload only (for profiler counter runs) and print its timing")
     ap.add_argument("--copy-mb", type=int, default=1024,
                     help="bytes moved by the plain device copy of --only copy (counter calibration)")

@@ -17,8 +17,9 @@
 // head dimension is cut into ND = 4 slices so that more workgroups share the
 // partial traffic. Inside a workgroup, thread (s, f) of 32 split lanes x FL
 // float4 lanes sums splits s, s + 32, ... for 4 consecutive d values, with
-// the loads of U splits in flight at a time (the first U before the maximum
-// is known); the 32 lane sums are then added through LDS in lane order.
+// the loads of U splits in flight at a time (with several slices, the first
+// U before the maximum is known); the 32 lane sums are then added through
+// LDS in lane order.
 #include "common.h"
 
 namespace attn {
@@ -74,26 +75,29 @@ __global__ __launch_bounds__(kD / ND / 4 * kSL) void merge_kernel(MergeParams p)
   const int n = s_len <= 0 ? 0 : min(p.max_splits, (s_len + p.chunk - 1) / p.chunk);
   const size_t base = (size_t)bh * p.max_splits;
 
-  // Every load that does not need the split count or the maximum is issued
-  // before them: rows up to max_splits lie inside the partial buffers, and
-  // the rows past the valid count are masked once it is known (their
-  // contents are never used). The first round of partials is in registers
-  // when the maximum arrives, so the merge waits for one round trip, not
-  // three.
+  // With several d-slices (many splits, few rows: latency decides) the
+  // first U splits of each lane are loaded before the split count and the
+  // maximum are known, so they are in registers when the maximum arrives:
+  // rows up to max_splits lie inside the partial buffers, and those past the
+  // valid count are masked once it is known (their contents are never used).
+  // The merge then waits for one round trip instead of three. With one slice
+  // (many rows: bytes decide) only valid rows are read, after the maximum.
+  constexpr int U0 = ND > 1 ? U : 0;
+  const int lim = ND > 1 ? p.max_splits : n;
   const int sl = tid / FL;
   const int d = (tid % FL) * 4;
-  float li0[U], mi0[U];
-  f32x4 oi0[U];
+  float li0[U0 > 0 ? U0 : 1], mi0[U0 > 0 ? U0 : 1];
+  f32x4 oi0[U0 > 0 ? U0 : 1];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
+  for (int u = 0; u < U0; ++u) {
     const int i = sl + u * kSL;
-    const bool in = i < p.max_splits;
+    const bool in = i < lim;
     li0[u] = in ? p.part_l[base + i] : 0.f;
     mi0[u] = in ? p.part_m[base + i] : -INFINITY;
     oi0[u] = in ? *reinterpret_cast<const f32x4*>(&p.part_o[(base + i) * kD + d0 + d]) : f32x4{};
   }
   float mloc = -INFINITY;
-  for (int i = tid; i < p.max_splits; i += NT) {
+  for (int i = tid; i < lim; i += NT) {
     const float mi = p.part_m[base + i];
     if (i < n && p.part_l[base + i] > 0.f) mloc = fmaxf(mloc, mi);
   }
@@ -114,14 +118,14 @@ __global__ __launch_bounds__(kD / ND / 4 * kSL) void merge_kernel(MergeParams p)
   f32x4 acc = f32x4{};
   float lacc = 0.f;
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
+  for (int u = 0; u < U0; ++u) {
     if (sl + u * kSL < n && li0[u] > 0.f) {
       const float w = fast_exp2((mi0[u] - big) * kLog2e);
       lacc += w * li0[u];
       acc += w * oi0[u];
     }
   }
-  for (int i0 = sl + U * kSL; i0 < n; i0 += U * kSL) {
+  for (int i0 = sl + U0 * kSL; i0 < n; i0 += U * kSL) {
     float li[U], mi[U];
     f32x4 oi[U];
 #pragma unroll
