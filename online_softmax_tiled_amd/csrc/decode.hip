@@ -86,9 +86,10 @@ __device__ __forceinline__ float sum_rows16(float x) {
 // group a covers keys 4a..4a+3 and 16+4a..16+4a+3, stored contiguously.
 __device__ __forceinline__ int vt_pos(int kk) { return ((kk & 12) << 1) | ((kk & 16) >> 2) | (kk & 3); }
 
-// STREAM: K/V loads carry the non-temporal hint (each byte read once). With
-// several head blocks the same keys are read by several workgroups, and the
-// loads must leave them in the caches.
+// STREAM: K/V loads carry the non-temporal hint (each byte read once). In
+// head mode the waves of a workgroup (and, beyond 4 head blocks, several
+// workgroups) read the same keys, and the loads must leave them in the
+// caches.
 template <int DT, bool PAGED, bool STREAM>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
   using E = Elem<DT>;

@@ -694,7 +694,8 @@ def test_decode_head_rows_partials_match_slices():
 @pytest.mark.parametrize("h,h_kv,paged", [(32, 1, False), (48, 2, True), (128, 1, False), (128, 1, True),
                                           (17, 1, False)])
 def test_decode_large_groups(h, h_kv, paged):
-    # g = 32, 24, 128 (MLA-style), 17: the group is tiled in blocks of 16 heads
+    # g = 32, 24, 17: blocks of 16 heads, one per wave (head mode); g = 128
+    # (MLA-style): the heads as the rows of the prefill kernel
     dec = make_decode(3, h, h_kv, 128, "bf16", seed=h + h_kv, len_range=(1, 700), paged=paged, page_size=16)
     sl = to_dev(np.asarray(dec["seq_lens"], dtype=np.int32))
     if paged:
