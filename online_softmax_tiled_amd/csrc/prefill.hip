@@ -96,6 +96,7 @@ constexpr int kVElems = kBc * kVStr;
 constexpr float kTau = 8.f;         // allowed lag of the reference max (log2 units)
 constexpr int kMaxOrder = 512;      // sequences a paged launch can reorder
 constexpr int kPfAhead = 3;         // DEC: tiles between a prefetch and its iteration
+constexpr int kMaxListTiles = 4096; // key-masked prefill: longest list of visible tiles
 
 struct PrefillParams {
   const uint16_t* q;
@@ -142,6 +143,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   // slot t % 3 (read in iteration t + 1).
   __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kKElems];
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[3][kVElems];
+  // Contiguous key-masked prefill: the tiles with a visible key, in order.
+  constexpr bool kCompact = KMASK && !PAGED && !DEC;
+  __shared__ uint16_t tile_list[kCompact ? kMaxListTiles : 1];
+  __shared__ int wave_count[kWaves];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -340,6 +345,50 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     return __ballot(PAGED ? (raw >= 0 && raw < p.num_pages) : raw != 0);
   };
 
+  // Fully masked tiles are skipped: with a key mask, the pipeline below
+  // walks the list of tiles that hold a visible key (position j -> tile
+  // tile_at(j)); a skipped tile would only have added exact zeros. Each wave
+  // scans a contiguous share of the tiles (the mask bytes of 8 tiles in
+  // flight at a time), then the shares are concatenated in order.
+  int n_vis = n_tiles;
+  const bool use_list = kCompact && n_tiles <= kMaxListTiles;
+  if (use_list) {
+    uint16_t* found = lds_v[1];   // per-wave scratch; V slot 1 is first written below
+    const int per = (n_tiles + kWaves - 1) / kWaves;
+    const int t0 = wave * per;
+    const int t1 = min(n_tiles, t0 + per);
+    int cnt = 0;
+    for (int tb = t0; tb < t1; tb += 8) {
+      int raw[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) raw[u] = tb + u < t1 ? key_raw(tb + u) : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (key_ballot(raw[u]) != 0) {
+          if (lane == 0) found[t0 + cnt] = (uint16_t)(tb + u);
+          ++cnt;
+        }
+      }
+    }
+    if (lane == 0) wave_count[wave] = cnt;
+    __syncthreads();
+    int before = 0;
+    n_vis = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      const int c = wave_count[w];
+      before += w < wave ? c : 0;
+      n_vis += c;
+    }
+    for (int i = lane; i < cnt; i += 64) tile_list[before + i] = found[t0 + i];
+    __syncthreads();
+  }
+  // Positions past the list map past the last tile: zeros, fully masked.
+  const int t_end = (T_k + kBc - 1) / kBc;
+  auto tile_at = [&](int j) -> int {
+    if (!use_list) return j;
+    return j < n_vis ? (int)tile_list[j] : t_end + j;
+  };
+
   f32x16 sc[2];     // scores of tile j
   u32x4 pp[4];      // P^T of tile j - 1
   uint64_t kbits = ~0ull;
@@ -348,26 +397,26 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   sc[0] = f32x16{};
   sc[1] = f32x16{};
 
-  if (n_tiles > 0) {
+  if (n_vis > 0) {
     if (PAGED) {
       pg_k[0] = page_of(0, 0);
       pg_k[1] = page_of(0, 1);
       pg_v[0] = pg_k[0];
       pg_v[1] = pg_k[1];
     }
-    load_k(0);
-    load_v(0);
+    load_k(tile_at(0));
+    load_v(tile_at(0));
     store_k(0);
     store_v(0);
-    if (n_tiles > 1) {
+    if (n_vis > 1) {
       if (PAGED) {
         pg_k[0] = page_of(1, 0);
         pg_k[1] = page_of(1, 1);
       }
-      load_k(1);
+      load_k(tile_at(1));
       store_k(1);
     }
-    if (KMASK) kbits = key_ballot(key_raw(0));
+    if (KMASK) kbits = key_ballot(key_raw(tile_at(0)));
   }
   if (PAGED) {
     // pages of tile 1 for V(1) and of tile 2 for K(2), used in iteration 0
@@ -419,18 +468,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   __syncthreads();
 
   float alpha = 1.f;   // rescale of O~ decided by the previous softmax
-  for (int j = 0; j <= n_tiles; ++j) {
+  for (int j = 0; j <= n_vis; ++j) {
     // Tiles past the end load as zeros; the slots they go to are free, so the
     // loads and stores need no conditions and the iteration stays one block
     // from the rescale below to the barrier.
-    load_k(j + 2);
-    load_v(j + 1);
+    load_k(tile_at(j + 2));
+    load_v(tile_at(j + 1));
     if (PAGED) {
       pg_n[0] = page_of(j + 3, 0);
       pg_n[1] = page_of(j + 3, 1);
     }
     int kraw = 0;
-    if (KMASK) kraw = key_raw(j + 1);
+    if (KMASK) kraw = key_raw(tile_at(j + 1));
     // O~ still holds PV(j-2) at the old reference; PV(j-1) below uses the
     // weights of the current one.
     if (__ballot(alpha != 1.f)) {
@@ -440,7 +489,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
 
     f32x16 sn[2];
     u32x4 pn[4];
-    mask(j, kbits, sc);
+    mask(tile_at(j), kbits, sc);
     {
       // Steady state: the 32 MFMAs of PV(j-1) and QK(j+1) in 8 slices of 4,
       // each slice carrying a share of the softmax VALU work of tile j, with

@@ -129,6 +129,37 @@ def test_prefill_masks_and_empty_rows(dtype):
     assert_outputs(o, lse, o_ref, lse_ref, dtype, "masked prefill")
 
 
+@pytest.mark.parametrize("dtype,causal", [("f16", False), ("bf16", True)])
+def test_prefill_skips_fully_masked_tiles(dtype, causal):
+    # tiles with no visible key are skipped: only the last, partial tile
+    # visible (batch 0); only one middle tile (batch 1); the first tiles
+    # masked, so early causal rows see nothing (batch 2); a run of masked
+    # tiles between visible ones (batch 3); T_k = 300 is not a tile multiple
+    inp = make_prefill(4, 8, 2, 300, 300, 128, dtype, seed=17 + causal, causal=causal)
+    km = np.ones((4, 300), dtype=np.uint8)
+    km[0, :256] = 0
+    km[1, :128] = 0
+    km[1, 192:] = 0
+    km[2, :130] = 0
+    km[3, 64:256] = 0
+    km[3, 10] = 0                      # and one partial tile
+    inp["key_mask"] = km
+    o, lse, o_ref, lse_ref = run_prefill(inp)
+    if causal:
+        assert np.isneginf(lse_ref[2, :, :130]).all()
+    assert_outputs(o, lse, o_ref, lse_ref, dtype, f"prefill with masked tiles causal={causal}")
+
+
+def test_prefill_key_mask_longer_than_tile_list():
+    # 4097 tiles of keys: more than the list of visible tiles holds, so the
+    # kernel walks every tile (masked ones included); checked on sampled rows
+    T_k = 4097 * 64
+    inp = make_prefill(1, 4, 1, 64, T_k, 128, "bf16", seed=19, causal=False, key_tile_p=0.25)
+    rows = np.array([0, 1, 17, 31, 32, 63])
+    o, lse, o_ref, lse_ref = run_prefill(inp, rows=rows)
+    assert_outputs(o, lse, o_ref, lse_ref, "bf16", "prefill key mask over 4097 tiles (sampled rows)")
+
+
 def test_prefill_all_keys_masked():
     inp = make_prefill(1, 4, 1, 40, 40, 128, "bf16", seed=6, causal=False)
     inp["key_mask"] = np.zeros((1, 40), dtype=np.uint8)
