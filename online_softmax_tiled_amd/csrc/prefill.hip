@@ -139,6 +139,7 @@ struct PrefillParams {
 template <int DT, bool CAUSAL, bool KMASK, bool PAGED, bool DEC>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   using E = Elem<DT>;
+  static_assert(!PAGED || KMASK, "paged K/V are addressed through the key-bit path");
   // K of tile t lives in slot t % 2 (read in iteration t - 1), V of tile t in
   // slot t % 3 (read in iteration t + 1).
   __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kKElems];
@@ -239,18 +240,28 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   auto tile_byte = [&](int t, int i) {
     return (uint32_t)(((t * kBc + ((tid + kThreads * i) >> 4)) * kD + (tid & 15) * 8) * 2);
   };
-  // Paged: the page id (block-table entry, -1 past T_k) of staging row i of
-  // tile t, and the pool row it gives; keys past T_k or on a page id outside
-  // the pool read as zeros. Page ids are fetched one iteration before the
-  // K tile that needs them and reused for the V tile one iteration later,
-  // so no tile load waits on a block-table load.
+  // Per-lane loads that decide masking (block-table entries, key-mask bytes)
+  // are range-checked buffer loads over the sequence's row: past its end
+  // they read zero, so they need no branch, and the range test is applied
+  // where the value is used. A branch around such a load would make the
+  // compiler wait for it (and, loads retiring in order, for every tile load
+  // issued before it) right where the branches join, before the products.
+  const auto r_key = !KMASK ? make_rsrc(nullptr, 0u)
+                     : PAGED ? make_rsrc(p.bt + (size_t)b * p.max_pages, (uint32_t)p.max_pages * 4u)
+                             : make_rsrc(p.key_mask + (size_t)b * T_k, (uint32_t)T_k);
+  // Paged: the block-table entry of staging row i of tile t, and the pool row
+  // it gives; keys past T_k or on a page id outside the pool read as zeros.
+  // Page ids are fetched one iteration before the K tile that needs them and
+  // reused for the V tile one iteration later, so no tile load waits on a
+  // block-table load.
   auto page_of = [&](int t, int i) -> int {
-    const int key = t * kBc + ((tid + kThreads * i) >> 4);
-    return key < T_k ? p.bt[(size_t)b * p.max_pages + ((k_lo + key) >> p.page_shift)] : -1;
+    const uint32_t key = (uint32_t)(k_lo + t * kBc + ((tid + kThreads * i) >> 4));
+    return (int)__builtin_amdgcn_raw_buffer_load_b32(r_key, (int)((key >> p.page_shift) * 4u), 0, 0);
   };
   auto paged_row = [&](int t, int i, int page) -> long {
-    if (page < 0 || page >= p.num_pages) return -1;
-    const int key = k_lo + t * kBc + ((tid + kThreads * i) >> 4);
+    const int key_l = t * kBc + ((tid + kThreads * i) >> 4);
+    if (key_l >= T_k || page < 0 || page >= p.num_pages) return -1;
+    const int key = k_lo + key_l;
     return (((long)page << p.page_shift) + (key & ((1 << p.page_shift) - 1))) * p.h_kv + kvh;
   };
   int pg_k[2] = {-1, -1}, pg_v[2] = {-1, -1}, pg_n[2] = {-1, -1};
@@ -333,16 +344,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   };
   // Visible-key bits of tile t (KMASK): the key mask, or with PAGED the keys
   // whose block-table entry names a page of the pool. The per-lane value is
-  // loaded early (key_raw) and turned into bits late (key_ballot), so the
-  // ballot's wait falls where the tile loads are awaited anyway.
+  // loaded early (key_raw) and turned into bits late (key_ballot, with the
+  // range test), so the ballot's wait falls where the tile loads are awaited
+  // anyway.
   auto key_raw = [&](int t) -> int {
-    const int key = t * kBc + lane;
-    if (key >= T_k) return PAGED ? -1 : 0;
-    return PAGED ? p.bt[(size_t)b * p.max_pages + ((k_lo + key) >> p.page_shift)]
-                 : (int)p.key_mask[(size_t)b * T_k + key];
+    const uint32_t key = (uint32_t)(t * kBc + lane);
+    return PAGED ? (int)__builtin_amdgcn_raw_buffer_load_b32(r_key, (int)(((k_lo + key) >> p.page_shift) * 4u), 0, 0)
+                 : (int)__builtin_amdgcn_raw_buffer_load_b8(r_key, (int)key, 0, 0);
   };
-  auto key_ballot = [&](int raw) -> uint64_t {
-    return __ballot(PAGED ? (raw >= 0 && raw < p.num_pages) : raw != 0);
+  auto key_ballot = [&](int t, int raw) -> uint64_t {
+    const bool in = t * kBc + lane < T_k;
+    return __ballot(in && (PAGED ? (raw >= 0 && raw < p.num_pages) : raw != 0));
   };
 
   // Fully masked tiles are skipped: with a key mask, the pipeline below
@@ -361,10 +373,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     for (int tb = t0; tb < t1; tb += 8) {
       int raw[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) raw[u] = tb + u < t1 ? key_raw(tb + u) : 0;
+      for (int u = 0; u < 8; ++u) raw[u] = key_raw(tb + u);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        if (key_ballot(raw[u]) != 0) {
+        if (tb + u < t1 && key_ballot(tb + u, raw[u]) != 0) {
           if (lane == 0) found[t0 + cnt] = (uint16_t)(tb + u);
           ++cnt;
         }
@@ -416,7 +428,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
       load_k(tile_at(1));
       store_k(1);
     }
-    if (KMASK) kbits = key_ballot(key_raw(tile_at(0)));
+    if (KMASK) kbits = key_ballot(tile_at(0), key_raw(tile_at(0)));
   }
   if (PAGED) {
     // pages of tile 1 for V(1) and of tile 2 for K(2), used in iteration 0
@@ -479,7 +491,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
       pg_n[1] = page_of(j + 3, 1);
     }
     int kraw = 0;
-    if (KMASK) kraw = key_raw(tile_at(j + 1));
+    const int t_kb = tile_at(j + 1);
+    if (KMASK) kraw = key_raw(t_kb);
     // O~ still holds PV(j-2) at the old reference; PV(j-1) below uses the
     // weights of the current one.
     if (__ballot(alpha != 1.f)) {
@@ -610,7 +623,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     for (int i = 0; i < 4; ++i) pp[i] = pn[i];
     sc[0] = sn[0];
     sc[1] = sn[1];
-    if (KMASK) kbits = key_ballot(kraw);
+    if (KMASK) kbits = key_ballot(t_kb, kraw);
     if (PAGED) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
