@@ -237,8 +237,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   // Staging: 1024 16-byte chunks per tile for K and for V; chunk tid + 512 i
   // holds key chunk / 16, d-chunk chunk % 16.
   u32x4 kreg[2], vreg[2];
+  // (unsigned: the tiles just past the end of the longest key range lie at
+  // about 2^31 bytes, which the buffer range check turns into zeros)
   auto tile_byte = [&](int t, int i) {
-    return (uint32_t)(((t * kBc + ((tid + kThreads * i) >> 4)) * kD + (tid & 15) * 8) * 2);
+    return ((uint32_t)(t * kBc + ((tid + kThreads * i) >> 4)) * kD + (uint32_t)(tid & 15) * 8u) * 2u;
   };
   // Per-lane loads that decide masking (block-table entries, key-mask bytes)
   // are range-checked buffer loads over the sequence's row: past its end
@@ -394,11 +396,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     for (int i = lane; i < cnt; i += 64) tile_list[before + i] = found[t0 + i];
     __syncthreads();
   }
-  // Positions past the list map past the last tile: zeros, fully masked.
+  // Positions past the list map to the tile past the last one: zeros, fully
+  // masked.
   const int t_end = (T_k + kBc - 1) / kBc;
   auto tile_at = [&](int j) -> int {
     if (!use_list) return j;
-    return j < n_vis ? (int)tile_list[j] : t_end + j;
+    return j < n_vis ? (int)tile_list[j] : t_end;
   };
 
   f32x16 sc[2];     // scores of tile j
