@@ -251,7 +251,9 @@ int attn_merge_lse(const void* o_a, const float* lse_a, const void* o_b, const f
  *   num_pages   pages in the pool; positions whose page id lies outside
  *               [0, num_pages) are left untouched.
  *   out         [B, h_kv, s_max, d_h] dtype; positions p >= seq_lens[b] are
- *               left untouched. page_size may be any positive value here.
+ *               left untouched. page_size may be any positive value here,
+ *               with max_pages * page_size below 2^31 (else
+ *               ATTN_ERR_UNSUPPORTED).
  */
 int attn_paged_gather(const void* pool, const int32_t* block_table, const int32_t* seq_lens,
                       int B, int h_kv, int d_h, int page_size, int max_pages, int num_pages,

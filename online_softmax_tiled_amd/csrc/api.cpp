@@ -271,6 +271,8 @@ int attn_paged_gather(const void* pool, const int32_t* block_table, const int32_
   REQUIRE(page_size > 0 && max_pages > 0 && num_pages > 0, ATTN_ERR_INVALID,
           "%s: page_size, max_pages and num_pages must be positive", fn);
   REQUIRE(B <= 65535, ATTN_ERR_UNSUPPORTED, "%s: grid too large", fn);
+  REQUIRE((long)max_pages * page_size < (1L << 31), ATTN_ERR_UNSUPPORTED,
+          "%s: max_pages * page_size = %ld keys (at most 2^31 - 1 supported)", fn, (long)max_pages * page_size);
   if (B == 0 || s_max == 0) return ok();
   REQUIRE(pool && block_table && seq_lens && out, ATTN_ERR_INVALID, "%s: a required pointer is NULL", fn);
   return from_hip(attn::paged_gather(pool, block_table, seq_lens, B, h_kv, page_size, max_pages, num_pages, s_max,

@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
                                     : p.q + (size_t)(b * p.h + hq) * T_q * kD;
     const auto rq = make_rsrc(qbase, wave_valid ? (uint32_t)T_q * q_rstride * 2 : 0u);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) qf[c] = buffer_load16(rq, (uint32_t)((qrow * q_rstride + c * 16 + half * 8) * 2));
+    for (int c = 0; c < 8; ++c) qf[c] = buffer_load16(rq, (uint32_t)(qrow * q_rstride + c * 16 + half * 8) * 2u);
   }
 
   const size_t kv_base = PAGED ? 0 : DEC ? ((size_t)bk * p.s_max + k_lo) * kD : (size_t)bk * T_k * kD;

@@ -136,6 +136,8 @@ def test_merge_and_gather_reject_before_launch(lib):
     assert lib.attn_merge_states(p(1), None, p(1), p(1), 64, 1, 8, 4, 128, p(1), None, 1, None) == 1
     assert lib.attn_merge_states(p(1), p(1), p(1), p(1), 64, 1, 8, 4, 64, p(1), None, 1, None) == 2
     assert lib.attn_paged_gather(p(1), p(1), p(1), 1, 8, 128, 0, 4, 4, 64, 1, p(1), None) == 1
+    # more addressable keys than an int holds
+    assert lib.attn_paged_gather(p(1), p(1), p(1), 1, 8, 128, 1 << 16, 1 << 15, 4, 64, 1, p(1), None) == 2
     assert lib.attn_paged_gather(p(1), None, p(1), 1, 8, 128, 16, 4, 4, 64, 1, p(1), None) == 1
     assert lib.attn_paged_gather(p(1), p(1), p(1), 1, 8, 128, 16, 4, 4, 64, 3, p(1), None) == 2
 
