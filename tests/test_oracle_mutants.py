@@ -4,8 +4,11 @@ oracle also passes would prove nothing; these tests show that the ones here
 fail on: an initial maximum of 0, an accumulator that is not rescaled, the
 wrong GQA head mapping, a missing or misplaced scale, top-left causal
 alignment, a log-sum-exp in base 2, a merge without the both-empty branch,
-a merge that drops the rescale, and a gather with the page index and slot
-swapped."""
+a merge that drops the rescale, a gather with the page index and slot
+swapped, split slices that drop a key, the wrong GQA head in decode, a merge
+that ignores the valid split count, an (O, LSE) merge that averages the two
+outputs or reads LSE = +inf as a real mass, and attention that ignores the
+key mask."""
 
 import math
 
@@ -48,7 +51,7 @@ def online_no_rescale(scores, values, block):
     return m, l, o
 
 
-def _attention_variant(gqa=None, scale_mode="before", causal_mode="bottom_right", log=np.log):
+def _attention_variant(gqa=None, scale_mode="before", causal_mode="bottom_right", log=np.log, use_key_mask=True):
     def att(q, k, v, scale, causal=False, key_mask=None, row_mask=None, rows=None):
         q, k, v = oatt._f64(q), oatt._f64(k), oatt._f64(v)
         b_, h, t_q, d = q.shape
@@ -58,7 +61,7 @@ def _attention_variant(gqa=None, scale_mode="before", causal_mode="bottom_right"
         o = np.zeros((b_, h, rows.size, v.shape[-1]))
         lse = np.full((b_, h, rows.size), -np.inf)
         for b in range(b_):
-            km = None if key_mask is None else np.asarray(key_mask)[b]
+            km = None if key_mask is None or not use_key_mask else np.asarray(key_mask)[b]
             rm = None if row_mask is None else np.asarray(row_mask)[b]
             if causal and causal_mode == "top_left":
                 vis = oatt.visible_mask(rows, t_k, t_k, True, km, rm)
@@ -113,6 +116,58 @@ def gather_swapped(pool, block_table, seq_lens, s_max, out=None):
     return out
 
 
+def split_states_short(q, k, v, seq_len, scale, chunk):
+    # mistake: each slice stops one key early
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    h, d = q.shape
+    g = h // k.shape[0]
+    n = -(-seq_len // chunk) if seq_len > 0 else 0
+    m, l, a = np.full((h, n), -np.inf), np.zeros((h, n)), np.zeros((h, n, d))
+    for i in range(h):
+        x = float(scale) * (k[i // g, :seq_len] @ q[i])
+        for s_ in range(n):
+            lo, hi = s_ * chunk, min(seq_len, (s_ + 1) * chunk) - 1
+            m[i, s_], l[i, s_], a[i, s_] = ost.state_ref(x[lo:hi], v[i // g, lo:hi])
+    return m, l, a
+
+
+def decode_wrong_head(q, k_seqs, v_seqs, seq_lens, scale):
+    # mistake: query head i reads KV head i % h_kv instead of i // g
+    q = np.asarray(q, dtype=np.float64)
+    b_, h, d = q.shape
+    o, lse = np.zeros((b_, h, d)), np.full((b_, h), -np.inf)
+    for b in range(b_):
+        s = int(seq_lens[b])
+        kb = np.asarray(k_seqs[b], dtype=np.float64)[:, :s]
+        vb = np.asarray(v_seqs[b], dtype=np.float64)[:, :s]
+        for i in range(h):
+            ob, lb = oatt._rows_attention(q[b, i][None, :], kb[i % kb.shape[0]], vb[i % kb.shape[0]], float(scale),
+                                          np.ones((1, s), dtype=bool))
+            o[b, i], lse[b, i] = ob[0], lb[0]
+    return o, lse
+
+
+def merge_partials_all(m, l, a, n_valid=None, order=None):
+    # mistake: merges every partial row, not only the valid ones
+    return ost.merge_partials_ref(m, l, a, n_valid=None, order=order)
+
+
+def merge_lse_average(o_a, lse_a, o_b, lse_b):
+    # mistake: averages the two normalised outputs
+    o, lse = ost.merge_lse_ref(o_a, lse_a, o_b, lse_b)
+    return 0.5 * (np.asarray(o_a) + np.asarray(o_b)), lse
+
+
+def merge_lse_inf_as_mass(o_a, lse_a, o_b, lse_b):
+    # mistake: an LSE of +inf is taken as a real (infinite) mass
+    o_a, o_b = np.asarray(o_a, dtype=np.float64), np.asarray(o_b, dtype=np.float64)
+    la, lb = np.asarray(lse_a, dtype=np.float64), np.asarray(lse_b, dtype=np.float64)
+    big = np.maximum(la, lb)
+    ea, eb = np.exp(la - big), np.exp(lb - big)
+    tot = ea + eb
+    return o_a * (ea / tot)[..., None] + o_b * (eb / tot)[..., None], big + np.log(tot)
+
+
 CASES = [
     ("online_ref", online_m0, pins.test_online_row_far_below_zero, ()),
     ("online_ref", online_no_rescale, pins.test_online_equals_safe_softmax_with_late_outlier, (load_golden,)),
@@ -124,6 +179,13 @@ CASES = [
     ("merge_ref", merge_no_empty_branch, pins.test_state_and_merge_empty_branches, ()),
     ("merge_ref", merge_no_rescale, pins.test_worked_example_two_blocks, (load_golden,)),
     ("paged_gather_ref", gather_swapped, pins.test_paged_gather_recovers_ground_truth, ()),
+    ("split_states_ref", split_states_short, pins.test_split_partials_merge_to_decode, (32,)),
+    ("decode_ref", decode_wrong_head, pins.test_decode_matches_brute_force, ()),
+    ("merge_partials_ref", merge_partials_all, pins.test_merge_partials_respects_valid_count, ()),
+    ("merge_lse_ref", merge_lse_average, pins.test_merge_lse_two_operand_form, ()),
+    ("merge_lse_ref", merge_lse_inf_as_mass, pins.test_merge_lse_two_operand_form, ()),
+    ("attention_ref", _attention_variant(use_key_mask=False), pins.test_attention_matches_brute_force,
+     (False, True, False, 3, 7)),
 ]
 
 
