@@ -51,12 +51,12 @@ namespace {
 constexpr int kHeadDim = 128;
 constexpr int kMaxGroup = 256;  // decode: query heads per KV head
 // Decode groups of up to kRowsMinGroup - 1 heads use the split kernel of
-// decode.hip (blocks of 16 heads as the columns of its MFMA); larger groups
-// use the prefill kernel with the heads as rows (32 per wave), which runs one
+// decode.hip (the heads as the 16 columns of its MFMA); larger groups use the
+// prefill kernel with the heads as rows (32 per wave), which runs one
 // workgroup per CU and is planned at one workgroup of work per CU. Measured
-// on 537 MB of K+V: g = 128 193 us against 366-394 us, g = 64 160 against
-// 207-227, g = 32 160-176 against 134-149 (one wave of rows is too few).
-constexpr int kRowsMinGroup = 33;
+// on 268-537 MB of K+V: g = 128 140-162 us against 366-429 us in blocks of
+// 16 heads; g = 32 119-128 us against 148-160; g = 24 119-121 against 143-144.
+constexpr int kRowsMinGroup = 17;
 constexpr int kRowsWgsPerCu = 1;
 
 // log2 of a power of two, else -1.

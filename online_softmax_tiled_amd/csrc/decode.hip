@@ -24,9 +24,9 @@
 // one head block and walks every tile of the split (head mode), so the four
 // waves read the same keys at the same time and each ends with a complete
 // state; a group of more than 4 head blocks spreads over several workgroups.
-// The library sends groups of more than 32 heads to the prefill kernel
+// The library sends groups of more than 16 heads to the prefill kernel
 // instead (the heads as its MFMA rows), except on a paged cache whose page
-// size is not a power of two.
+// size is not a power of two: head mode serves those.
 //
 // Per 32-key tile and wave (v_mfma_f32_16x16x32, the up to 16 query heads of
 // the head block as the 16 columns, unused columns zero):

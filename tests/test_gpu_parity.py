@@ -722,16 +722,18 @@ def test_decode_head_rows_partials_match_slices():
                 assert abs(lse_g - lse_r) / max(1.0, abs(lse_r)) < LSE_TOL
 
 
-@pytest.mark.parametrize("h,h_kv,paged", [(32, 1, False), (48, 2, True), (128, 1, False), (128, 1, True),
-                                          (17, 1, False)])
-def test_decode_large_groups(h, h_kv, paged):
-    # g = 32, 24, 17: blocks of 16 heads, one per wave (head mode); g = 128
-    # (MLA-style): the heads as the rows of the prefill kernel
-    dec = make_decode(3, h, h_kv, 128, "bf16", seed=h + h_kv, len_range=(1, 700), paged=paged, page_size=16)
+@pytest.mark.parametrize("h,h_kv,paged,page_size", [(32, 1, False, 16), (48, 2, True, 16), (128, 1, False, 16),
+                                                    (128, 1, True, 16), (17, 1, False, 16),
+                                                    (48, 2, True, 48), (17, 1, True, 80), (160, 2, True, 48)])
+def test_decode_large_groups(h, h_kv, paged, page_size):
+    # g = 32, 24, 128 (MLA-style), 17: the heads as the rows of the prefill
+    # kernel; pages of 48 or 80 tokens (not a power of two): blocks of 16
+    # heads, one per wave (head mode), with g = 80 spread over two workgroups
+    dec = make_decode(3, h, h_kv, 128, "bf16", seed=h + h_kv, len_range=(1, 700), paged=paged, page_size=page_size)
     sl = to_dev(np.asarray(dec["seq_lens"], dtype=np.int32))
     if paged:
         o, lse, plan = api.decode(to_dev(dec["q"]), to_dev(dec["k_pool"]), to_dev(dec["v_pool"]), sl,
-                                  block_table=to_dev(dec["block_table"]), page_size=16, scale=dec["scale"])
+                                  block_table=to_dev(dec["block_table"]), page_size=page_size, scale=dec["scale"])
     else:
         o, lse, plan = api.decode(to_dev(dec["q"]), to_dev(dec["k"]), to_dev(dec["v"]), sl, scale=dec["scale"])
     torch.cuda.synchronize()
