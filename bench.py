@@ -229,11 +229,12 @@ def bench_merge_lse(steps, warmup, dev, copies=3):
                 rotated_input_sets=copies)
 
 
-def bench_decode_large_group(steps, warmup, dev):
+def bench_decode_large_group(steps, warmup, dev, paged=False):
     """Decode with a 128-head group on one KV head (g = 128, the heads as
-    the rows of the prefill kernel): 32 sequences of 32768 contiguous keys,
-    537 MB of K+V (more than the 256 MB last-level cache), synthetic N(0,1)
-    drawn on the device. GB/s = K+V bytes / (split + merge time)."""
+    the rows of the prefill kernel): 32 sequences of 32768 keys, 537 MB of
+    K+V (more than the 256 MB last-level cache), synthetic N(0,1) drawn on
+    the device; contiguous, or (paged) in 16-token pages placed by a seeded
+    permutation of the pool. GB/s = K+V bytes / (split + merge time)."""
     import torch
     from online_softmax_tiled_amd import api
     B, h, h_kv, s, d = 32, 128, 1, 32768, 128
@@ -241,6 +242,16 @@ def bench_decode_large_group(steps, warmup, dev):
     q = torch.randn((B, h, d), generator=g, device=dev).to(torch.bfloat16)
     k = torch.randn((B, h_kv, s, d), generator=g, device=dev).to(torch.bfloat16)
     v = torch.randn((B, h_kv, s, d), generator=g, device=dev).to(torch.bfloat16)
+    bt, page = None, 16
+    if paged:
+        n_pg = s // page
+        perm = torch.randperm(B * n_pg, generator=torch.Generator().manual_seed(1008)).to(dev)
+        k_pool = torch.empty((B * n_pg, page, h_kv, d), dtype=k.dtype, device=dev)
+        v_pool = torch.empty_like(k_pool)
+        k_pool[perm] = k.permute(0, 2, 1, 3).reshape(B * n_pg, page, h_kv, d)
+        v_pool[perm] = v.permute(0, 2, 1, 3).reshape(B * n_pg, page, h_kv, d)
+        bt = perm.view(B, n_pg).to(torch.int32).contiguous()
+        k, v = k_pool, v_pool
     lens = np.full(B, s, dtype=np.int32)
     sl = torch.from_numpy(lens).to(dev)
     chunk, splits = api.decode_plan(lens, h, h_kv, device=dev)
@@ -252,13 +263,14 @@ def bench_decode_large_group(steps, warmup, dev):
     kv_bytes = 2 * B * h_kv * s * d * 2
 
     def full(i=0):
-        api.decode_split(q, k, v, sl, chunk, splits, part_o=po, part_m=pm, part_l=pl)
+        api.decode_split(q, k, v, sl, chunk, splits, block_table=bt, page_size=page, part_o=po, part_m=pm,
+                         part_l=pl)
         api.merge_states(po, pm, pl, sl, chunk, q.dtype, out=o, lse=lse)
 
     ms, _ = time_loop(full, steps, warmup)
     return dict(kv_bytes=kv_bytes, us_per_step=ms * 1e3, gbs=kv_bytes / (ms * 1e-3) / 1e9,
                 frac_hbm=kv_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, plan=[chunk, splits],
-                shape="B=32 h=128 h_kv=1 s=32768 d=128 bf16")
+                shape="B=32 h=128 h_kv=1 s=32768 d=128 bf16" + (", 16-token pages" if paged else ""))
 
 
 def bench_decode_contiguous(steps, warmup, dev, copies=40):
@@ -484,6 +496,9 @@ def main():
         r6 = bench_decode_large_group(max(20, args.steps), 3, dev)
         log(f"decode g=128 b32 s32768: {r6['us_per_step']:.1f} us/step, {r6['gbs']:.0f} GB/s, plan {r6['plan']}")
         decode["decode_g128_b32_s32768"] = r6
+        r7 = bench_decode_large_group(max(20, args.steps), 3, dev, paged=True)
+        log(f"decode g=128 b32 s32768 paged: {r7['us_per_step']:.1f} us/step, {r7['gbs']:.0f} GB/s, plan {r7['plan']}")
+        decode["decode_g128_b32_s32768_paged"] = r7
         for v in decode.values():
             for key in list(v):
                 if isinstance(v[key], float):

@@ -443,28 +443,58 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   // V slot 2 is read (with P = 0) in the first iteration.
   for (int i = tid; i < kVElems / 8; i += kThreads) store16(&lds_v[2][i * 8], u32x4{});
   __syncthreads();
-  if (DEC && !PAGED && n_rb <= 4 && wave >= 4) {
-    // Contiguous decode with at most 128 heads: waves 4-7 have no rows. They
-    // do their share of the staging and, each iteration, one load per
-    // 128-byte line of K (waves 4, 5) or V (waves 6, 7) of the tile kPfAhead
-    // ahead. That tile is then on its way through the L2 when the staging
-    // loads reach it, so each CU keeps about twice the bytes in flight of
-    // the staging alone (a streaming workgroup holds only one tile of loads
-    // in registers). The loaded values are discarded. Loads retire in order,
-    // so each one is consumed one iteration after its issue, where the wait
-    // for that iteration's staging loads has already covered it; the loop is
-    // unrolled by two so that the two values have fixed registers.
+  if (DEC && n_rb <= 4 && wave >= 4) {
+    // Decode with at most 128 heads: waves 4-7 have no rows. They do their
+    // share of the staging and, each iteration, one load per 128-byte line of
+    // K (waves 4, 5) or V (waves 6, 7) of the tile kPfAhead ahead. That tile
+    // is then on its way through the L2 when the staging loads reach it, so
+    // each CU keeps about twice the bytes in flight of the staging alone (a
+    // streaming workgroup holds only one tile of loads in registers). The
+    // loaded values are discarded. Loads retire in order, so each one is
+    // consumed one iteration after its issue, where the wait for that
+    // iteration's staging loads has already covered it; the loop is unrolled
+    // by two so that the two values have fixed registers. Paged: the page of
+    // a lane's line is looked up one iteration ahead, before that
+    // iteration's prefetch, so waiting for it never waits for a prefetch; a
+    // line past the keys or on a page outside the pool reads pool row 0.
+    const int lane_line = (tid - 4 * 64) & 127;   // line of this lane in a K or V tile
     const auto rs = wave < 6 ? rk : rv;
-    const uint32_t loff = (uint32_t)(((tid - 4 * 64) & 127) * 128);
+    const uint16_t* pool = wave < 6 ? p.k : p.v;
     __syncthreads();   // the other waves' reads of K(0), below
     uint32_t pf[2] = {0u, 0u};
+    int pbt[2] = {0, 0};
+    auto lookup = [&](int t) -> int {   // block-table entry of this lane's line in tile t
+      const uint32_t key = (uint32_t)(k_lo + t * kBc + (lane_line >> 1));
+      return (int)__builtin_amdgcn_raw_buffer_load_b32(r_key, (int)((key >> p.page_shift) * 4u), 0, 0);
+    };
+    if (PAGED) pbt[1] = lookup(kPfAhead);
     auto step = [&](int j, int u) {
       load_k(j + 2);
       load_v(j + 1);
-      pf[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)((uint32_t)(j + kPfAhead) * (kBc * kD * 2) + loff), 0, 0);
+      if (PAGED) {
+        pg_n[0] = page_of(j + 3, 0);
+        pg_n[1] = page_of(j + 3, 1);
+        pbt[u] = lookup(j + kPfAhead + 1);
+        const int key_l = (j + kPfAhead) * kBc + (lane_line >> 1);
+        const int page = pbt[u ^ 1];
+        const bool ok = key_l < T_k && page >= 0 && page < p.num_pages;
+        const long row = ok ? (((long)page << p.page_shift) + ((k_lo + key_l) & ((1 << p.page_shift) - 1))) * p.h_kv + kvh
+                            : 0;
+        pf[u] = *reinterpret_cast<const uint32_t*>(pool + row * kD + (lane_line & 1) * 64);
+      } else {
+        pf[u] = __builtin_amdgcn_raw_buffer_load_b32(
+            rs, (int)((uint32_t)(j + kPfAhead) * (kBc * kD * 2) + (uint32_t)lane_line * 128u), 0, 0);
+      }
       store_k(j & 1);
       store_v((j + 1) % 3);
       asm volatile("" ::"v"(pf[u ^ 1]));
+      if (PAGED) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          pg_v[i] = pg_k[i];
+          pg_k[i] = pg_n[i];
+        }
+      }
       __syncthreads();
     };
     // One barrier per iteration j = 0 .. n_tiles, as in the main loop.
