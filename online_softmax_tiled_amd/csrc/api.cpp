@@ -135,6 +135,8 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, const uint8_t*
           kMaxSeq, T_q, T_k);
   const long rows = (long)B * h * T_q;
   REQUIRE(rows * kHeadDim < (1L << 40), ATTN_ERR_INVALID, "%s: problem too large", fn);
+  // (batch, head) pairs are numbered in 32-bit ints on the device.
+  REQUIRE((long)B * h < (1L << 31), ATTN_ERR_UNSUPPORTED, "%s: B * h = %ld too large", fn, (long)B * h);
   if (rows == 0) return ok();
   REQUIRE(q && o, ATTN_ERR_INVALID, "%s: q and o must not be NULL", fn);
   REQUIRE(T_k == 0 || (k && v), ATTN_ERR_INVALID, "%s: k and v must not be NULL", fn);

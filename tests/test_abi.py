@@ -84,6 +84,7 @@ def prefill_call(lib, **kw):
     (dict(B=-1), 1, "negative"),
     (dict(q=None), 1, "NULL"),
     (dict(k=None), 1, "NULL"),
+    (dict(B=1 << 20, h=1 << 12, h_kv=1 << 12, T_q=1, T_k=1, causal=0), 2, "B * h"),
 ])
 def test_prefill_rejects_before_launch(lib, kw, code, msg):
     from online_softmax_tiled_amd import api
