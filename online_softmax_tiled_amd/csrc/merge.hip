@@ -16,10 +16,11 @@
 // Layout: one workgroup per (sequence, head, d-slice). With many splits the
 // head dimension is cut into ND = 4 slices so that more workgroups share the
 // partial traffic. Inside a workgroup, thread (s, f) of 32 split lanes x FL
-// float4 lanes sums splits s, s + 32, ... for 4 consecutive d values, with
-// the loads of U splits in flight at a time (with several slices, the first
-// U before the maximum is known); the 32 lane sums are then added through
-// LDS in lane order.
+// d-lanes sums splits s, s + 32, ... for 4 consecutive d values (one slice of
+// 32) or 16 (one slice of 128: 256 threads instead of 1024, so a CU holds
+// four times as many rows at once), with the loads of U splits in flight at
+// a time (with several slices, the first U before the maximum is known); the
+// 32 lane sums are then added through LDS in lane order.
 #include "common.h"
 
 namespace attn {
@@ -44,8 +45,8 @@ __device__ __forceinline__ float wave_max(float x) {
 }
 
 // ND: d-slices per (sequence, head); each slice is kD / ND values, handled
-// by FL = kD / ND / 4 float4 lanes and kSL = 32 split lanes (FL * 32
-// threads: 1024 for one slice, 256 for four). Split lane s sums splits s,
+// by FL = kD / ND / (4 V) d-lanes of V float4 each and kSL = 32 split lanes
+// (FL * 32 threads: 256 in both layouts used). Split lane s sums splits s,
 // s + 32, s + 64, ... in that order, with U partials in flight, and the 32
 // lane sums are added in lane order. The
 // summation order of a row therefore depends only on its own split count,
@@ -56,11 +57,11 @@ __device__ __forceinline__ float wave_max(float x) {
 // the sequence length alone).
 constexpr int kSL = 32;
 
-template <int DT, int ND, int U>
-__global__ __launch_bounds__(kD / ND / 4 * kSL) void merge_kernel(MergeParams p) {
+template <int DT, int ND, int U, int V>
+__global__ __launch_bounds__(kD / ND / (4 * V) * kSL) void merge_kernel(MergeParams p) {
   using E = Elem<DT>;
   constexpr int kSlice = kD / ND;
-  constexpr int FL = kSlice / 4;
+  constexpr int FL = kSlice / (4 * V);
   constexpr int NT = FL * kSL;
   constexpr int NW = NT / 64;
   __shared__ float red_m[NW];
@@ -85,16 +86,18 @@ __global__ __launch_bounds__(kD / ND / 4 * kSL) void merge_kernel(MergeParams p)
   constexpr int U0 = ND > 1 ? U : 0;
   const int lim = ND > 1 ? p.max_splits : n;
   const int sl = tid / FL;
-  const int d = (tid % FL) * 4;
+  const int d = (tid % FL) * 4 * V;
   float li0[U0 > 0 ? U0 : 1], mi0[U0 > 0 ? U0 : 1];
-  f32x4 oi0[U0 > 0 ? U0 : 1];
+  f32x4 oi0[U0 > 0 ? U0 : 1][V];
 #pragma unroll
   for (int u = 0; u < U0; ++u) {
     const int i = sl + u * kSL;
     const bool in = i < lim;
     li0[u] = in ? p.part_l[base + i] : 0.f;
     mi0[u] = in ? p.part_m[base + i] : -INFINITY;
-    oi0[u] = in ? *reinterpret_cast<const f32x4*>(&p.part_o[(base + i) * kD + d0 + d]) : f32x4{};
+#pragma unroll
+    for (int c = 0; c < V; ++c)
+      oi0[u][c] = in ? *reinterpret_cast<const f32x4*>(&p.part_o[(base + i) * kD + d0 + d + 4 * c]) : f32x4{};
   }
   float mloc = -INFINITY;
   for (int i = tid; i < lim; i += NT) {
@@ -115,37 +118,44 @@ __global__ __launch_bounds__(kD / ND / 4 * kSL) void merge_kernel(MergeParams p)
     return;
   }
 
-  f32x4 acc = f32x4{};
+  f32x4 acc[V];
+#pragma unroll
+  for (int c = 0; c < V; ++c) acc[c] = f32x4{};
   float lacc = 0.f;
 #pragma unroll
   for (int u = 0; u < U0; ++u) {
     if (sl + u * kSL < n && li0[u] > 0.f) {
       const float w = fast_exp2((mi0[u] - big) * kLog2e);
       lacc += w * li0[u];
-      acc += w * oi0[u];
+#pragma unroll
+      for (int c = 0; c < V; ++c) acc[c] += w * oi0[u][c];
     }
   }
   for (int i0 = sl + U0 * kSL; i0 < n; i0 += U * kSL) {
     float li[U], mi[U];
-    f32x4 oi[U];
+    f32x4 oi[U][V];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = i0 + u * kSL;
       const bool ok = i < n;
       li[u] = ok ? p.part_l[base + i] : 0.f;
       mi[u] = ok ? p.part_m[base + i] : -INFINITY;
-      oi[u] = ok ? *reinterpret_cast<const f32x4*>(&p.part_o[(base + i) * kD + d0 + d]) : f32x4{};
+#pragma unroll
+      for (int c = 0; c < V; ++c)
+        oi[u][c] = ok ? *reinterpret_cast<const f32x4*>(&p.part_o[(base + i) * kD + d0 + d + 4 * c]) : f32x4{};
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (li[u] > 0.f) {
         const float w = fast_exp2((mi[u] - big) * kLog2e);
         lacc += w * li[u];
-        acc += w * oi[u];
+#pragma unroll
+        for (int c = 0; c < V; ++c) acc[c] += w * oi[u][c];
       }
     }
   }
-  *reinterpret_cast<f32x4*>(&red_o[sl][d]) = acc;
+#pragma unroll
+  for (int c = 0; c < V; ++c) *reinterpret_cast<f32x4*>(&red_o[sl][d + 4 * c]) = acc[c];
   if (tid % FL == 0) red_l[sl] = lacc;
   __syncthreads();
   if (tid < kSlice / 2) {
@@ -170,9 +180,9 @@ hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
   // Many splits and few (sequence, head) pairs: cut d into 4 slices so that
   // more workgroups share the partial traffic (same bits as one slice).
   if (p.max_splits >= 64 && (long)p.B * p.h < 1024) {
-    hipLaunchKernelGGL((merge_kernel<DT, 4, 8>), dim3((unsigned)(p.B * p.h), 4), dim3(kD / 4 / 4 * kSL), 0, stream, p);
+    hipLaunchKernelGGL((merge_kernel<DT, 4, 8, 1>), dim3((unsigned)(p.B * p.h), 4), dim3(kD / 4 / 4 * kSL), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((merge_kernel<DT, 1, 4>), dim3((unsigned)(p.B * p.h), 1), dim3(kD / 4 * kSL), 0, stream, p);
+    hipLaunchKernelGGL((merge_kernel<DT, 1, 4, 4>), dim3((unsigned)(p.B * p.h), 1), dim3(kD / 16 * kSL), 0, stream, p);
   }
   return hipGetLastError();
 }
