@@ -398,6 +398,65 @@ def test_decode_graph_replay_matches_eager():
     assert_outputs(o, lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16", "graph decode")
 
 
+def test_prefill_and_row_decode_graph_replay_matches_eager():
+    # key-masked prefill (tile list), paged prefill (launch order in the
+    # kernel arguments) and a 64-head-group decode (the row form, with its
+    # prefetching waves) captured in one HIP graph; every replay, with eager
+    # work and synchronisations between replays, reproduces the eager bits
+    from online_softmax_tiled_amd.workloads import make_chunked_prefill
+    inp = make_prefill(1, 8, 2, 200, 200, 128, "bf16", seed=23, causal=True, key_tile_p=0.3)
+    q, k, v, km = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"]), to_dev(inp["key_mask"])
+    o1 = torch.empty_like(q)
+    l1 = torch.empty((1, 8, 200), dtype=torch.float32, device=DEV)
+    c = make_chunked_prefill(3, 8, 2, 128, "bf16", seed=24, ctx_range=(100, 400), new_range=(10, 90))
+    cq, cu, kp, vp = to_dev(c["q"]), to_dev(c["cu_seqlens_q"]), to_dev(c["k_pool"]), to_dev(c["v_pool"])
+    bt, slk = to_dev(c["block_table"]), to_dev(c["seq_lens_k"])
+    o2 = torch.empty_like(cq)
+    l2 = torch.empty(cq.shape[:2], dtype=torch.float32, device=DEV)
+    dec = make_decode(B=2, h=64, h_kv=1, d=128, dtype="bf16", seed=25, seq_lens=[300, 1100], paged=False)
+    dq, dk, dv, dsl = to_dev(dec["q"]), to_dev(dec["k"]), to_dev(dec["v"]), to_dev(dec["seq_lens"])
+    chunk, splits = api.decode_plan(dec["seq_lens"], 64, 1)
+    po = torch.empty((2, 64, splits, 128), dtype=torch.float32, device=DEV)
+    pm = torch.empty((2, 64, splits), dtype=torch.float32, device=DEV)
+    pl = torch.empty_like(pm)
+    o3 = torch.empty((2, 64, 128), dtype=torch.bfloat16, device=DEV)
+    l3 = torch.empty((2, 64), dtype=torch.float32, device=DEV)
+    outs = (o1, l1, o2, l2, o3, l3)
+
+    def step():
+        api.prefill(q, k, v, causal=True, scale=inp["scale"], key_mask=km, out=o1, lse=l1)
+        api.prefill_paged(cq, cu, c["max_q"], kp, vp, bt, slk, causal=True, scale=c["scale"], out=o2, lse=l2,
+                          seq_lens_k_host=c["seq_lens_k"])
+        api.decode_split(dq, dk, dv, dsl, chunk, splits, scale=dec["scale"], part_o=po, part_m=pm, part_l=pl)
+        api.merge_states(po, pm, pl, dsl, chunk, torch.bfloat16, out=o3, lse=l3)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(4):
+        for t in outs:
+            t.fill_(3.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for t, e in zip(outs, eager):
+            assert torch.equal(t.view(torch.int16) if t.dtype == torch.bfloat16 else t,
+                               e.view(torch.int16) if e.dtype == torch.bfloat16 else e), rep
+        step()                              # eager work between replays
+        torch.cuda.synchronize()
+    o_ref, lse_ref = decode_ref(dec["q"], dec["k_seqs"], dec["v_seqs"], dec["seq_lens"], dec["scale"])
+    assert_outputs(o3, l3.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16", "graph row-form decode")
+
+
 # ------------------------------------------------------------------ (O, LSE) merge
 
 @pytest.mark.parametrize("dtype,T_k,split", [("bf16", 300, 128), ("f16", 257, 1), ("bf16", 200, 199)])
