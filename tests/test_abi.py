@@ -191,6 +191,27 @@ def test_plan_on_the_measured_workloads(lib):
     assert units >= 12 * 256 * 0.9 and splits <= 16
 
 
+def test_plan_for_large_groups(lib):
+    # more than 16 heads per KV head run on the row form, one workgroup per
+    # CU: the plan aims at one workgroup of work per CU
+    assert plan([32768] * 32, 128, 1, 256) == (4096, 8)
+    assert plan([16384] * 64, 32, 1, 256) == (4096, 4)
+    # the 16-head kernel's target (12 per CU) up to 16 heads
+    chunk16, _ = plan([16384] * 64, 16, 1, 256)
+    assert chunk16 < 4096
+    rng = np.random.default_rng(2)
+    for _ in range(100):
+        B = int(rng.integers(1, 65))
+        h_kv = int(rng.choice([1, 2, 4]))
+        g = int(rng.choice([17, 24, 32, 64, 128]))
+        lens = rng.integers(0, 40000, size=B)
+        chunk, splits = plan(lens, h_kv * g, h_kv, 256)
+        assert chunk % 64 == 0 and chunk >= 64
+        units = h_kv * sum(math.ceil(int(s) / chunk) for s in lens)
+        assert units >= 256 or chunk == 64
+        assert units <= 2 * 256 or chunk == 128        # about one per CU, never far above
+
+
 def test_plan_rejects_bad_input(lib):
     from online_softmax_tiled_amd import api
     with pytest.raises(api.AttnError):
