@@ -61,6 +61,14 @@
 //   per-tile key bits as the key mask. The host may pass a launch order of
 //   the sequences (longest context first).
 //
+// Decode form (DEC)
+//   Split-KV decode of large GQA groups: the rows are the group's query heads
+//   (one token each, 32 per wave), one workgroup per (sequence, KV head,
+//   split), and the epilogue writes the split's partial state for the merge.
+//   With at most 128 heads (STG), waves 4-7 hold no rows and stage every K/V
+//   tile two iterations ahead, so a CU keeps two tile pairs of loads in
+//   flight while waves 0-3 compute.
+//
 // Two running sums per row: l, the fp32 sum of the weights p (for the LSE),
 // and l~, the sum of the weights as rounded to the operand dtype for the PV
 // product. O~ accumulates the rounded weights, so it is divided by l~: the
@@ -95,7 +103,6 @@ constexpr int kKElems = kBc * kKStr;
 constexpr int kVElems = kBc * kVStr;
 constexpr float kTau = 8.f;         // allowed lag of the reference max (log2 units)
 constexpr int kMaxOrder = 512;      // sequences a paged launch can reorder
-constexpr int kPfAhead = 3;         // DEC: tiles between a prefetch and its iteration
 constexpr int kMaxListTiles = 4096; // key-masked prefill: longest list of visible tiles
 
 struct PrefillParams {
@@ -136,10 +143,11 @@ struct PrefillParams {
   uint16_t order[kMaxOrder];
 };
 
-template <int DT, bool CAUSAL, bool KMASK, bool PAGED, bool DEC>
+template <int DT, bool CAUSAL, bool KMASK, bool PAGED, bool DEC, bool STG>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   using E = Elem<DT>;
   static_assert(!PAGED || KMASK, "paged K/V are addressed through the key-bit path");
+  static_assert(!STG || DEC, "staging waves are a decode form (at most 4 row blocks)");
   // K of tile t lives in slot t % 2 (read in iteration t - 1), V of tile t in
   // slot t % 3 (read in iteration t + 1).
   __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kKElems];
@@ -443,58 +451,83 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   // V slot 2 is read (with P = 0) in the first iteration.
   for (int i = tid; i < kVElems / 8; i += kThreads) store16(&lds_v[2][i * 8], u32x4{});
   __syncthreads();
-  if (DEC && n_rb <= 4 && wave >= 4) {
-    // Decode with at most 128 heads: waves 4-7 have no rows. They do their
-    // share of the staging and, each iteration, one load per 128-byte line of
-    // K (waves 4, 5) or V (waves 6, 7) of the tile kPfAhead ahead. That tile
-    // is then on its way through the L2 when the staging loads reach it, so
-    // each CU keeps about twice the bytes in flight of the staging alone (a
-    // streaming workgroup holds only one tile of loads in registers). The
-    // loaded values are discarded. Loads retire in order, so each one is
-    // consumed one iteration after its issue, where the wait for that
-    // iteration's staging loads has already covered it; the loop is unrolled
-    // by two so that the two values have fixed registers. Paged: the page of
-    // a lane's line is looked up one iteration ahead, before that
-    // iteration's prefetch, so waiting for it never waits for a prefetch; a
-    // line past the keys or on a page outside the pool reads pool row 0.
-    const int lane_line = (tid - 4 * 64) & 127;   // line of this lane in a K or V tile
-    const auto rs = wave < 6 ? rk : rv;
-    const uint16_t* pool = wave < 6 ? p.k : p.v;
+  // STG (decode with at most 128 heads, launched only for n_rb <= 4): waves
+  // 4-7 have no rows and stage every K/V tile of the main loop; waves 0-3
+  // only compute.
+  constexpr bool stagers = STG;
+  if (STG && wave >= 4) {
+    // The pair stored in iteration j, K(j+2) and V(j+1), was loaded in
+    // iteration j-2 into one of two register sets, so each CU keeps two tile
+    // pairs (64 KB) of loads in flight instead of one. Each lane holds 16-byte
+    // chunk st + 256 i of a tile (row st / 16 + 16 i). Paged: the pages of the
+    // loads issued in iteration j are looked up in iteration j-1, before that
+    // iteration's tile loads; loads retire in order, so waiting for the
+    // lookups waits only for loads issued before them, i.e. the pair stored in
+    // iteration j. The loop is unrolled by two so that the register sets and
+    // the page sets have fixed registers (a copy of a pending load would wait
+    // for it). Loads issued for tiles past the end are never stored.
+    const int st = tid - 4 * 64;
     __syncthreads();   // the other waves' reads of K(0), below
-    uint32_t pf[2] = {0u, 0u};
-    int pbt[2] = {0, 0};
-    auto lookup = [&](int t) -> int {   // block-table entry of this lane's line in tile t
-      const uint32_t key = (uint32_t)(k_lo + t * kBc + (lane_line >> 1));
+    auto s_row = [&](int i) { return (st >> 4) + 16 * i; };
+    auto s_page = [&](int t, int i) -> int {
+      const uint32_t key = (uint32_t)(k_lo + t * kBc + s_row(i));
       return (int)__builtin_amdgcn_raw_buffer_load_b32(r_key, (int)((key >> p.page_shift) * 4u), 0, 0);
     };
-    if (PAGED) pbt[1] = lookup(kPfAhead);
-    auto step = [&](int j, int u) {
-      load_k(j + 2);
-      load_v(j + 1);
-      if (PAGED) {
-        pg_n[0] = page_of(j + 3, 0);
-        pg_n[1] = page_of(j + 3, 1);
-        pbt[u] = lookup(j + kPfAhead + 1);
-        const int key_l = (j + kPfAhead) * kBc + (lane_line >> 1);
-        const int page = pbt[u ^ 1];
-        const bool ok = key_l < T_k && page >= 0 && page < p.num_pages;
-        const long row = ok ? (((long)page << p.page_shift) + ((k_lo + key_l) & ((1 << p.page_shift) - 1))) * p.h_kv + kvh
-                            : 0;
-        pf[u] = *reinterpret_cast<const uint32_t*>(pool + row * kD + (lane_line & 1) * 64);
-      } else {
-        pf[u] = __builtin_amdgcn_raw_buffer_load_b32(
-            rs, (int)((uint32_t)(j + kPfAhead) * (kBc * kD * 2) + (uint32_t)lane_line * 128u), 0, 0);
-      }
-      store_k(j & 1);
-      store_v((j + 1) % 3);
-      asm volatile("" ::"v"(pf[u ^ 1]));
-      if (PAGED) {
+    // Paged: a chunk whose row is past the keys or on a page outside the pool
+    // loads pool row 0 (no branch: a conditional load would make the compiler
+    // count it as possibly not issued and wait for later loads too) and is
+    // stored as zeros; bit i (K) and 4 + i (V) of ok[u] mark the valid chunks.
+    auto s_load = [&](const uint16_t* pool, const decltype(rk)& r, int t, int i, int page, uint32_t& ok,
+                      int bit) -> u32x4 {
+      if (!PAGED) return buffer_load16(r, ((uint32_t)(t * kBc + s_row(i)) * kD + (uint32_t)(st & 15) * 8u) * 2u);
+      const int key_l = t * kBc + s_row(i);
+      const bool valid = key_l < T_k && page >= 0 && page < p.num_pages;
+      const long row =
+          valid ? (((long)page << p.page_shift) + ((k_lo + key_l) & ((1 << p.page_shift) - 1))) * p.h_kv + kvh : 0;
+      ok |= valid ? 1u << bit : 0u;
+      return load16(pool + row * kD + (st & 15) * 8);
+    };
+    u32x4 sk[2][4], sv[2][4];
+    uint32_t ok[2] = {0u, 0u};
+    int pgk[2][4], pgv[2][4];   // paged: pages of the K and V loads of the next two iterations
+    auto lookup = [&](int u, int tk, int tv) {
+      if (!PAGED) return;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          pg_v[i] = pg_k[i];
-          pg_k[i] = pg_n[i];
-        }
+      for (int i = 0; i < 4; ++i) {
+        pgk[u][i] = s_page(tk, i);
+        pgv[u][i] = s_page(tv, i);
       }
+    };
+    auto issue = [&](int u, int tk, int tv, int pu) {
+      ok[u] = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sk[u][i] = s_load(p.k, rk, tk, i, PAGED ? pgk[pu][i] : 0, ok[u], i);
+        sv[u][i] = s_load(p.v, rv, tv, i, PAGED ? pgv[pu][i] : 0, ok[u], 4 + i);
+      }
+    };
+    auto put = [&](int j, int u) {
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        store16(&lds_k[j & 1][s_row(i) * kKStr + (st & 15) * 8], !PAGED || (ok[u] >> i & 1u) ? sk[u][i] : zero);
+        store16(&lds_v[(j + 1) % 3][s_row(i) * kVStr + (st & 15) * 8],
+                !PAGED || (ok[u] >> (4 + i) & 1u) ? sv[u][i] : zero);
+      }
+    };
+    // The pairs stored in iterations 0 and 1, with the pages of iteration 0's
+    // loads looked up between them: the loads then stand in the order of the
+    // steady state (pair, pages, pair), so the waits the compiler derives for
+    // the loop hold on entry too.
+    lookup(1, 2, 1);
+    issue(0, 2, 1, 1);
+    lookup(1, 3, 2);
+    lookup(0, 4, 3);
+    issue(1, 3, 2, 1);
+    auto step = [&](int j, int u) {
+      put(j, u);
+      lookup(u ^ 1, j + 5, j + 4);
+      issue(u, j + 4, j + 3, u);
       __syncthreads();
     };
     // One barrier per iteration j = 0 .. n_tiles, as in the main loop.
@@ -503,8 +536,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
       step(j, 0);
       step(j + 1, 1);
     }
-    if (j <= n_tiles) step(j, 0);
-    asm volatile("" ::"v"(pf[0]), "v"(pf[1]));
+    if (j <= n_tiles) {
+      put(j, 0);
+      __syncthreads();
+    }
     return;
   }
   qk(lds_k[0], sc);
@@ -517,11 +552,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     // Tiles past the end load as zeros; the slots they go to are free, so the
     // loads and stores need no conditions and the iteration stays one block
     // from the rescale below to the barrier.
-    load_k(tile_at(j + 2));
-    load_v(tile_at(j + 1));
-    if (PAGED) {
-      pg_n[0] = page_of(j + 3, 0);
-      pg_n[1] = page_of(j + 3, 1);
+    if (!stagers) {
+      load_k(tile_at(j + 2));
+      load_v(tile_at(j + 1));
+      if (PAGED) {
+        pg_n[0] = page_of(j + 3, 0);
+        pg_n[1] = page_of(j + 3, 1);
+      }
     }
     int kraw = 0;
     const int t_kb = tile_at(j + 1);
@@ -657,16 +694,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     sc[0] = sn[0];
     sc[1] = sn[1];
     if (KMASK) kbits = key_ballot(t_kb, kraw);
-    if (PAGED) {
+    if (!stagers) {
+      if (PAGED) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        pg_v[i] = pg_k[i];
-        pg_k[i] = pg_n[i];
+        for (int i = 0; i < 2; ++i) {
+          pg_v[i] = pg_k[i];
+          pg_k[i] = pg_n[i];
+        }
       }
+      store_k(j & 1);
+      store_v((j + 1) % 3);
     }
-
-    store_k(j & 1);
-    store_v((j + 1) % 3);
     __syncthreads();
   }
 
@@ -718,7 +756,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
 template <int DT, bool CAUSAL, bool KMASK, bool PAGED>
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.n_grp * p.B * p.h_kv));
-  hipLaunchKernelGGL((prefill_kernel<DT, CAUSAL, KMASK, PAGED, false>), grid, dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((prefill_kernel<DT, CAUSAL, KMASK, PAGED, false, false>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -727,7 +765,10 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
 template <int DT, bool PAGED>
 hipError_t launch_decode_rows(const PrefillParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((long)p.B * p.h_kv * p.max_splits));
-  hipLaunchKernelGGL((prefill_kernel<DT, false, PAGED, PAGED, true>), grid, dim3(kThreads), 0, stream, p);
+  if (p.n_rb <= 4)
+    hipLaunchKernelGGL((prefill_kernel<DT, false, PAGED, PAGED, true, true>), grid, dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((prefill_kernel<DT, false, PAGED, PAGED, true, false>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

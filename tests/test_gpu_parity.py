@@ -716,7 +716,7 @@ def test_decode_head_rows(dtype, paged, page_size, plans):
 
 
 def test_decode_head_rows_repeatable():
-    # g = 128, contiguous: waves 4-7 only stage and prefetch, and reach
+    # g = 128, contiguous: waves 4-7 only stage, and reach
     # iteration 0's store of K(2) into K(0)'s slot long before the other
     # waves; a barrier after the reads of K(0) keeps that store out of them.
     # Short splits put a first tile in every workgroup; every run must give
