@@ -65,9 +65,10 @@
 //   Split-KV decode of large GQA groups: the rows are the group's query heads
 //   (one token each, 32 per wave), one workgroup per (sequence, KV head,
 //   split), and the epilogue writes the split's partial state for the merge.
-//   With at most 128 heads (STG), waves 4-7 hold no rows and stage every K/V
-//   tile two iterations ahead, so a CU keeps two tile pairs of loads in
-//   flight while waves 0-3 compute.
+//   With at most 128 heads (STG != 0), waves 4-7 hold no rows and stage
+//   every K/V tile two iterations ahead, so a CU keeps two tile pairs of
+//   loads in flight while waves 0-3 compute; on a paged pool under 4 GB
+//   (STG == 2) they address it with range-checked 32-bit buffer offsets.
 //
 // Two running sums per row: l, the fp32 sum of the weights p (for the LSE),
 // and l~, the sum of the weights as rounded to the operand dtype for the PV
@@ -137,17 +138,25 @@ struct PrefillParams {
   float* part_m;
   float* part_l;
   int chunk, max_splits, s_max;
+  // Paged decode with staging waves (STG == 2): bytes of one K (or V) pool
+  // and of one page of it, when the pool is under 4 GB, so that the staging
+  // waves address it with 32-bit buffer offsets.
+  uint32_t pool_bytes, page_bytes;
   // Optional launch order of the sequences (longest context first), given
   // when the host knows the key counts; n_order = 0 means natural order.
   int n_order;
   uint16_t order[kMaxOrder];
 };
 
-template <int DT, bool CAUSAL, bool KMASK, bool PAGED, bool DEC, bool STG>
+// STG: 0 = every wave computes and stages; 1 = decode with staging waves
+// (at most 4 row blocks); 2 = the same on a paged pool under 4 GB, addressed
+// with range-checked 32-bit buffer offsets.
+template <int DT, bool CAUSAL, bool KMASK, bool PAGED, bool DEC, int STG>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   using E = Elem<DT>;
   static_assert(!PAGED || KMASK, "paged K/V are addressed through the key-bit path");
-  static_assert(!STG || DEC, "staging waves are a decode form (at most 4 row blocks)");
+  static_assert(STG == 0 || DEC, "staging waves are a decode form (at most 4 row blocks)");
+  static_assert(STG != 2 || PAGED, "32-bit pool offsets are a paged form");
   // K of tile t lives in slot t % 2 (read in iteration t - 1), V of tile t in
   // slot t % 3 (read in iteration t + 1).
   __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kKElems];
@@ -239,8 +248,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   }
 
   const size_t kv_base = PAGED ? 0 : DEC ? ((size_t)bk * p.s_max + k_lo) * kD : (size_t)bk * T_k * kD;
-  const auto rk = make_rsrc(p.k + kv_base, PAGED ? 0u : (uint32_t)T_k * kD * 2);
-  const auto rv = make_rsrc(p.v + kv_base, PAGED ? 0u : (uint32_t)T_k * kD * 2);
+  // (STG == 2: the whole pools)
+  const uint32_t kv_range = PAGED ? (STG == 2 ? p.pool_bytes : 0u) : (uint32_t)T_k * kD * 2;
+  const auto rk = make_rsrc(p.k + kv_base, kv_range);
+  const auto rv = make_rsrc(p.v + kv_base, kv_range);
 
   // Staging: 1024 16-byte chunks per tile for K and for V; chunk tid + 512 i
   // holds key chunk / 16, d-chunk chunk % 16.
@@ -454,8 +465,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   // STG (decode with at most 128 heads, launched only for n_rb <= 4): waves
   // 4-7 have no rows and stage every K/V tile of the main loop; waves 0-3
   // only compute.
-  constexpr bool stagers = STG;
-  if (STG && wave >= 4) {
+  constexpr bool stagers = STG != 0;
+  if (stagers && wave >= 4) {
     // The pair stored in iteration j, K(j+2) and V(j+1), was loaded in
     // iteration j-2 into one of two register sets, so each CU keeps two tile
     // pairs (64 KB) of loads in flight instead of one. Each lane holds 16-byte
@@ -481,6 +492,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
                       int bit) -> u32x4 {
       if (!PAGED) return buffer_load16(r, ((uint32_t)(t * kBc + s_row(i)) * kD + (uint32_t)(st & 15) * 8u) * 2u);
       const int key_l = t * kBc + s_row(i);
+      if (STG == 2) {
+        // A row past the keys or on a page outside the pool gets an offset
+        // past the pool's range and reads zeros: no pool-row-0 load, no
+        // select when stored.
+        const bool valid = key_l < T_k && (uint32_t)page < (uint32_t)p.num_pages;
+        const uint32_t slot = (uint32_t)(k_lo + key_l) & ((1u << p.page_shift) - 1u);
+        const uint32_t off = (uint32_t)page * p.page_bytes + (slot * (uint32_t)p.h_kv + (uint32_t)kvh) * (kD * 2u) +
+                             (uint32_t)(st & 15) * 16u;
+        return buffer_load16(r, valid ? off : 0xFFFFFFF0u);
+      }
       const bool valid = key_l < T_k && page >= 0 && page < p.num_pages;
       const long row =
           valid ? (((long)page << p.page_shift) + ((k_lo + key_l) & ((1 << p.page_shift) - 1))) * p.h_kv + kvh : 0;
@@ -510,23 +531,28 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
       const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        store16(&lds_k[j & 1][s_row(i) * kKStr + (st & 15) * 8], !PAGED || (ok[u] >> i & 1u) ? sk[u][i] : zero);
+        const bool as_is = !PAGED || STG == 2;
+        store16(&lds_k[j & 1][s_row(i) * kKStr + (st & 15) * 8], as_is || (ok[u] >> i & 1u) ? sk[u][i] : zero);
         store16(&lds_v[(j + 1) % 3][s_row(i) * kVStr + (st & 15) * 8],
-                !PAGED || (ok[u] >> (4 + i) & 1u) ? sv[u][i] : zero);
+                as_is || (ok[u] >> (4 + i) & 1u) ? sv[u][i] : zero);
       }
     };
     // The pairs stored in iterations 0 and 1, with the pages of iteration 0's
     // loads looked up between them: the loads then stand in the order of the
     // steady state (pair, pages, pair), so the waits the compiler derives for
     // the loop hold on entry too.
+    // (The scheduling fences keep the compiler from moving tile loads above
+    // the lookups issued before them.)
     lookup(1, 2, 1);
     issue(0, 2, 1, 1);
     lookup(1, 3, 2);
     lookup(0, 4, 3);
+    __builtin_amdgcn_sched_barrier(0);
     issue(1, 3, 2, 1);
     auto step = [&](int j, int u) {
       put(j, u);
       lookup(u ^ 1, j + 5, j + 4);
+      __builtin_amdgcn_sched_barrier(0);
       issue(u, j + 4, j + 3, u);
       __syncthreads();
     };
@@ -756,7 +782,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
 template <int DT, bool CAUSAL, bool KMASK, bool PAGED>
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.n_grp * p.B * p.h_kv));
-  hipLaunchKernelGGL((prefill_kernel<DT, CAUSAL, KMASK, PAGED, false, false>), grid, dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((prefill_kernel<DT, CAUSAL, KMASK, PAGED, false, 0>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -765,10 +791,16 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
 template <int DT, bool PAGED>
 hipError_t launch_decode_rows(const PrefillParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((long)p.B * p.h_kv * p.max_splits));
-  if (p.n_rb <= 4)
-    hipLaunchKernelGGL((prefill_kernel<DT, false, PAGED, PAGED, true, true>), grid, dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((prefill_kernel<DT, false, PAGED, PAGED, true, false>), grid, dim3(kThreads), 0, stream, p);
+  if (p.n_rb > 4)
+    hipLaunchKernelGGL((prefill_kernel<DT, false, PAGED, PAGED, true, 0>), grid, dim3(kThreads), 0, stream, p);
+  else if constexpr (PAGED) {
+    if (p.pool_bytes != 0)
+      hipLaunchKernelGGL((prefill_kernel<DT, false, true, true, true, 2>), grid, dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((prefill_kernel<DT, false, true, true, true, 1>), grid, dim3(kThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((prefill_kernel<DT, false, false, false, true, 1>), grid, dim3(kThreads), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
@@ -867,8 +899,18 @@ hipError_t decode_split_rows(const void* q, const void* k, const void* v, const 
   p.chunk = chunk_keys;
   p.max_splits = max_splits;
   p.s_max = s_max;
-  if (B == 0 || h == 0) return hipSuccess;
   const bool paged = block_table != nullptr;
+  if (paged) {
+    // 32-bit buffer offsets when a pool [num_pages, page_size, h_kv, d] is
+    // under 4 GB (with room for the out-of-range offset of invalid rows).
+    const uint64_t page_bytes = ((uint64_t)h_kv << page_shift) * kD * 2;
+    const uint64_t pool_bytes = (uint64_t)num_pages * page_bytes;
+    if (pool_bytes <= 0xFFFFFF00ull) {
+      p.pool_bytes = (uint32_t)pool_bytes;
+      p.page_bytes = (uint32_t)page_bytes;
+    }
+  }
+  if (B == 0 || h == 0) return hipSuccess;
   if (dtype == ATTN_DTYPE_BF16)
     return paged ? launch_decode_rows<ATTN_DTYPE_BF16, true>(p, stream) : launch_decode_rows<ATTN_DTYPE_BF16, false>(p, stream);
   return paged ? launch_decode_rows<ATTN_DTYPE_F16, true>(p, stream) : launch_decode_rows<ATTN_DTYPE_F16, false>(p, stream);

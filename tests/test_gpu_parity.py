@@ -592,6 +592,28 @@ def _run_paged_prefill(c, causal, rows_per_seq=None, host_order=False):
         assert_outputs(ob, lb, o_ref, lse_ref, c["dtype"], f"paged prefill seq {b} ({tq} new / {tk} keys)")
 
 
+def test_paged_prefill_pool_over_4gb():
+    # the chunked-prefill kernel on pools of 2^19 + 64 pages of 16 keys x 2
+    # KV heads (4.3 GB each, NaN-filled), half the used pages past 4 GB
+    from online_softmax_tiled_amd.workloads import make_chunked_prefill
+    c = make_chunked_prefill(3, 8, 2, 128, "bf16", seed=77, ctx_range=(100, 400), new_range=(10, 90), page_size=16)
+    n_big = (1 << 19) + 64
+    assert n_big * 16 * 2 * 128 * 2 > 1 << 32
+    n_used = c["k_pool"].shape[0]
+    new_id = np.array([n_big - 1 - p if p % 2 == 0 else p for p in range(n_used)], dtype=np.int64)
+    k_big = torch.full((n_big, 16, 2, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+    v_big = torch.full_like(k_big, float("nan"))
+    idx = torch.from_numpy(new_id).to(DEV)
+    k_big[idx] = to_dev(c["k_pool"])
+    v_big[idx] = to_dev(c["v_pool"])
+    bt = c["block_table"].astype(np.int64)
+    c = dict(c, k_pool=k_big, v_pool=v_big,
+             block_table=np.where(bt >= 0, new_id[np.maximum(bt, 0)], -1).astype(np.int32))
+    _run_paged_prefill(c, True)
+    del c, k_big, v_big
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("dtype,page_size,causal,host_order", [("bf16", 16, True, False), ("f16", 32, True, True),
                                                                ("bf16", 64, False, True), ("bf16", 16, False, False)])
 def test_paged_prefill_small(dtype, page_size, causal, host_order):
@@ -755,6 +777,41 @@ def test_decode_head_rows_page_outside_pool():
         torch.cuda.synchronize()
         assert_outputs(o, lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16",
                        f"decode g=128 pages outside the pool plan={used}")
+
+
+def test_decode_head_rows_pool_over_4gb():
+    # pools of 2^20 + 64 pages of 16 keys (4.3 GB each, NaN-filled): past
+    # 4 GB the staging waves take their 64-bit path; half the pages sit past
+    # the 4 GB mark, one table entry is outside the pool (its rows load pool
+    # row 0, here NaN, and must be stored as zeros), the rest stay low
+    lens = [500, 77]
+    dec = make_decode(B=2, h=64, h_kv=1, d=128, dtype="bf16", seed=44, seq_lens=lens, paged=True, page_size=16)
+    n_big = (1 << 20) + 64
+    assert n_big * 16 * 128 * 2 > 1 << 32
+    n_used = dec["k_pool"].shape[0]
+    new_id = np.array([n_big - 1 - p if p % 2 == 0 else p for p in range(n_used)], dtype=np.int64)
+    assert 0 not in new_id
+    k_big = torch.full((n_big, 16, 1, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+    v_big = torch.full_like(k_big, float("nan"))
+    idx = torch.from_numpy(new_id).to(DEV)
+    k_big[idx] = to_dev(dec["k_pool"])
+    v_big[idx] = to_dev(dec["v_pool"])
+    bt = dec["block_table"].astype(np.int64)
+    bt = np.where(bt >= 0, new_id[np.maximum(bt, 0)], -1).astype(np.int32)
+    bt[0, 3] = n_big + 9                       # keys 48..63 of sequence 0
+    keep0 = np.r_[0:48, 64:500]
+    k_seqs = [dec["k_seqs"][0][:, keep0], dec["k_seqs"][1]]
+    v_seqs = [dec["v_seqs"][0][:, keep0], dec["v_seqs"][1]]
+    o_ref, lse_ref = decode_ref(dec["q"], k_seqs, v_seqs, np.array([keep0.size, 77]), dec["scale"])
+    sl = to_dev(dec["seq_lens"])
+    for plan in (None, (64, 9)):
+        o, lse, used = api.decode(to_dev(dec["q"]), k_big, v_big, sl, seq_lens_host=dec["seq_lens"],
+                                  block_table=to_dev(bt), page_size=16, scale=dec["scale"], plan=plan)
+        torch.cuda.synchronize()
+        assert_outputs(o, lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16",
+                       f"decode g=64 on 4.3 GB pools plan={used}")
+    del k_big, v_big
+    torch.cuda.empty_cache()
 
 
 def test_decode_head_rows_partials_match_slices():
