@@ -65,10 +65,14 @@
 //   Split-KV decode of large GQA groups: the rows are the group's query heads
 //   (one token each, 32 per wave), one workgroup per (sequence, KV head,
 //   split), and the epilogue writes the split's partial state for the merge.
-//   With at most 128 heads (STG != 0), waves 4-7 hold no rows and stage
+//   With at most 128 heads (kStagers), waves 4-7 hold no rows and stage
 //   every K/V tile two iterations ahead, so a CU keeps two tile pairs of
-//   loads in flight while waves 0-3 compute; on a paged pool under 4 GB
-//   (STG == 2) they address it with range-checked 32-bit buffer offsets.
+//   loads in flight while waves 0-3 compute.
+//
+// Paged pools under 4 GB (kPool32, paged and decode forms): K/V rows are
+// addressed with range-checked 32-bit buffer offsets over the whole pool; a
+// row past the keys or on a page outside the pool gets an offset past the
+// range and reads zeros, with no branch and no select.
 //
 // Two running sums per row: l, the fp32 sum of the weights p (for the LSE),
 // and l~, the sum of the weights as rounded to the operand dtype for the PV
@@ -138,9 +142,8 @@ struct PrefillParams {
   float* part_m;
   float* part_l;
   int chunk, max_splits, s_max;
-  // Paged decode with staging waves (STG == 2): bytes of one K (or V) pool
-  // and of one page of it, when the pool is under 4 GB, so that the staging
-  // waves address it with 32-bit buffer offsets.
+  // Paged forms with kPool32: bytes of one K (or V) pool (under 4 GB) and of
+  // one page of it.
   uint32_t pool_bytes, page_bytes;
   // Optional launch order of the sequences (longest context first), given
   // when the host knows the key counts; n_order = 0 means natural order.
@@ -148,15 +151,19 @@ struct PrefillParams {
   uint16_t order[kMaxOrder];
 };
 
-// STG: 0 = every wave computes and stages; 1 = decode with staging waves
-// (at most 4 row blocks); 2 = the same on a paged pool under 4 GB, addressed
-// with range-checked 32-bit buffer offsets.
-template <int DT, bool CAUSAL, bool KMASK, bool PAGED, bool DEC, int STG>
+// OPT flags: kStagers = decode with staging waves (at most 4 row blocks);
+// kPool32 = paged pool under 4 GB, addressed with 32-bit buffer offsets.
+constexpr int kStagers = 1;
+constexpr int kPool32 = 2;
+
+template <int DT, bool CAUSAL, bool KMASK, bool PAGED, bool DEC, int OPT>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   using E = Elem<DT>;
+  constexpr bool stagers = (OPT & kStagers) != 0;
+  constexpr bool pool32 = (OPT & kPool32) != 0;
   static_assert(!PAGED || KMASK, "paged K/V are addressed through the key-bit path");
-  static_assert(STG == 0 || DEC, "staging waves are a decode form (at most 4 row blocks)");
-  static_assert(STG != 2 || PAGED, "32-bit pool offsets are a paged form");
+  static_assert(!stagers || DEC, "staging waves are a decode form (at most 4 row blocks)");
+  static_assert(!pool32 || PAGED, "32-bit pool offsets are a paged form");
   // K of tile t lives in slot t % 2 (read in iteration t - 1), V of tile t in
   // slot t % 3 (read in iteration t + 1).
   __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kKElems];
@@ -248,8 +255,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   }
 
   const size_t kv_base = PAGED ? 0 : DEC ? ((size_t)bk * p.s_max + k_lo) * kD : (size_t)bk * T_k * kD;
-  // (STG == 2: the whole pools)
-  const uint32_t kv_range = PAGED ? (STG == 2 ? p.pool_bytes : 0u) : (uint32_t)T_k * kD * 2;
+  // (kPool32: the whole pools)
+  const uint32_t kv_range = PAGED ? (pool32 ? p.pool_bytes : 0u) : (uint32_t)T_k * kD * 2;
   const auto rk = make_rsrc(p.k + kv_base, kv_range);
   const auto rv = make_rsrc(p.v + kv_base, kv_range);
 
@@ -285,11 +292,23 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     const int key = k_lo + key_l;
     return (((long)page << p.page_shift) + (key & ((1 << p.page_shift) - 1))) * p.h_kv + kvh;
   };
+  // kPool32: byte offset of 16-byte chunk c of key key_l (counted from k_lo)
+  // on page `page`; past the pool's range (reads zeros) when the key is past
+  // T_k or the page lies outside the pool.
+  auto pool_off = [&](int key_l, int page, int c) -> uint32_t {
+    const bool valid = key_l < T_k && (uint32_t)page < (uint32_t)p.num_pages;
+    const uint32_t slot = (uint32_t)(k_lo + key_l) & ((1u << p.page_shift) - 1u);
+    const uint32_t off =
+        (uint32_t)page * p.page_bytes + (slot * (uint32_t)p.h_kv + (uint32_t)kvh) * (kD * 2u) + (uint32_t)c * 16u;
+    return valid ? off : 0xFFFFFFF0u;
+  };
   int pg_k[2] = {-1, -1}, pg_v[2] = {-1, -1}, pg_n[2] = {-1, -1};
   auto load_k = [&](int t) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      if (PAGED) {
+      if (PAGED && pool32) {
+        kreg[i] = buffer_load16(rk, pool_off(t * kBc + ((tid + kThreads * i) >> 4), pg_k[i], tid & 15));
+      } else if (PAGED) {
         const long r = paged_row(t, i, pg_k[i]);
         kreg[i] = r >= 0 ? load16(p.k + r * kD + (tid & 15) * 8) : u32x4{0u, 0u, 0u, 0u};
       } else {
@@ -300,7 +319,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   auto load_v = [&](int t) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      if (PAGED) {
+      if (PAGED && pool32) {
+        vreg[i] = buffer_load16(rv, pool_off(t * kBc + ((tid + kThreads * i) >> 4), pg_v[i], tid & 15));
+      } else if (PAGED) {
         const long r = paged_row(t, i, pg_v[i]);
         vreg[i] = r >= 0 ? load16(p.v + r * kD + (tid & 15) * 8) : u32x4{0u, 0u, 0u, 0u};
       } else {
@@ -462,10 +483,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   // V slot 2 is read (with P = 0) in the first iteration.
   for (int i = tid; i < kVElems / 8; i += kThreads) store16(&lds_v[2][i * 8], u32x4{});
   __syncthreads();
-  // STG (decode with at most 128 heads, launched only for n_rb <= 4): waves
-  // 4-7 have no rows and stage every K/V tile of the main loop; waves 0-3
-  // only compute.
-  constexpr bool stagers = STG != 0;
+  // kStagers (decode with at most 128 heads, launched only for n_rb <= 4):
+  // waves 4-7 have no rows and stage every K/V tile of the main loop; waves
+  // 0-3 only compute.
   if (stagers && wave >= 4) {
     // The pair stored in iteration j, K(j+2) and V(j+1), was loaded in
     // iteration j-2 into one of two register sets, so each CU keeps two tile
@@ -492,16 +512,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
                       int bit) -> u32x4 {
       if (!PAGED) return buffer_load16(r, ((uint32_t)(t * kBc + s_row(i)) * kD + (uint32_t)(st & 15) * 8u) * 2u);
       const int key_l = t * kBc + s_row(i);
-      if (STG == 2) {
-        // A row past the keys or on a page outside the pool gets an offset
-        // past the pool's range and reads zeros: no pool-row-0 load, no
-        // select when stored.
-        const bool valid = key_l < T_k && (uint32_t)page < (uint32_t)p.num_pages;
-        const uint32_t slot = (uint32_t)(k_lo + key_l) & ((1u << p.page_shift) - 1u);
-        const uint32_t off = (uint32_t)page * p.page_bytes + (slot * (uint32_t)p.h_kv + (uint32_t)kvh) * (kD * 2u) +
-                             (uint32_t)(st & 15) * 16u;
-        return buffer_load16(r, valid ? off : 0xFFFFFFF0u);
-      }
+      if (pool32) return buffer_load16(r, pool_off(key_l, page, st & 15));
       const bool valid = key_l < T_k && page >= 0 && page < p.num_pages;
       const long row =
           valid ? (((long)page << p.page_shift) + ((k_lo + key_l) & ((1 << p.page_shift) - 1))) * p.h_kv + kvh : 0;
@@ -531,7 +542,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
       const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool as_is = !PAGED || STG == 2;
+        const bool as_is = !PAGED || pool32;
         store16(&lds_k[j & 1][s_row(i) * kKStr + (st & 15) * 8], as_is || (ok[u] >> i & 1u) ? sk[u][i] : zero);
         store16(&lds_v[(j + 1) % 3][s_row(i) * kVStr + (st & 15) * 8],
                 as_is || (ok[u] >> (4 + i) & 1u) ? sv[u][i] : zero);
@@ -782,7 +793,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
 template <int DT, bool CAUSAL, bool KMASK, bool PAGED>
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.n_grp * p.B * p.h_kv));
-  hipLaunchKernelGGL((prefill_kernel<DT, CAUSAL, KMASK, PAGED, false, 0>), grid, dim3(kThreads), 0, stream, p);
+  if (PAGED && p.pool_bytes != 0)
+    hipLaunchKernelGGL((prefill_kernel<DT, CAUSAL, KMASK, PAGED, false, PAGED ? kPool32 : 0>), grid, dim3(kThreads), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((prefill_kernel<DT, CAUSAL, KMASK, PAGED, false, 0>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -791,15 +806,23 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
 template <int DT, bool PAGED>
 hipError_t launch_decode_rows(const PrefillParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((long)p.B * p.h_kv * p.max_splits));
-  if (p.n_rb > 4)
-    hipLaunchKernelGGL((prefill_kernel<DT, false, PAGED, PAGED, true, 0>), grid, dim3(kThreads), 0, stream, p);
-  else if constexpr (PAGED) {
-    if (p.pool_bytes != 0)
-      hipLaunchKernelGGL((prefill_kernel<DT, false, true, true, true, 2>), grid, dim3(kThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL((prefill_kernel<DT, false, true, true, true, 1>), grid, dim3(kThreads), 0, stream, p);
+  const bool stg = p.n_rb <= 4;
+  if constexpr (PAGED) {
+    if (p.pool_bytes != 0) {
+      if (stg)
+        hipLaunchKernelGGL((prefill_kernel<DT, false, true, true, true, kStagers | kPool32>), grid, dim3(kThreads), 0,
+                           stream, p);
+      else
+        hipLaunchKernelGGL((prefill_kernel<DT, false, true, true, true, kPool32>), grid, dim3(kThreads), 0, stream, p);
+    } else if (stg) {
+      hipLaunchKernelGGL((prefill_kernel<DT, false, true, true, true, kStagers>), grid, dim3(kThreads), 0, stream, p);
+    } else {
+      hipLaunchKernelGGL((prefill_kernel<DT, false, true, true, true, 0>), grid, dim3(kThreads), 0, stream, p);
+    }
+  } else if (stg) {
+    hipLaunchKernelGGL((prefill_kernel<DT, false, false, false, true, kStagers>), grid, dim3(kThreads), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((prefill_kernel<DT, false, false, false, true, 1>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((prefill_kernel<DT, false, false, false, true, 0>), grid, dim3(kThreads), 0, stream, p);
   }
   return hipGetLastError();
 }
@@ -815,6 +838,18 @@ hipError_t dispatch_prefill(const PrefillParams& p, bool causal, bool kmask, hip
 template <int DT>
 hipError_t dispatch_prefill_paged(const PrefillParams& p, bool causal, hipStream_t s) {
   return causal ? launch_prefill<DT, true, true, true>(p, s) : launch_prefill<DT, false, true, true>(p, s);
+}
+
+// kPool32 when a pool [num_pages, page_size, h_kv, d] is under 4 GB, with
+// room above it for the out-of-range offset of invalid rows; else the
+// pool_bytes = 0 left by the caller selects the 64-bit addressing.
+void set_pool32(PrefillParams& p, int num_pages, int h_kv, int page_shift) {
+  const uint64_t page_bytes = ((uint64_t)h_kv << page_shift) * kD * 2;
+  const uint64_t pool_bytes = (uint64_t)num_pages * page_bytes;
+  if (pool_bytes <= 0xFFFFFF00ull) {
+    p.pool_bytes = (uint32_t)pool_bytes;
+    p.page_bytes = (uint32_t)page_bytes;
+  }
 }
 
 PrefillParams common_params(const void* q, const void* k, const void* v, void* o, float* lse, int B, int h,
@@ -873,6 +908,7 @@ hipError_t prefill_paged(const void* q, const int32_t* cu_seqlens_q, int max_q, 
   p.max_pages = max_pages;
   p.num_pages = num_pages;
   p.page_shift = page_shift;
+  set_pool32(p, num_pages, h_kv, page_shift);
   if (B == 0 || max_q == 0 || h == 0) return hipSuccess;
   if (dtype == ATTN_DTYPE_BF16) return dispatch_prefill_paged<ATTN_DTYPE_BF16>(p, causal != 0, stream);
   return dispatch_prefill_paged<ATTN_DTYPE_F16>(p, causal != 0, stream);
@@ -900,16 +936,7 @@ hipError_t decode_split_rows(const void* q, const void* k, const void* v, const 
   p.max_splits = max_splits;
   p.s_max = s_max;
   const bool paged = block_table != nullptr;
-  if (paged) {
-    // 32-bit buffer offsets when a pool [num_pages, page_size, h_kv, d] is
-    // under 4 GB (with room for the out-of-range offset of invalid rows).
-    const uint64_t page_bytes = ((uint64_t)h_kv << page_shift) * kD * 2;
-    const uint64_t pool_bytes = (uint64_t)num_pages * page_bytes;
-    if (pool_bytes <= 0xFFFFFF00ull) {
-      p.pool_bytes = (uint32_t)pool_bytes;
-      p.page_bytes = (uint32_t)page_bytes;
-    }
-  }
+  if (paged) set_pool32(p, num_pages, h_kv, page_shift);
   if (B == 0 || h == 0) return hipSuccess;
   if (dtype == ATTN_DTYPE_BF16)
     return paged ? launch_decode_rows<ATTN_DTYPE_BF16, true>(p, stream) : launch_decode_rows<ATTN_DTYPE_BF16, false>(p, stream);

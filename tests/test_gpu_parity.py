@@ -781,35 +781,40 @@ def test_decode_head_rows_page_outside_pool():
 
 def test_decode_head_rows_pool_over_4gb():
     # pools of 2^20 + 64 pages of 16 keys (4.3 GB each, NaN-filled): past
-    # 4 GB the staging waves take their 64-bit path; half the pages sit past
-    # the 4 GB mark, one table entry is outside the pool (its rows load pool
-    # row 0, here NaN, and must be stored as zeros), the rest stay low
-    lens = [500, 77]
-    dec = make_decode(B=2, h=64, h_kv=1, d=128, dtype="bf16", seed=44, seq_lens=lens, paged=True, page_size=16)
+    # 4 GB the row form takes its 64-bit addressing (g = 64: staging waves;
+    # g = 256: every wave computes); half the pages sit past the 4 GB mark,
+    # one table entry is outside the pool (its rows must read as zeros, not
+    # as the NaN of pool row 0), the rest stay low
     n_big = (1 << 20) + 64
     assert n_big * 16 * 128 * 2 > 1 << 32
-    n_used = dec["k_pool"].shape[0]
-    new_id = np.array([n_big - 1 - p if p % 2 == 0 else p for p in range(n_used)], dtype=np.int64)
-    assert 0 not in new_id
-    k_big = torch.full((n_big, 16, 1, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
-    v_big = torch.full_like(k_big, float("nan"))
-    idx = torch.from_numpy(new_id).to(DEV)
-    k_big[idx] = to_dev(dec["k_pool"])
-    v_big[idx] = to_dev(dec["v_pool"])
-    bt = dec["block_table"].astype(np.int64)
-    bt = np.where(bt >= 0, new_id[np.maximum(bt, 0)], -1).astype(np.int32)
-    bt[0, 3] = n_big + 9                       # keys 48..63 of sequence 0
-    keep0 = np.r_[0:48, 64:500]
-    k_seqs = [dec["k_seqs"][0][:, keep0], dec["k_seqs"][1]]
-    v_seqs = [dec["v_seqs"][0][:, keep0], dec["v_seqs"][1]]
-    o_ref, lse_ref = decode_ref(dec["q"], k_seqs, v_seqs, np.array([keep0.size, 77]), dec["scale"])
-    sl = to_dev(dec["seq_lens"])
-    for plan in (None, (64, 9)):
-        o, lse, used = api.decode(to_dev(dec["q"]), k_big, v_big, sl, seq_lens_host=dec["seq_lens"],
-                                  block_table=to_dev(bt), page_size=16, scale=dec["scale"], plan=plan)
-        torch.cuda.synchronize()
-        assert_outputs(o, lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16",
-                       f"decode g=64 on 4.3 GB pools plan={used}")
+    k_big = torch.empty((n_big, 16, 1, 128), dtype=torch.bfloat16, device=DEV)
+    v_big = torch.empty_like(k_big)
+    lens = [500, 77]
+    for h in (64, 256):
+        dec = make_decode(B=2, h=h, h_kv=1, d=128, dtype="bf16", seed=44 + h, seq_lens=lens, paged=True,
+                          page_size=16)
+        n_used = dec["k_pool"].shape[0]
+        new_id = np.array([n_big - 1 - p if p % 2 == 0 else p for p in range(n_used)], dtype=np.int64)
+        assert 0 not in new_id
+        k_big.fill_(float("nan"))
+        v_big.fill_(float("nan"))
+        idx = torch.from_numpy(new_id).to(DEV)
+        k_big[idx] = to_dev(dec["k_pool"])
+        v_big[idx] = to_dev(dec["v_pool"])
+        bt = dec["block_table"].astype(np.int64)
+        bt = np.where(bt >= 0, new_id[np.maximum(bt, 0)], -1).astype(np.int32)
+        bt[0, 3] = n_big + 9                       # keys 48..63 of sequence 0
+        keep0 = np.r_[0:48, 64:500]
+        k_seqs = [dec["k_seqs"][0][:, keep0], dec["k_seqs"][1]]
+        v_seqs = [dec["v_seqs"][0][:, keep0], dec["v_seqs"][1]]
+        o_ref, lse_ref = decode_ref(dec["q"], k_seqs, v_seqs, np.array([keep0.size, 77]), dec["scale"])
+        sl = to_dev(dec["seq_lens"])
+        for plan in (None, (64, 9)):
+            o, lse, used = api.decode(to_dev(dec["q"]), k_big, v_big, sl, seq_lens_host=dec["seq_lens"],
+                                      block_table=to_dev(bt), page_size=16, scale=dec["scale"], plan=plan)
+            torch.cuda.synchronize()
+            assert_outputs(o, lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16",
+                           f"decode g={h} on 4.3 GB pools plan={used}")
     del k_big, v_big
     torch.cuda.empty_cache()
 
@@ -840,10 +845,12 @@ def test_decode_head_rows_partials_match_slices():
 
 @pytest.mark.parametrize("h,h_kv,paged,page_size", [(32, 1, False, 16), (48, 2, True, 16), (128, 1, False, 16),
                                                     (128, 1, True, 16), (17, 1, False, 16),
-                                                    (48, 2, True, 48), (17, 1, True, 80), (160, 2, True, 48)])
+                                                    (48, 2, True, 48), (17, 1, True, 80), (160, 2, True, 48),
+                                                    (256, 1, True, 32), (256, 1, False, 16)])
 def test_decode_large_groups(h, h_kv, paged, page_size):
     # g = 32, 24, 128 (MLA-style), 17: the heads as the rows of the prefill
-    # kernel; pages of 48 or 80 tokens (not a power of two): blocks of 16
+    # kernel (with staging waves up to 128 heads, every wave computing at
+    # 256); pages of 48 or 80 tokens (not a power of two): blocks of 16
     # heads, one per wave (head mode), with g = 80 spread over two workgroups
     dec = make_decode(3, h, h_kv, 128, "bf16", seed=h + h_kv, len_range=(1, 700), paged=paged, page_size=page_size)
     sl = to_dev(np.asarray(dec["seq_lens"], dtype=np.int32))
