@@ -54,8 +54,9 @@ constexpr int kMaxGroup = 256;  // decode: query heads per KV head
 // decode.hip (the heads as the 16 columns of its MFMA); larger groups use the
 // prefill kernel with the heads as rows (32 per wave), which runs one
 // workgroup per CU and is planned at one workgroup of work per CU. Measured
-// on 268-537 MB of K+V: g = 128 140-162 us against 366-429 us in blocks of
-// 16 heads; g = 32 119-128 us against 148-160; g = 24 119-121 against 143-144.
+// on 268-537 MB of K+V (split + merge, contiguous / 16-token pages): g = 128
+// 114 / 120 us against 366-429 us in blocks of 16 heads; g = 32 101 / 115 us
+// against 148-160; g = 24 100 / 119 us against 143-144.
 constexpr int kRowsMinGroup = 17;
 constexpr int kRowsWgsPerCu = 1;
 
