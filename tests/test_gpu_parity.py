@@ -671,12 +671,14 @@ def test_paged_prefill_matches_contiguous_prefill():
 
 # ------------------------------------------------------------------ batch-invariant decode
 
+@pytest.mark.parametrize("h", [8, 64])
 @pytest.mark.parametrize("paged", [False, True])
-def test_decode_batch_invariant_with_fixed_split(paged):
+def test_decode_batch_invariant_with_fixed_split(paged, h):
     # One sequence decoded alone and inside a batch whose longest sequence
     # needs >= 64 splits (the merge then runs its 4-slice layout): with the
-    # same fixed split length its output bits are identical.
-    h, h_kv, d, split = 8, 1, 128, 256
+    # same fixed split length its output bits are identical, for 8 heads per
+    # KV head (16-head blocks) and 64 (the heads as rows, staging waves).
+    h_kv, d, split = 1, 128, 256
     lens = [3000, 100, 20000, 777, 5000]
     dec = make_decode(len(lens), h, h_kv, d, "bf16", seed=31, seq_lens=lens, paged=paged, page_size=16)
     alone = make_decode(1, h, h_kv, d, "bf16", seed=32, seq_lens=[3000], paged=paged, page_size=16)
