@@ -224,8 +224,10 @@ int attn_decode_split(const void* q, const void* k, const void* v, const int32_t
     REQUIRE(s_max <= kMaxSeq, ATTN_ERR_UNSUPPORTED, "%s: s_max = %d keys (at most %d supported)", fn, s_max, kMaxSeq);
   }
   if (B == 0) return ok();
-  REQUIRE(q && k && v && seq_lens && part_o && part_m && part_l, ATTN_ERR_INVALID,
-          "%s: a required pointer is NULL", fn);
+  REQUIRE(q && seq_lens && part_o && part_m && part_l, ATTN_ERR_INVALID, "%s: a required pointer is NULL", fn);
+  // Contiguous K/V with s_max = 0 hold no key (every sequence is empty), so
+  // they may be NULL; a paged pool always holds num_pages > 0 pages.
+  REQUIRE((k && v) || (!block_table && s_max == 0), ATTN_ERR_INVALID, "%s: k and v must not be NULL", fn);
   const int shift = block_table ? log2_exact(page_size) : 0;
   if (h / h_kv >= kRowsMinGroup && shift >= 0)
     return from_hip(attn::decode_split_rows(q, k, v, block_table, max_pages, shift, num_pages, seq_lens, s_max, B, h,

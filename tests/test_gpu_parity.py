@@ -314,6 +314,20 @@ def test_decode_small(paged, page_size, dtype):
         assert_outputs(o, lse, o_ref, lse_ref, dtype, f"decode paged={paged} plan={used}")
 
 
+@pytest.mark.parametrize("h", [8, 64])
+def test_decode_no_keys_at_all(h):
+    # every sequence empty and s_max = 0: K/V are empty (NULL) tensors, the
+    # output is zeros and the LSE -inf (16-head blocks and the row form)
+    B, h_kv = 3, 1
+    q = torch.randn((B, h, 128), device=DEV).to(torch.bfloat16)
+    kv = torch.empty((B, h_kv, 0, 128), dtype=torch.bfloat16, device=DEV)
+    sl = torch.zeros(B, dtype=torch.int32, device=DEV)
+    o, lse, plan = api.decode(q, kv, kv, sl, seq_lens_host=np.zeros(B, dtype=np.int32), scale=0.088)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(o.float()) == 0
+    assert bool(torch.all(torch.isneginf(lse)))
+
+
 def test_decode_split_partials_match_slices():
     dec = make_decode(B=2, h=8, h_kv=1, d=128, dtype="bf16", seed=12, seq_lens=[700, 129], paged=False)
     chunk, S = 128, 6
