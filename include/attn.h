@@ -157,7 +157,8 @@ int attn_decode_plan(int B, const int32_t* seq_lens_host, int h, int h_kv, int d
  * addressing that follows "What the merge costs".
  *
  *   q            [B, h, d_h] dtype
- *   k, v         contiguous: [B, h_kv, s_max, d_h] (block_table == NULL);
+ *   k, v         contiguous: [B, h_kv, s_max, d_h] (block_table == NULL;
+ *                may be NULL when s_max = 0: no key exists);
  *                paged: pools [num_pages, page_size, h_kv, d_h].
  *   block_table  NULL, or [B, max_pages] int32 physical page ids: key p of
  *                sequence b is slot p % page_size of page
