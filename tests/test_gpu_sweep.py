@@ -19,7 +19,7 @@ from tests.test_gpu_parity import _run_paged_prefill, assert_outputs, run_decode
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 24
+N_CASES = 40
 
 
 @pytest.mark.parametrize("case", range(N_CASES))
