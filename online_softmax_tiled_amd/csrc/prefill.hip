@@ -505,9 +505,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
       return (int)__builtin_amdgcn_raw_buffer_load_b32(r_key, (int)((key >> p.page_shift) * 4u), 0, 0);
     };
     // Paged: a chunk whose row is past the keys or on a page outside the pool
-    // loads pool row 0 (no branch: a conditional load would make the compiler
-    // count it as possibly not issued and wait for later loads too) and is
-    // stored as zeros; bit i (K) and 4 + i (V) of ok[u] mark the valid chunks.
+    // reads zeros through an offset past the pool's range (kPool32), or, with
+    // 64-bit addressing, loads pool row 0 and is stored as zeros (bit i (K) and
+    // 4 + i (V) of ok[u] mark the valid chunks). Neither form branches: a
+    // conditional load would make the compiler count it as possibly not
+    // issued and wait for later loads too.
     auto s_load = [&](const uint16_t* pool, const decltype(rk)& r, int t, int i, int page, uint32_t& ok,
                       int bit) -> u32x4 {
       if (!PAGED) return buffer_load16(r, ((uint32_t)(t * kBc + s_row(i)) * kD + (uint32_t)(st & 15) * 8u) * 2u);
