@@ -504,6 +504,26 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
       const uint32_t key = (uint32_t)(k_lo + t * kBc + s_row(i));
       return (int)__builtin_amdgcn_raw_buffer_load_b32(r_key, (int)((key >> p.page_shift) * 4u), 0, 0);
     };
+    // kPool32: staging group i of a tile (rows 16 i .. 16 i + 15 of it, from a
+    // 16-aligned key) lies on one page, so its page id and its byte offset in
+    // the pool are the same for every staging lane. The page ids are read
+    // with scalar loads (the block table does not change during the kernel),
+    // one step before use, and the group's offset is added to a per-lane
+    // constant; a group past the keys or on a page outside the pool gets the
+    // pool's size, past the range, which reads zeros.
+    const __attribute__((address_space(4))) int32_t* bt_row =
+        (const __attribute__((address_space(4))) int32_t*)(PAGED ? p.bt + (size_t)b * p.max_pages : p.bt);
+    const uint32_t lane_off =
+        ((uint32_t)(st >> 4) * (uint32_t)p.h_kv + (uint32_t)kvh) * (kD * 2u) + (uint32_t)(st & 15) * 16u;
+    auto grp_page = [&](int t, int i) -> int {   // first key of the group: t * kBc + 16 i from k_lo
+      return bt_row[min((k_lo + t * kBc + 16 * i) >> p.page_shift, p.max_pages - 1)];
+    };
+    auto grp_off = [&](int t, int i, int page) -> uint32_t {
+      const int g = t * kBc + 16 * i;
+      const bool ok = g < T_k && (uint32_t)page < (uint32_t)p.num_pages;
+      const uint32_t slot0 = (uint32_t)(k_lo + g) & ((1u << p.page_shift) - 1u);
+      return ok ? (uint32_t)page * p.page_bytes + slot0 * (uint32_t)p.h_kv * (kD * 2u) : p.pool_bytes;
+    };
     // Paged: a chunk whose row is past the keys or on a page outside the pool
     // reads zeros through an offset past the pool's range (kPool32), or, with
     // 64-bit addressing, loads pool row 0 and is stored as zeros (bit i (K) and
@@ -514,7 +534,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
                       int bit) -> u32x4 {
       if (!PAGED) return buffer_load16(r, ((uint32_t)(t * kBc + s_row(i)) * kD + (uint32_t)(st & 15) * 8u) * 2u);
       const int key_l = t * kBc + s_row(i);
-      if (pool32) return buffer_load16(r, pool_off(key_l, page, st & 15));
+      if (pool32) return buffer_load16(r, key_l < T_k ? grp_off(t, i, page) + lane_off : 0xFFFFFFF0u);
       const bool valid = key_l < T_k && page >= 0 && page < p.num_pages;
       const long row =
           valid ? (((long)page << p.page_shift) + ((k_lo + key_l) & ((1 << p.page_shift) - 1))) * p.h_kv + kvh : 0;
@@ -528,8 +548,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
       if (!PAGED) return;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pgk[u][i] = s_page(tk, i);
-        pgv[u][i] = s_page(tv, i);
+        pgk[u][i] = pool32 ? grp_page(tk, i) : s_page(tk, i);
+        pgv[u][i] = pool32 ? grp_page(tv, i) : s_page(tv, i);
       }
     };
     auto issue = [&](int u, int tk, int tv, int pu) {
@@ -564,9 +584,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     issue(1, 3, 2, 1);
     auto step = [&](int j, int u) {
       put(j, u);
-      lookup(u ^ 1, j + 5, j + 4);
-      __builtin_amdgcn_sched_barrier(0);
-      issue(u, j + 4, j + 3, u);
+      if (pool32) {
+        // scalar lookups after the tile loads: the wait for them, before the
+        // next step's loads, then also covers only loads already done
+        issue(u, j + 4, j + 3, u);
+        lookup(u ^ 1, j + 5, j + 4);
+      } else {
+        lookup(u ^ 1, j + 5, j + 4);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(u, j + 4, j + 3, u);
+      }
       __syncthreads();
     };
     // One barrier per iteration j = 0 .. n_tiles, as in the main loop.
@@ -843,12 +870,13 @@ hipError_t dispatch_prefill_paged(const PrefillParams& p, bool causal, hipStream
 }
 
 // kPool32 when a pool [num_pages, page_size, h_kv, d] is under 4 GB, with
-// room above it for the out-of-range offset of invalid rows; else the
-// pool_bytes = 0 left by the caller selects the 64-bit addressing.
+// room above it for the out-of-range offsets of invalid rows (the pool's size
+// plus an in-page offset must not wrap); else the pool_bytes = 0 left by the
+// caller selects the 64-bit addressing.
 void set_pool32(PrefillParams& p, int num_pages, int h_kv, int page_shift) {
   const uint64_t page_bytes = ((uint64_t)h_kv << page_shift) * kD * 2;
   const uint64_t pool_bytes = (uint64_t)num_pages * page_bytes;
-  if (pool_bytes <= 0xFFFFFF00ull) {
+  if (pool_bytes + page_bytes <= 0xFFFFFF00ull) {
     p.pool_bytes = (uint32_t)pool_bytes;
     p.page_bytes = (uint32_t)page_bytes;
   }
