@@ -282,7 +282,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   // Page ids are fetched one iteration before the K tile that needs them and
   // reused for the V tile one iteration later, so no tile load waits on a
   // block-table load.
+  // kPool32: the rows a wave stages from a tile come in groups that lie on
+  // one page (4 rows from a 4-aligned key for the compute waves, 16 from a
+  // 16-aligned one for the staging waves; pages hold at least 16 keys and
+  // ranges start 16-aligned), so those page ids are read with scalar loads
+  // (the block table does not change during the kernel).
+  const __attribute__((address_space(4))) int32_t* bt_row =
+      (const __attribute__((address_space(4))) int32_t*)(PAGED ? p.bt + (size_t)b * p.max_pages : p.bt);
   auto page_of = [&](int t, int i) -> int {
+    if (pool32)   // rows 4 wave + 32 i + 0..3 of tile t
+      return bt_row[min((k_lo + t * kBc + 4 * wave + 32 * i) >> p.page_shift, p.max_pages - 1)];
     const uint32_t key = (uint32_t)(k_lo + t * kBc + ((tid + kThreads * i) >> 4));
     return (int)__builtin_amdgcn_raw_buffer_load_b32(r_key, (int)((key >> p.page_shift) * 4u), 0, 0);
   };
@@ -292,22 +301,25 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     const int key = k_lo + key_l;
     return (((long)page << p.page_shift) + (key & ((1 << p.page_shift) - 1))) * p.h_kv + kvh;
   };
-  // kPool32: byte offset of 16-byte chunk c of key key_l (counted from k_lo)
-  // on page `page`; past the pool's range (reads zeros) when the key is past
-  // T_k or the page lies outside the pool.
-  auto pool_off = [&](int key_l, int page, int c) -> uint32_t {
-    const bool valid = key_l < T_k && (uint32_t)page < (uint32_t)p.num_pages;
-    const uint32_t slot = (uint32_t)(k_lo + key_l) & ((1u << p.page_shift) - 1u);
-    const uint32_t off =
-        (uint32_t)page * p.page_bytes + (slot * (uint32_t)p.h_kv + (uint32_t)kvh) * (kD * 2u) + (uint32_t)c * 16u;
-    return valid ? off : 0xFFFFFFF0u;
+  // kPool32: byte offset of this lane's chunk of staging row i of tile t on
+  // page `page` (the wave's group offset, uniform, plus a per-lane constant);
+  // past the pool's range (reads zeros) when the row is past T_k or the page
+  // lies outside the pool.
+  const uint32_t main_lane_off =
+      ((uint32_t)(lane >> 4) * (uint32_t)p.h_kv + (uint32_t)kvh) * (kD * 2u) + (uint32_t)(tid & 15) * 16u;
+  auto pool_off = [&](int t, int i, int page) -> uint32_t {
+    const int g = t * kBc + 4 * wave + 32 * i;   // first key of the wave's 4 rows, counted from k_lo
+    const bool ok = (uint32_t)page < (uint32_t)p.num_pages;
+    const uint32_t slot0 = (uint32_t)(k_lo + g) & ((1u << p.page_shift) - 1u);
+    const uint32_t go = ok ? (uint32_t)page * p.page_bytes + slot0 * (uint32_t)p.h_kv * (kD * 2u) : p.pool_bytes;
+    return g + (lane >> 4) < T_k ? go + main_lane_off : 0xFFFFFFF0u;
   };
   int pg_k[2] = {-1, -1}, pg_v[2] = {-1, -1}, pg_n[2] = {-1, -1};
   auto load_k = [&](int t) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       if (PAGED && pool32) {
-        kreg[i] = buffer_load16(rk, pool_off(t * kBc + ((tid + kThreads * i) >> 4), pg_k[i], tid & 15));
+        kreg[i] = buffer_load16(rk, pool_off(t, i, pg_k[i]));
       } else if (PAGED) {
         const long r = paged_row(t, i, pg_k[i]);
         kreg[i] = r >= 0 ? load16(p.k + r * kD + (tid & 15) * 8) : u32x4{0u, 0u, 0u, 0u};
@@ -320,7 +332,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       if (PAGED && pool32) {
-        vreg[i] = buffer_load16(rv, pool_off(t * kBc + ((tid + kThreads * i) >> 4), pg_v[i], tid & 15));
+        vreg[i] = buffer_load16(rv, pool_off(t, i, pg_v[i]));
       } else if (PAGED) {
         const long r = paged_row(t, i, pg_v[i]);
         vreg[i] = r >= 0 ? load16(p.v + r * kD + (tid & 15) * 8) : u32x4{0u, 0u, 0u, 0u};
@@ -507,12 +519,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     // kPool32: staging group i of a tile (rows 16 i .. 16 i + 15 of it, from a
     // 16-aligned key) lies on one page, so its page id and its byte offset in
     // the pool are the same for every staging lane. The page ids are read
-    // with scalar loads (the block table does not change during the kernel),
-    // one step before use, and the group's offset is added to a per-lane
+    // with scalar loads one step before use, and the group's offset is added
+    // to a per-lane
     // constant; a group past the keys or on a page outside the pool gets the
     // pool's size, past the range, which reads zeros.
-    const __attribute__((address_space(4))) int32_t* bt_row =
-        (const __attribute__((address_space(4))) int32_t*)(PAGED ? p.bt + (size_t)b * p.max_pages : p.bt);
     const uint32_t lane_off =
         ((uint32_t)(st >> 4) * (uint32_t)p.h_kv + (uint32_t)kvh) * (kD * 2u) + (uint32_t)(st & 15) * 16u;
     auto grp_page = [&](int t, int i) -> int {   // first key of the group: t * kBc + 16 i from k_lo
