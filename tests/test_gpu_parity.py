@@ -606,13 +606,22 @@ def _run_paged_prefill(c, causal, rows_per_seq=None, host_order=False):
         assert_outputs(ob, lb, o_ref, lse_ref, c["dtype"], f"paged prefill seq {b} ({tq} new / {tk} keys)")
 
 
-def test_paged_prefill_pool_over_4gb():
-    # the chunked-prefill kernel on pools of 2^19 + 64 pages of 16 keys x 2
-    # KV heads (4.3 GB each, NaN-filled), half the used pages past 4 GB
+# pools just under the largest addressed with 32-bit offsets (pool + one page
+# <= 2^32 - 256 bytes) and just over 4 GB (64-bit addressing)
+_UNDER_4GB = lambda page_bytes: 0xFFFFFF00 // page_bytes - 1
+_OVER_4GB = lambda page_bytes: (1 << 32) // page_bytes + 64
+
+
+@pytest.mark.parametrize("size", ["under_4gb", "over_4gb"])
+def test_paged_prefill_large_pools(size):
+    # the chunked-prefill kernel on pools of 16-key pages x 2 KV heads at the
+    # edges of the 32-bit addressing (NaN-filled), half the used pages at the
+    # top of the pool
     from online_softmax_tiled_amd.workloads import make_chunked_prefill
     c = make_chunked_prefill(3, 8, 2, 128, "bf16", seed=77, ctx_range=(100, 400), new_range=(10, 90), page_size=16)
-    n_big = (1 << 19) + 64
-    assert n_big * 16 * 2 * 128 * 2 > 1 << 32
+    page_bytes = 16 * 2 * 128 * 2
+    n_big = (_UNDER_4GB if size == "under_4gb" else _OVER_4GB)(page_bytes)
+    assert (n_big * page_bytes + page_bytes <= 0xFFFFFF00) == (size == "under_4gb")
     n_used = c["k_pool"].shape[0]
     new_id = np.array([n_big - 1 - p if p % 2 == 0 else p for p in range(n_used)], dtype=np.int64)
     k_big = torch.full((n_big, 16, 2, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
@@ -795,14 +804,17 @@ def test_decode_head_rows_page_outside_pool():
                        f"decode g=128 pages outside the pool plan={used}")
 
 
-def test_decode_head_rows_pool_over_4gb():
-    # pools of 2^20 + 64 pages of 16 keys (4.3 GB each, NaN-filled): past
-    # 4 GB the row form takes its 64-bit addressing (g = 64: staging waves;
-    # g = 256: every wave computes); half the pages sit past the 4 GB mark,
-    # one table entry is outside the pool (its rows must read as zeros, not
-    # as the NaN of pool row 0), the rest stay low
-    n_big = (1 << 20) + 64
-    assert n_big * 16 * 128 * 2 > 1 << 32
+@pytest.mark.parametrize("size", ["under_4gb", "over_4gb"])
+def test_decode_head_rows_large_pools(size):
+    # pools of 16-key pages (NaN-filled) just under the largest addressed
+    # with 32-bit offsets and just over 4 GB (64-bit addressing), for the row
+    # form with staging waves (g = 64) and with every wave computing (g = 256);
+    # half the pages sit at the top of the pool, one table entry is outside
+    # the pool (its rows must read as zeros, not as the NaN of pool row 0),
+    # the rest stay low
+    page_bytes = 16 * 128 * 2
+    n_big = (_UNDER_4GB if size == "under_4gb" else _OVER_4GB)(page_bytes)
+    assert (n_big * page_bytes + page_bytes <= 0xFFFFFF00) == (size == "under_4gb")
     k_big = torch.empty((n_big, 16, 1, 128), dtype=torch.bfloat16, device=DEV)
     v_big = torch.empty_like(k_big)
     lens = [500, 77]
@@ -830,7 +842,7 @@ def test_decode_head_rows_pool_over_4gb():
                                       block_table=to_dev(bt), page_size=16, scale=dec["scale"], plan=plan)
             torch.cuda.synchronize()
             assert_outputs(o, lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16",
-                           f"decode g={h} on 4.3 GB pools plan={used}")
+                           f"decode g={h} on {size} pools of {n_big} pages plan={used}")
     del k_big, v_big
     torch.cuda.empty_cache()
 
