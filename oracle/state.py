@@ -23,46 +23,65 @@ import numpy as np
 EMPTY_M = -np.inf
 
 
+def _empty(d):
+    """The state of no keys: reference -inf, mass 0, numerator 0."""
+    return EMPTY_M, 0.0, np.zeros(d)
+
+
 def state_ref(scores, values):
     """Partial state (m, l, a) of one block of keys.
 
     scores: [n] logits of the block (-inf marks an excluded key); values:
-    [n, d]. A block with no keys, or with every key excluded, is the empty
-    state (-inf, 0, zeros) -- returned by an explicit branch so that
-    -inf - (-inf) is never formed ("The Online Softmax Recurrence", section
-    "Worked example", the state function's empty-block branch, and section
-    "Where it breaks").
+    [n, d]. The reference m is the largest visible logit, and every weight
+    exp(x - m) lies in (0, 1] ("The Online Softmax Recurrence", section "The
+    recurrence"). With no visible key the reference would be -inf and
+    x - m would read -inf - (-inf), so that case is decided before any
+    subtraction and gives the empty state ("The Online Softmax Recurrence",
+    section "Where it breaks"; "Merge normalized attention without averaging
+    tile outputs", paragraph on fully masked tiles).
     """
-    scores = np.asarray(scores, dtype=np.float64)
-    values = np.asarray(values, dtype=np.float64)
-    d = values.shape[-1]
-    if scores.size == 0 or np.all(np.isneginf(scores)):
-        return EMPTY_M, 0.0, np.zeros(d)
-    m = float(scores.max())
-    p = np.exp(scores - m)
-    return m, float(p.sum()), p @ values
+    logits = np.asarray(scores, dtype=np.float64)
+    rows = np.asarray(values, dtype=np.float64)
+    visible = ~np.isneginf(logits)
+    if not visible.any():
+        return _empty(rows.shape[-1])
+    ref = float(logits[visible].max())
+    weights = np.exp(logits - ref)          # excluded keys: exp(-inf) = 0
+    return ref, float(weights.sum()), weights @ rows
+
+
+def _combine(states):
+    """Fold any number of states of disjoint key sets into one.
+
+    The combined reference is the largest of the inputs' references; input
+    i enters with the factor exp(m_i - m), which is in [0, 1], applied to
+    its mass and its numerator ("Merge normalized attention without
+    averaging tile outputs", paragraph on disjoint nonempty tiles; "The
+    Online Softmax Recurrence", section "The recurrence"). Inputs whose
+    reference is -inf (empty) get the factor 0 without forming
+    -inf - (-inf); if every input is empty the result is the empty state
+    ("Merge normalized attention without averaging tile outputs", paragraph
+    on fully masked tiles).
+    """
+    refs = np.array([float(s[0]) for s in states])
+    width = np.asarray(states[0][2], dtype=np.float64).shape[-1]
+    live = ~np.isneginf(refs)
+    if not live.any():
+        return _empty(width)
+    top = float(refs[live].max())
+    factor = [math.exp(r - top) if ok else 0.0 for r, ok in zip(refs, live)]
+    mass = 0.0
+    numer = np.zeros(width)
+    for f, (_, l_i, a_i) in zip(factor, states):
+        mass = mass + l_i * f
+        numer = numer + np.asarray(a_i, dtype=np.float64) * f
+    return top, mass, numer
 
 
 def merge_ref(a, b):
-    """Merge two states of disjoint key sets.
-
-    The new reference is the larger maximum; each side's mass and numerator
-    are multiplied by exp(old max - new max), a factor in [0, 1], then added
-    ("Merge normalized attention without averaging tile outputs", paragraph
-    on disjoint nonempty tiles; "The Online Softmax Recurrence", section
-    "The recurrence", the general two-state form). If both sides are empty
-    the result is the empty state, by an explicit branch
-    ("Merge normalized attention without averaging tile outputs", paragraph
-    on fully masked tiles). An empty side has m = -inf and contributes
-    exp(-inf) = 0 against a finite maximum.
-    """
-    (ma, la, xa), (mb, lb, xb) = a, b
-    m = max(ma, mb)
-    if np.isneginf(m):
-        return EMPTY_M, 0.0, np.zeros_like(np.asarray(xa, dtype=np.float64))
-    sa = math.exp(ma - m) if not np.isneginf(ma) else 0.0
-    sb = math.exp(mb - m) if not np.isneginf(mb) else 0.0
-    return m, la * sa + lb * sb, np.asarray(xa) * sa + np.asarray(xb) * sb
+    """Merge two states of disjoint key sets (the two-input case of the
+    fold above); the result does not depend on the order of a and b."""
+    return _combine([a, b])
 
 
 def finalize_ref(state):
@@ -82,32 +101,34 @@ def online_ref(scores, values, block):
     """One left-to-right pass over the row in blocks of ``block`` keys.
 
     The streaming recurrence of "Naive attention and the online softmax",
-    section (3) "The online recurrence", extended to the output in section
-    "Extending the recurrence to the output": with the running state
-    (m, l, O~) starting at (-inf, 0, 0), each block B raises the maximum to
-    m' = max(m, max B), forms alpha = exp(m - m'), and sets
-    l <- alpha l + sum_B exp(x - m'), O~ <- alpha O~ + sum_B exp(x - m') v.
-    alpha is taken as 0 while the old maximum is still -inf (the base-case
-    guard of that page's numerical check), and a block that leaves the
-    maximum at -inf (nothing visible yet) leaves the state unchanged.
+    section (3) "The online recurrence", carried to the output in section
+    "Extending the recurrence to the output": the running reference after a
+    block is the largest logit seen so far; when it rises from r to r', the
+    mass and the output accumulator collected so far are multiplied by
+    exp(r - r') before the block's weights exp(x - r') are added. Before
+    any visible key the state is empty (reference -inf): a block that leaves
+    it there adds nothing, and the first block that does not gets the decay
+    0 in place of exp(-inf - r').
 
     Returns the final state (m, l, O~); divide once at the end with
     :func:`finalize_ref`.
     """
-    scores = np.asarray(scores, dtype=np.float64)
-    values = np.asarray(values, dtype=np.float64)
-    m, l, o = EMPTY_M, 0.0, np.zeros(values.shape[-1])
-    for j in range(0, scores.size, block):
-        xb, vb = scores[j:j + block], values[j:j + block]
-        m_new = max(m, float(xb.max())) if xb.size else m
-        if np.isneginf(m_new):
-            continue                              # still empty: no -inf - -inf
-        alpha = math.exp(m - m_new) if not np.isneginf(m) else 0.0
-        p = np.exp(xb - m_new)
-        l = alpha * l + float(p.sum())
-        o = alpha * o + p @ vb
-        m = m_new
-    return m, l, o
+    logits = np.asarray(scores, dtype=np.float64)
+    rows = np.asarray(values, dtype=np.float64)
+    starts = range(0, logits.size, block)
+    # running reference after each block: a prefix maximum of block maxima
+    refs = np.maximum.accumulate([float(logits[s:s + block].max()) for s in starts]) if logits.size else []
+    ref, mass, acc = EMPTY_M, 0.0, np.zeros(rows.shape[-1])
+    for s, r_new in zip(starts, refs):
+        r_new = float(r_new)
+        if np.isneginf(r_new):
+            continue
+        decay = 0.0 if np.isneginf(ref) else math.exp(ref - r_new)
+        w = np.exp(logits[s:s + block] - r_new)
+        mass = decay * mass + float(w.sum())
+        acc = decay * acc + w @ rows[s:s + block]
+        ref = r_new
+    return ref, mass, acc
 
 
 def split_states_ref(q, k, v, seq_len, scale, chunk):

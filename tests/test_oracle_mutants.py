@@ -21,34 +21,33 @@ import tests.test_oracle as pins
 from tests.conftest import load_golden
 
 
-def online_m0(scores, values, block):
-    # mistake: the running maximum starts at 0 instead of -inf
-    scores = np.asarray(scores, dtype=np.float64)
-    m, l, o = 0.0, 0.0, np.zeros(values.shape[-1])
-    for j in range(0, scores.size, block):
-        xb, vb = scores[j:j + block], values[j:j + block]
-        m_new = max(m, float(xb.max()))
-        alpha = math.exp(m - m_new)
-        p = np.exp(xb - m_new)
-        l = alpha * l + float(p.sum())
-        o = alpha * o + p @ vb
-        m = m_new
-    return m, l, o
+def _online_variant(start_ref, rescale_acc):
+    """A copy of oracle.state.online_ref with one step changed: the running
+    reference starts at ``start_ref``, and the output accumulator is
+    multiplied by the decay only if ``rescale_acc``."""
+    def online(scores, values, block):
+        logits = np.asarray(scores, dtype=np.float64)
+        rows = np.asarray(values, dtype=np.float64)
+        starts = range(0, logits.size, block)
+        refs = np.maximum.accumulate([max(start_ref, float(logits[s:s + block].max())) for s in starts])
+        ref, mass, acc = start_ref, 0.0, np.zeros(rows.shape[-1])
+        for s, r_new in zip(starts, refs):
+            r_new = float(r_new)
+            if np.isneginf(r_new):
+                continue
+            decay = 0.0 if np.isneginf(ref) else math.exp(ref - r_new)
+            w = np.exp(logits[s:s + block] - r_new)
+            mass = decay * mass + float(w.sum())
+            acc = (decay if rescale_acc else 1.0) * acc + w @ rows[s:s + block]
+            ref = r_new
+        return ref, mass, acc
+    return online
 
 
-def online_no_rescale(scores, values, block):
-    # mistake: l is rescaled but the output accumulator is not
-    scores = np.asarray(scores, dtype=np.float64)
-    m, l, o = -np.inf, 0.0, np.zeros(values.shape[-1])
-    for j in range(0, scores.size, block):
-        xb, vb = scores[j:j + block], values[j:j + block]
-        m_new = max(m, float(xb.max()))
-        alpha = math.exp(m - m_new) if np.isfinite(m) else 0.0
-        p = np.exp(xb - m_new)
-        l = alpha * l + float(p.sum())
-        o = o + p @ vb
-        m = m_new
-    return m, l, o
+# mistake: the running maximum starts at 0 instead of -inf
+online_m0 = _online_variant(0.0, True)
+# mistake: l is rescaled but the output accumulator is not
+online_no_rescale = _online_variant(-np.inf, False)
 
 
 def _attention_variant(gqa=None, scale_mode="before", causal_mode="bottom_right", log=np.log, use_key_mask=True):
@@ -86,20 +85,31 @@ def _attention_variant(gqa=None, scale_mode="before", causal_mode="bottom_right"
     return att
 
 
-def merge_no_empty_branch(a, b):
-    (ma, la, xa), (mb, lb, xb) = a, b
-    m = max(ma, mb)
-    with np.errstate(invalid="ignore"):
-        sa, sb = np.exp(ma - m), np.exp(mb - m)
-    return m, la * sa + lb * sb, np.asarray(xa) * sa + np.asarray(xb) * sb
+def _merge_variant(guard_empty, rescale):
+    """A copy of the oracle's state fold (oracle.state._combine) for two
+    states with one step changed: without the empty-state guard the factors
+    are exp(m_i - max) even when every reference is -inf; without the
+    rescale every factor is 1."""
+    def merge(a, b):
+        states = [a, b]
+        refs = np.array([float(s[0]) for s in states])
+        width = np.asarray(states[0][2], dtype=np.float64).shape[-1]
+        live = ~np.isneginf(refs) if guard_empty else np.ones(2, dtype=bool)
+        if not live.any():
+            return ost.EMPTY_M, 0.0, np.zeros(width)
+        top = float(refs[live].max())
+        with np.errstate(invalid="ignore"):
+            factor = [float(np.exp(r - top)) if rescale else 1.0 for r in refs]
+        mass, numer = 0.0, np.zeros(width)
+        for f, (_, l_i, a_i) in zip(factor, states):
+            mass = mass + l_i * f
+            numer = numer + np.asarray(a_i, dtype=np.float64) * f
+        return top, mass, numer
+    return merge
 
 
-def merge_no_rescale(a, b):
-    (ma, la, xa), (mb, lb, xb) = a, b
-    m = max(ma, mb)
-    if np.isneginf(m):
-        return ost.EMPTY_M, 0.0, np.zeros_like(np.asarray(xa, dtype=np.float64))
-    return m, la + lb, np.asarray(xa) + np.asarray(xb)
+merge_no_empty_branch = _merge_variant(False, True)
+merge_no_rescale = _merge_variant(True, False)
 
 
 def gather_swapped(pool, block_table, seq_lens, s_max, out=None):
@@ -190,8 +200,7 @@ CASES = [
 
 
 @pytest.mark.parametrize("name,mutant,pin,args", CASES,
-                         ids=[f"{c[0]}-{c[1].__name__ if hasattr(c[1], '__name__') else i}-{c[2].__name__}"
-                              for i, c in enumerate(CASES)])
+                         ids=[f"{c[0]}-{i}-{c[2].__name__}" for i, c in enumerate(CASES)])
 def test_pin_catches_mutant(monkeypatch, name, mutant, pin, args):
     # the unmodified oracle passes the pin ...
     pin(*args)
