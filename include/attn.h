@@ -136,16 +136,35 @@ int attn_prefill_paged(const void* q, const int32_t* cu_seqlens_q, int max_q,
  * units = h_kv * sum_b n_b is at least num_cus whenever the keys allow it.
  *
  * The plan depends on the whole batch, so a sequence's output bits may change
- * with its companions. For batch-invariant results ([DA] section "Split-K
- * breaks bitwise reproducibility": fix the split tile so the split count is a
- * function of the sequence length alone) skip this plan and pass a fixed
- * chunk_keys (a multiple of 16, e.g. 2048) with max_splits = ceil(max_b
- * seq_lens[b] / chunk_keys) to attn_decode_split and attn_merge_states: a
- * row's splits and the merge's summation order then depend only on its own
- * length.
+ * with its companions; attn_decode_plan_fixed gives batch-invariant plans.
  */
 int attn_decode_plan(int B, const int32_t* seq_lens_host, int h, int h_kv, int d_h,
                      int num_cus, int32_t* chunk_keys, int32_t* max_splits);
+
+/*
+ * Batch-invariant decode plan (host only, pure): a split length fixed by the
+ * caller instead of derived from the batch. [DA] section "Split-K breaks
+ * bitwise reproducibility" (fix the split tile, so that the split count of a
+ * sequence is a function of its own length alone) and section "CUDA graphs
+ * need the split count pinned" (a grid sized once for the longest sequence,
+ * the active splits decided on the device).
+ *
+ *   seq_lens_host [B] host int32, the KV length of each sequence (>= 0).
+ *   split_keys    keys per split, a positive multiple of 16 (e.g. 2048).
+ *   chunk_keys    (out) = split_keys.
+ *   max_splits    (out) = max(1, ceil(max_b seq_lens[b] / split_keys)), the
+ *                 split dimension of the partial buffers and of the grid.
+ * With this plan, split i of sequence b covers keys [i*split_keys,
+ * (i+1)*split_keys) and the merge sums a row's splits in an order that
+ * depends only on its own split count, so each sequence's output and LSE
+ * bits are the same whatever other sequences share the call. A plan whose
+ * max_splits would exceed 65535 (what attn_decode_split accepts) returns
+ * ATTN_ERR_UNSUPPORTED; a split_keys that is not a positive multiple of 16
+ * or a negative length returns ATTN_ERR_INVALID. Outputs are written only
+ * on success.
+ */
+int attn_decode_plan_fixed(int B, const int32_t* seq_lens_host, int split_keys,
+                           int32_t* chunk_keys, int32_t* max_splits);
 
 /*
  * Decode stage 1 (split-KV, FlashDecoding): one query token per sequence;

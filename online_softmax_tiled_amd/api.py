@@ -27,6 +27,7 @@ _SIGNATURES = {
     "attn_prefill_paged": [_c_void_p, _c_void_p, _c_int] + [_c_void_p] * 5 + [_c_int] * 8 + [_c_float, _c_int]
                           + [_c_void_p] * 3,
     "attn_decode_plan": [_c_int, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_void_p],
+    "attn_decode_plan_fixed": [_c_int, _c_void_p, _c_int, _c_void_p, _c_void_p],
     "attn_decode_split": [_c_void_p] * 4 + [_c_int] * 3 + [_c_void_p] + [_c_int] * 8 + [_c_float]
                          + [_c_void_p] * 4,
     "attn_merge_states": [_c_void_p] * 4 + [_c_int] * 5 + [_c_void_p, _c_void_p, _c_int, _c_void_p],
@@ -191,16 +192,17 @@ def decode_plan(seq_lens, h, h_kv, num_cus=None, d=HEAD_DIM, device=None):
 
 
 def decode_plan_fixed(seq_lens, split_keys=2048):
-    """(chunk_keys, max_splits) for a split length that does not depend on the
-    batch: each sequence's output bits then depend only on its own query,
-    keys and ``split_keys`` (batch-invariant decode). ``split_keys`` must be a
-    positive multiple of 16."""
-    lens = np.asarray(seq_lens, dtype=np.int64)
-    split_keys = int(split_keys)
-    if split_keys <= 0 or split_keys % 16:
-        raise ValueError(f"split_keys must be a positive multiple of 16 (got {split_keys})")
-    s_max = int(lens.max()) if lens.size else 0
-    return split_keys, max(1, -(-s_max // split_keys))
+    """(chunk_keys, max_splits) from attn_decode_plan_fixed: a split length
+    that does not depend on the batch, so each sequence's output bits depend
+    only on its own query, keys and ``split_keys`` (batch-invariant decode).
+    seq_lens: host ints; ``split_keys`` a positive multiple of 16."""
+    lib = load()
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    chunk, splits = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check("attn_decode_plan_fixed", lib.attn_decode_plan_fixed(
+        int(lens.size), lens.ctypes.data_as(ctypes.c_void_p), int(split_keys),
+        ctypes.byref(chunk), ctypes.byref(splits)))
+    return chunk.value, splits.value
 
 
 def decode_split(q, k, v, seq_lens, chunk_keys, max_splits, block_table=None, page_size=16,

@@ -196,6 +196,29 @@ int attn_decode_plan(int B, const int32_t* seq_lens_host, int h, int h_kv, int d
   return ok();
 }
 
+int attn_decode_plan_fixed(int B, const int32_t* seq_lens_host, int split_keys, int32_t* chunk_keys,
+                           int32_t* max_splits) {
+  const char* fn = "attn_decode_plan_fixed";
+  REQUIRE(B >= 0, ATTN_ERR_INVALID, "%s: negative batch %d", fn, B);
+  REQUIRE(split_keys > 0 && split_keys % 16 == 0, ATTN_ERR_INVALID,
+          "%s: split_keys must be a positive multiple of 16 (got %d)", fn, split_keys);
+  REQUIRE(chunk_keys && max_splits, ATTN_ERR_INVALID, "%s: output pointers must not be NULL", fn);
+  REQUIRE(B == 0 || seq_lens_host, ATTN_ERR_INVALID, "%s: seq_lens_host must not be NULL", fn);
+  int s_max = 0;
+  for (int b = 0; b < B; ++b) {
+    REQUIRE(seq_lens_host[b] >= 0, ATTN_ERR_INVALID, "%s: seq_lens[%d] = %d is negative", fn, b, seq_lens_host[b]);
+    s_max = seq_lens_host[b] > s_max ? seq_lens_host[b] : s_max;
+  }
+  // A sequence's split count depends on its own length only: the splits are
+  // [i * split_keys, (i + 1) * split_keys), and the grid covers the longest.
+  const long splits = s_max == 0 ? 1 : ((long)s_max + split_keys - 1) / split_keys;
+  REQUIRE(splits <= 65535, ATTN_ERR_UNSUPPORTED, "%s: %ld splits of %d keys (at most 65535 supported)", fn, splits,
+          split_keys);
+  *chunk_keys = split_keys;
+  *max_splits = (int32_t)splits;
+  return ok();
+}
+
 int attn_decode_split(const void* q, const void* k, const void* v, const int32_t* block_table, int max_pages,
                       int page_size, int num_pages, const int32_t* seq_lens, int s_max, int B, int h, int h_kv,
                       int d_h, int chunk_keys, int max_splits, int dtype, float scale, float* part_o,

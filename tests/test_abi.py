@@ -266,10 +266,45 @@ def test_paged_prefill_empty_is_ok_without_launch(lib):
     assert paged_prefill_call(lib, max_q=0, q=None, o=None) == 0
 
 
-def test_fixed_decode_plan_is_batch_independent():
+def test_fixed_decode_plan_is_batch_independent(lib):
+    # attn_decode_plan_fixed through the C ABI: the split length is the
+    # caller's, a sequence's split count depends on its own length only, and
+    # the grid covers the longest sequence
+    import ctypes
     from online_softmax_tiled_amd import api
-    assert api.decode_plan_fixed([3000], 256) == (256, 12)
+
+    def fixed(lens, split):
+        arr = np.ascontiguousarray(np.asarray(lens, dtype=np.int32))
+        chunk, splits = ctypes.c_int32(-5), ctypes.c_int32(-5)
+        rc = lib.attn_decode_plan_fixed(int(arr.size), arr.ctypes.data_as(ctypes.c_void_p) if arr.size else None,
+                                        split, ctypes.byref(chunk), ctypes.byref(splits))
+        return rc, chunk.value, splits.value
+
+    assert fixed([3000], 256) == (0, 256, 12)
+    assert fixed([3000, 20000, 5], 256) == (0, 256, 79)
+    assert fixed([], 2048) == (0, 2048, 1)
+    assert fixed([0, 0], 2048) == (0, 2048, 1)
+    assert fixed([2048], 2048) == (0, 2048, 1)
+    assert fixed([2049], 2048) == (0, 2048, 2)
+    rng = np.random.default_rng(5)
+    for _ in range(100):
+        lens = rng.integers(0, 1 << 20, size=int(rng.integers(1, 65)))
+        split = 16 * int(rng.integers(1, 512))
+        rc, chunk, splits = fixed(lens, split)
+        assert rc == 0 and chunk == split
+        assert splits == max(1, -(-int(lens.max()) // split))
+        # one sequence alone gets the same slices as inside the batch: its
+        # own split count does not depend on the companions
+        b = int(rng.integers(0, lens.size))
+        rc1, chunk1, splits1 = fixed(lens[b:b + 1], split)
+        assert chunk1 == chunk and -(-int(lens[b]) // split) <= splits1 <= splits
+    # invalid and unsupported inputs leave the outputs untouched
+    assert fixed([10], 100)[0] == 1 and fixed([10], 100)[1:] == (-5, -5)
+    assert fixed([10], 0)[0] == 1
+    assert fixed([-1], 64)[0] == 1
+    assert fixed([(1 << 23)], 16)[0] == 2                  # 524288 splits > 65535
+    assert lib.attn_decode_plan_fixed(1, None, 64, ctypes.byref(ctypes.c_int32()), ctypes.byref(ctypes.c_int32())) == 1
+    # the binding returns the library's plan and raises on its errors
     assert api.decode_plan_fixed([3000, 20000, 5], 256) == (256, 79)
-    assert api.decode_plan_fixed([], 2048) == (2048, 1)
-    with pytest.raises(ValueError):
+    with pytest.raises(api.AttnError):
         api.decode_plan_fixed([10], 100)
