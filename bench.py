@@ -387,7 +387,31 @@ def cpu_baseline(inp, budget_s=15.0):
         heads += 1
     return dict(value=flop / spent / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
                 sample=f"{rows_total} random query rows ({heads} blocks of 256, cycling over the heads) of the T=8192 causal "
-                       f"prefill, float64 numpy materialised attention, {spent:.1f} s of oracle time")
+                       f"prefill, float64 numpy materialised attention, {spent:.1f} s of oracle time",
+                affinity_cores=len(os.sched_getaffinity(0)), cpu_model=cpu_model(), blas=blas_config(),
+                threads_note="cores = BLAS threads of the matmuls; the exponentials (np.exp) run on one thread")
+
+
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None if unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def blas_config():
+    """numpy's BLAS as threadpoolctl reports it, and the thread variables."""
+    import threadpoolctl
+    libs = [{k: p.get(k) for k in ("internal_api", "version", "threading_layer", "num_threads", "architecture")}
+            for p in threadpoolctl.threadpool_info() if p.get("user_api") == "blas"]
+    env = {k: os.environ[k] for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+           if k in os.environ}
+    return {"libraries": libs, "env": env}
 
 
 def run_only(args, dev):

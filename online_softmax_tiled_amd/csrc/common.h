@@ -86,6 +86,20 @@ struct Elem<ATTN_DTYPE_F16> {
   }
 };
 
+// A pair of bf16 values (lo in bits [15:0]) as a pair of fp16 values. Every
+// bf16 value of magnitude in [2^-14, 65536) is an fp16 value (fp16 has more
+// significand bits and covers that exponent range), so these convert
+// exactly; smaller ones land on the fp16 subnormal grid (absolute error below
+// 2^-24), and magnitudes of 65536 or more do not fit (they come out as
+// +-65504). `vmax` keeps the largest magnitude seen, so the caller can tell.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t x, float& vmax) {
+  const float lo = __builtin_bit_cast(float, x << 16);
+  const float hi = __builtin_bit_cast(float, x & 0xffff0000u);
+  vmax = fmaxf(vmax, fmaxf(fabsf(lo), fabsf(hi)));
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+}
+constexpr float kF16Overflow = 65536.f;   // smallest bf16 magnitude fp16 cannot hold
+
 // Byte select of v_perm_b32: result byte i = byte sel[i] of {hi:lo} (0-3 lo).
 __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);

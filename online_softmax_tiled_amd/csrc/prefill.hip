@@ -20,7 +20,7 @@
 //   lane l holds query row l%32 and, for register r of 32-key block kb, key
 //   kb*32 + 8*(r/4) + 4*(l/32) + r%4.
 //   O~^T += V^T P^T on the same MFMA: P^T is the B operand straight from the
-//   score registers (rounded to the operand dtype; the 8 keys of lane group
+//   score registers (rounded to fp16, see below; the 8 keys of lane group
 //   h in 16-key chunk cc are 16cc + 4h + {0..3} and 16cc + 8 + 4h + {0..3});
 //   the V^T A operand is two transposing LDS reads of 4 consecutive keys x 1
 //   column each from the natural V tile.
@@ -74,17 +74,28 @@
 // row past the keys or on a page outside the pool gets an offset past the
 // range and reads zeros, with no branch and no select.
 //
+// Operand type of the PV product: fp16, for both input types. P is rounded
+// to fp16 (11 significant bits against bf16's 8) and bf16 V is converted to
+// fp16 when it is staged into LDS; every bf16 value of magnitude below 65536
+// converts exactly (smaller than 2^-14 with an absolute error below 2^-24).
+// With bf16 weights the error of the convex combination reaches about
+// 2^-9 * sum_j w_j |v_j - O|, which with the output's own rounding (half a
+// bf16 step, 2^-8 for |O| in [2, 4)) can pass 1e-2; fp16 weights cut that
+// term by 8. A workgroup that stages a V value fp16 cannot hold (a bf16
+// magnitude of 65536 or more) runs its pass again with bf16 operands.
+//
 // Two running sums per row: l, the fp32 sum of the weights p (for the LSE),
-// and l~, the sum of the weights as rounded to the operand dtype for the PV
-// product. O~ accumulates the rounded weights, so it is divided by l~: the
-// output is then an exact convex combination of the value rows with weights
-// p~ / l~, whatever the magnitude of the dominant weight (up to 2^kTau here).
+// and l~, the sum of the weights as rounded for the PV product. O~
+// accumulates the rounded weights, so it is divided by l~: the output is then
+// an exact convex combination of the value rows with weights p~ / l~,
+// whatever the magnitude of the dominant weight (up to 2^kTau here).
 //
 // Epilogue: O = O~/l~ rounded to the output dtype, LSE = (m + log2 l) ln 2.
 // l = 0 (no visible key) or a zero row-mask entry gives +0.0 output and
 // LSE = -inf ("Merge normalized attention without averaging tile outputs",
 // last paragraph).
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -345,16 +356,27 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) store16(&lds_k[slot][((tid + kThreads * i) >> 4) * kKStr + (tid & 15) * 8], kreg[i]);
   };
-  auto store_v = [&](int slot) {
+  // V tiles reach LDS in the element type of the PV product: fp16 in the
+  // fp16 pass (bf16 inputs are converted here, exactly below 65536 in
+  // magnitude; v_max records the largest magnitude staged), the input type
+  // in the fallback pass.
+  float v_max = 0.f;
+  auto conv_v = [&](u32x4 x, auto pv16) -> u32x4 {
+    if constexpr (decltype(pv16)::value && DT == ATTN_DTYPE_BF16) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) store16(&lds_v[slot][((tid + kThreads * i) >> 4) * kVStr + (tid & 15) * 8], vreg[i]);
+      for (int e = 0; e < 4; ++e) x[e] = bf16x2_to_f16x2(x[e], v_max);
+    }
+    return x;
+  };
+  auto store_v = [&](int slot, auto pv16) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      store16(&lds_v[slot][((tid + kThreads * i) >> 4) * kVStr + (tid & 15) * 8], conv_v(vreg[i], pv16));
   };
 
   const int v_lane_off = (4 * half + ((lane & 15) >> 2)) * kVStr + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   f32x16 acc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
   float m_ref = -INFINITY;
   float l_run = 0.f;
   float lr_run = 0.f;
@@ -456,6 +478,19 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     return j < n_vis ? (int)tile_list[j] : t_end;
   };
 
+  // One pass over the key tiles. PV16: the PV product takes fp16 operands
+  // (P rounded to fp16 -- 3 more significand bits than bf16 -- and V as
+  // staged by store_v); with bf16 inputs the pass is run again with bf16
+  // operands if a V value of magnitude 65536 or more was staged (fp16 cannot
+  // hold it). Every wave of the workgroup takes the same passes.
+  auto pass = [&](auto pv16) {
+  constexpr bool PV16 = decltype(pv16)::value;
+  using EP = Elem<PV16 ? ATTN_DTYPE_F16 : DT>;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+  m_ref = -INFINITY;
+  l_run = 0.f;
+  lr_run = 0.f;
   f32x16 sc[2];     // scores of tile j
   u32x4 pp[4];      // P^T of tile j - 1
   uint64_t kbits = ~0ull;
@@ -474,7 +509,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     load_k(tile_at(0));
     load_v(tile_at(0));
     store_k(0);
-    store_v(0);
+    store_v(0, pv16);
     if (n_vis > 1) {
       if (PAGED) {
         pg_k[0] = page_of(1, 0);
@@ -577,7 +612,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
         const bool as_is = !PAGED || pool32;
         store16(&lds_k[j & 1][s_row(i) * kKStr + (st & 15) * 8], as_is || (ok[u] >> i & 1u) ? sk[u][i] : zero);
         store16(&lds_v[(j + 1) % 3][s_row(i) * kVStr + (st & 15) * 8],
-                as_is || (ok[u] >> (4 + i) & 1u) ? sv[u][i] : zero);
+                conv_v(as_is || (ok[u] >> (4 + i) & 1u) ? sv[u][i] : zero, pv16));
       }
     };
     // The pairs stored in iterations 0 and 1, with the pages of iteration 0's
@@ -679,7 +714,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(sc[0][r], sc[1][r]));
       read_v(1, fb);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) acc[db] = E::mfma32(fa[db], pp[0], acc[db]);
+      for (int db = 0; db < 4; ++db) acc[db] = EP::mfma32(fa[db], pp[0], acc[db]);
       __builtin_amdgcn_sched_barrier(0);
       // slice 1: PV chunk 1 | reference update, exps of block 0 rows 0-7
       read_v(2, fa);
@@ -693,7 +728,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
         base = m_ref == -INFINITY ? 0.f : m_ref;
       }
 #pragma unroll
-      for (int db = 0; db < 4; ++db) acc[db] = E::mfma32(fb[db], pp[1], acc[db]);
+      for (int db = 0; db < 4; ++db) acc[db] = EP::mfma32(fb[db], pp[1], acc[db]);
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         sc[0][r] = fast_exp2(__builtin_fmaf(sc[0][r], p.c, -base));
@@ -703,7 +738,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
       // slice 2: PV chunk 2 | exps of block 0 rows 8-15
       read_v(3, fb);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) acc[db] = E::mfma32(fa[db], pp[2], acc[db]);
+      for (int db = 0; db < 4; ++db) acc[db] = EP::mfma32(fa[db], pp[2], acc[db]);
 #pragma unroll
       for (int r = 8; r < 16; ++r) {
         sc[0][r] = fast_exp2(__builtin_fmaf(sc[0][r], p.c, -base));
@@ -713,7 +748,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
       // slice 3: PV chunk 3 | exps of block 1 rows 0-7
       read_k(0, fa);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) acc[db] = E::mfma32(fb[db], pp[3], acc[db]);
+      for (int db = 0; db < 4; ++db) acc[db] = EP::mfma32(fb[db], pp[3], acc[db]);
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         sc[1][r] = fast_exp2(__builtin_fmaf(sc[1][r], p.c, -base));
@@ -747,20 +782,20 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
 #pragma unroll
           for (int cc = 0; cc < 2; ++cc) {
             const int r0 = cc * 8;
-            pn[cc] = u32x4{E::pack2(sc[0][r0 + 0], sc[0][r0 + 1]), E::pack2(sc[0][r0 + 2], sc[0][r0 + 3]),
-                           E::pack2(sc[0][r0 + 4], sc[0][r0 + 5]), E::pack2(sc[0][r0 + 6], sc[0][r0 + 7])};
+            pn[cc] = u32x4{EP::pack2(sc[0][r0 + 0], sc[0][r0 + 1]), EP::pack2(sc[0][r0 + 2], sc[0][r0 + 3]),
+                           EP::pack2(sc[0][r0 + 4], sc[0][r0 + 5]), EP::pack2(sc[0][r0 + 6], sc[0][r0 + 7])};
           }
         } else if (c2 == 2) {
 #pragma unroll
           for (int cc = 2; cc < 4; ++cc) {
             const int r0 = (cc - 2) * 8;
-            pn[cc] = u32x4{E::pack2(sc[1][r0 + 0], sc[1][r0 + 1]), E::pack2(sc[1][r0 + 2], sc[1][r0 + 3]),
-                           E::pack2(sc[1][r0 + 4], sc[1][r0 + 5]), E::pack2(sc[1][r0 + 6], sc[1][r0 + 7])};
+            pn[cc] = u32x4{EP::pack2(sc[1][r0 + 0], sc[1][r0 + 1]), EP::pack2(sc[1][r0 + 2], sc[1][r0 + 3]),
+                           EP::pack2(sc[1][r0 + 4], sc[1][r0 + 5]), EP::pack2(sc[1][r0 + 6], sc[1][r0 + 7])};
           }
         } else {
 #pragma unroll
           for (int cc = 0; cc < 4; ++cc)
-            lr_run = E::add_pair(pn[cc][3], E::add_pair(pn[cc][2], E::add_pair(pn[cc][1], E::add_pair(pn[cc][0], lr_run))));
+            lr_run = EP::add_pair(pn[cc][3], EP::add_pair(pn[cc][2], EP::add_pair(pn[cc][1], EP::add_pair(pn[cc][0], lr_run))));
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -779,11 +814,19 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
         }
       }
       store_k(j & 1);
-      store_v((j + 1) % 3);
+      store_v((j + 1) % 3, pv16);
     }
     __syncthreads();
   }
+  };
 
+  pass(std::true_type{});
+  if constexpr (DT == ATTN_DTYPE_BF16) {
+    // a staged V value fp16 cannot hold: the workgroup runs the pass again
+    // with bf16 operands (all waves take the same decision)
+    if (__syncthreads_or(v_max >= kF16Overflow)) pass(std::false_type{});
+  }
+  if (stagers && wave >= 4) return;
   if (!wave_valid || qrow >= T_q) return;
   const float l_tot = sum_halves(l_run);
   const float lr_tot = sum_halves(lr_run);

@@ -5,14 +5,15 @@ Tolerances (max abs error on outputs; LSE relative error |d| / max(1, |LSE|)):
 fp16 outputs 2e-3, bf16 outputs 1e-2, LSE 1e-4; the paged gather and the
 outputs of rows with no visible key (+0.0 bits, LSE -inf) are bit-exact.
 
-The output tolerance bounds the kernel's result before its final rounding
-to the output format: an element passes when it is the nearest-even rounding
-of some value within the tolerance of the exact result, i.e.
-|o - exact| <= tol + half the format's spacing at o. The flat reading cannot
-be met by any bf16 output on the logit-std-30 stress workload: there the
-exact float64 result, rounded to the nearest bf16, is itself up to 0.0155
-away (|O| reaches 5.1, where bf16 values are 2^-5 apart). Each check also
-reports how many elements needed the rounding allowance.
+The output gate is flat: every element must lie within the tolerance of the
+exact result. The one exception is an element whose exact value the output
+format cannot hold that closely: half the format's spacing at the exact
+value exceeds the tolerance and the exact value is not itself a format
+value (bf16 from |O| >= 4, fp16 from |O| >= 8). Such an element must be
+within the tolerance plus half that spacing, i.e. a rounding of a value
+within the tolerance. The excepted set depends on the exact values only, not
+on the GPU's; each check asserts a bound on its size and records its counts
+in the session summary.
 """
 
 import math
@@ -46,26 +47,42 @@ def lse_rel(a, b):
     return np.abs(a - b) / np.maximum(1.0, np.abs(b))
 
 
-def assert_outputs(o_gpu_t, lse_gpu, o_ref, lse_ref, dtype, what):
-    """o_gpu_t: torch output (any leading shape, last dim d); refs float64."""
+TORCH_DT = {"f16": torch.float16, "bf16": torch.bfloat16}
+GATE_RECORDS = []   # (what, elements, excepted, beyond the flat gate, max abs err)
+
+
+def format_exception(exact, dtype):
+    """Elements whose exact value the output format cannot hold within the
+    tolerance: half its spacing there exceeds TOL and the exact value is not
+    a format value. Returns (mask, half spacing at the exact value)."""
+    mag = np.abs(exact)
+    half = np.where(mag > 0, np.exp2(np.floor(np.log2(np.where(mag > 0, mag, 1.0))) - MANT_BITS[dtype] - 1), 0.0)
+    rne = torch.from_numpy(np.ascontiguousarray(exact)).to(TORCH_DT[dtype]).double().numpy()
+    return (half > TOL[dtype]) & (rne != exact), half
+
+
+def assert_outputs(o_gpu_t, lse_gpu, o_ref, lse_ref, dtype, what, max_excepted_frac=2e-5):
+    """o_gpu_t: torch output (any leading shape, last dim d); refs float64.
+    Flat gate everywhere except the format's exception set (module
+    docstring), whose size must stay within max(2, max_excepted_frac * n)."""
     o_gpu = o_gpu_t.float().cpu().numpy().astype(np.float64)
     empty = np.isneginf(lse_ref)
     diff = np.abs(o_gpu - o_ref)
     err = float(np.max(diff)) if o_ref.size else 0.0
-    # half the spacing of the output grid at the stored value
-    mag = np.abs(o_gpu)
-    half_ulp = np.where(mag > 0, np.exp2(np.floor(np.log2(np.where(mag > 0, mag, 1.0))) - MANT_BITS[dtype] - 1), 0.0)
-    bad = diff > TOL[dtype] + half_ulp
+    exc, half = format_exception(o_ref, dtype)
+    bad = np.where(exc, diff > TOL[dtype] + half, diff > TOL[dtype])
     if bad.any():
         idx = np.argwhere(bad)[:6]
         detail = "; ".join(f"at {tuple(int(x) for x in i)}: exact {o_ref[tuple(i)]:.6f} "
                            f"got {o_gpu[tuple(i)]:.6f}" for i in idx)
-        raise AssertionError(f"{what}: max abs err {err:.3e}; {int(bad.sum())} elements beyond "
-                             f"{TOL[dtype]} + half an output ulp: {detail}")
-    n_allow = int((diff > TOL[dtype]).sum())
-    if n_allow:
-        print(f"{what}: {n_allow} of {diff.size} elements within tolerance only after the output "
-              f"rounding allowance (max abs err {err:.3e})")
+        raise AssertionError(f"{what}: max abs err {err:.3e}; {int(bad.sum())} elements beyond the gate "
+                             f"(flat {TOL[dtype]}, or {TOL[dtype]} + half the format spacing where the format "
+                             f"cannot hold the exact value): {detail}")
+    n_exc = int(exc.sum())
+    n_beyond = int((diff > TOL[dtype]).sum())
+    GATE_RECORDS.append((what, int(diff.size), n_exc, n_beyond, err))
+    limit = max(2, int(max_excepted_frac * diff.size))
+    assert n_exc <= limit, f"{what}: {n_exc} of {diff.size} elements in the format's exception set (limit {limit})"
     if lse_gpu is not None:
         assert np.array_equal(np.isneginf(lse_gpu), empty), f"{what}: empty-row LSE mismatch"
         fin = ~empty
@@ -171,23 +188,29 @@ def test_prefill_all_keys_masked():
 def test_prefill_stress_config_reduced():
     inp = make_config("stress_prefill_t4096", T_q=1024, T_k=1024)
     o, lse, o_ref, lse_ref = run_prefill(inp)
-    assert_outputs(o, lse, o_ref, lse_ref, "bf16", "stress prefill T=1024")
+    assert_outputs(o, lse, o_ref, lse_ref, "bf16", "stress prefill T=1024", max_excepted_frac=1e-4)
 
 
 def test_prefill_stress_config_full():
     inp = make_config("stress_prefill_t4096")
     o, lse, o_ref, lse_ref = run_prefill(inp)
     assert np.isneginf(lse_ref).any()
-    assert_outputs(o, lse, o_ref, lse_ref, "bf16", "stress prefill T=4096")
+    assert_outputs(o, lse, o_ref, lse_ref, "bf16", "stress prefill T=4096", max_excepted_frac=1e-4)
 
 
-def test_prefill_llama3_8b_t8192_sampled_rows():
+def test_prefill_llama3_8b_t8192_every_row_block():
+    # the full-size launch the bench times: two random rows from every
+    # 32-row block (one in each half), the same for every head, so every
+    # (head, row block) pair -- i.e. every wave of every workgroup -- is
+    # compared with the oracle, plus the edge rows
     inp = make_config("llama3_8b_prefill_t8192")
     rng = np.random.default_rng(2)
-    rows = np.unique(np.concatenate([[0, 1, 31, 32, 63, 64, 4095, 8190, 8191],
-                                     rng.choice(8192, 55, replace=False)]))
+    blocks = np.arange(0, 8192, 32)
+    rows = np.unique(np.concatenate([blocks + rng.integers(0, 16, blocks.size),
+                                     blocks + 16 + rng.integers(0, 16, blocks.size),
+                                     [0, 1, 31, 32, 63, 64, 4095, 8190, 8191]]))
     o, lse, o_ref, lse_ref = run_prefill(inp, rows=rows)
-    assert_outputs(o, lse, o_ref, lse_ref, "bf16", "llama3-8b prefill T=8192 (sampled rows)")
+    assert_outputs(o, lse, o_ref, lse_ref, "bf16", f"llama3-8b prefill T=8192 ({rows.size} rows per head)")
 
 
 def test_prefill_causal_single_key_row_is_exact():
@@ -573,10 +596,10 @@ def test_merge_lse_llama3_8b_shape_sampled():
 
 # ------------------------------------------------------------------ paged (chunked) prefill
 
-def _run_paged_prefill(c, causal, rows_per_seq=None, host_order=False):
+def _run_paged_prefill(c, causal, rows_per_block=False, host_order=False, max_excepted_frac=2e-5):
     """attn_prefill_paged on a chunked-prefill case; checks every sequence
-    against the oracle over its ground-truth contiguous K/V (optionally on a
-    sample of its query rows)."""
+    against the oracle over its ground-truth contiguous K/V (every query row,
+    or with rows_per_block one random row from each 32-row block)."""
     from online_softmax_tiled_amd.workloads import DTYPES
     q = to_dev(c["q"])
     o, lse = api.prefill_paged(q, to_dev(c["cu_seqlens_q"]), c["max_q"], to_dev(c["k_pool"]), to_dev(c["v_pool"]),
@@ -597,13 +620,17 @@ def _run_paged_prefill(c, causal, rows_per_seq=None, host_order=False):
             km = np.ones((1, tk), dtype=np.uint8)
             km[0, excluded[b]] = 0
         rows = None
-        if rows_per_seq is not None and tq > rows_per_seq:
-            rows = np.sort(np.random.default_rng(b).choice(tq, size=rows_per_seq, replace=False))
+        if rows_per_block and tq > 32:
+            # one random row from every 32-row block of the sequence
+            starts = np.arange(0, tq, 32)
+            rows = np.minimum(starts + np.random.default_rng(b).integers(0, 32, starts.size), tq - 1)
+            rows = np.unique(np.concatenate([rows, [0, tq - 1]]))
         o_ref, lse_ref = attention_ref(qb, kb, vb, c["scale"], causal, key_mask=km, rows=rows)
         sel = np.arange(tq) if rows is None else rows
         ob = o[cu[b]:cu[b + 1]][torch.from_numpy(sel).to(DEV)].permute(1, 0, 2).unsqueeze(0)
         lb = lse[cu[b]:cu[b + 1]].cpu().numpy().astype(np.float64)[sel].T[None]
-        assert_outputs(ob, lb, o_ref, lse_ref, c["dtype"], f"paged prefill seq {b} ({tq} new / {tk} keys)")
+        assert_outputs(ob, lb, o_ref, lse_ref, c["dtype"], f"paged prefill seq {b} ({tq} new / {tk} keys)",
+                       max_excepted_frac=max_excepted_frac)
 
 
 # pools just under the largest addressed with 32-bit offsets (pool + one page
@@ -668,9 +695,10 @@ def test_paged_prefill_edge_sequences():
 
 def test_paged_prefill_chunked_llama3_8b_b8():
     # the measured chunked-prefill workload, in the bench's launch
-    # configuration, on 96 sampled query rows per sequence
+    # configuration, on one random query row from every 32-row block of
+    # every sequence (every wave's rows are compared)
     c = make_config("chunked_prefill_llama3_8b_b8")
-    _run_paged_prefill(c, True, rows_per_seq=96, host_order=True)
+    _run_paged_prefill(c, True, rows_per_block=True, host_order=True)
 
 
 def test_paged_prefill_matches_contiguous_prefill():
@@ -891,3 +919,57 @@ def test_decode_large_groups(h, h_kv, paged, page_size):
     o_ref, lse_ref = decode_ref(dec["q"], dec["k_seqs"], dec["v_seqs"], dec["seq_lens"], dec["scale"])
     assert_outputs(o, lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16",
                    f"decode g={h // h_kv} paged={paged} plan={plan}")
+
+
+# ------------------------------------------------------------------ PV product operand type
+
+def _check_big_column(o, lse, o_ref, lse_ref, col, what):
+    """Flat gate on every output column but ``col``; on ``col`` (which holds
+    weighted sums of a value of 2^17) a relative bound of 2^-7: bf16 weights
+    and the bf16 output each round to 2^-9 relative, while a value clamped to
+    the fp16 maximum would be off by up to half."""
+    keep = [c for c in range(o_ref.shape[-1]) if c != col]
+    assert_outputs(o[..., keep], lse, o_ref[..., keep], lse_ref, "bf16", what)
+    got = o[..., col].float().cpu().numpy().astype(np.float64)
+    ref = o_ref[..., col]
+    assert np.abs(ref).max() >= 100          # the big value carries real weight somewhere
+    rel = np.abs(got - ref) / np.maximum(np.abs(ref), 1.0)
+    assert float(rel.max()) <= 2.0 ** -7, f"{what}: column {col} rel err {rel.max():.3e}"
+
+
+def test_bf16_values_beyond_fp16_range_take_the_bf16_pass():
+    # The PV product runs on fp16 operands (bf16 V converted exactly when it
+    # is staged). A bf16 value of magnitude 65536 or more does not fit fp16:
+    # the workgroups that stage one must rerun with bf16 operands, so the
+    # result is the exact one up to bf16 rounding, not one computed with a
+    # value clamped to 65504. One V value of 2^17 in each form that stages V.
+    from online_softmax_tiled_amd.workloads import make_chunked_prefill
+    big = float(2 ** 17)
+    # contiguous prefill, with and without a key mask
+    for km in (0.0, 0.2):
+        inp = make_prefill(1, 8, 2, 96, 96, 128, "bf16", seed=61, causal=True, key_p=km)
+        inp["v"][0, 1, 5, 3] = big
+        o, lse, o_ref, lse_ref = run_prefill(inp)
+        _check_big_column(o, lse, o_ref, lse_ref, 3, f"prefill with V = 2^17 (key mask p={km})")
+    # paged (chunked) prefill: sequence 1, key 7, column 9
+    c = make_chunked_prefill(2, 8, 2, 128, "bf16", seed=62, ctx_range=(60, 200), new_range=(20, 60), page_size=16)
+    b, key = 1, 7
+    c["v_pool"][c["block_table"][b, key // 16], key % 16, 0, 9] = big
+    c["v_seqs"][b][0, key, 9] = big
+    q = to_dev(c["q"])
+    o, lse = api.prefill_paged(q, to_dev(c["cu_seqlens_q"]), c["max_q"], to_dev(c["k_pool"]), to_dev(c["v_pool"]),
+                               to_dev(c["block_table"]), to_dev(c["seq_lens_k"]), causal=True, scale=c["scale"])
+    torch.cuda.synchronize()
+    cu = c["cu_seqlens_q"]
+    qb = c["q"][cu[b]:cu[b + 1]].permute(1, 0, 2).unsqueeze(0)
+    o_ref, lse_ref = attention_ref(qb, c["k_seqs"][b].unsqueeze(0), c["v_seqs"][b].unsqueeze(0), c["scale"], True)
+    ob = o[cu[b]:cu[b + 1]].permute(1, 0, 2).unsqueeze(0)
+    lb = lse[cu[b]:cu[b + 1]].cpu().numpy().astype(np.float64).T[None]
+    _check_big_column(ob, lb, o_ref, lse_ref, 9, "paged prefill with V = 2^17")
+    # decode with the heads as rows (staging waves), contiguous: column 100
+    dec = make_decode(B=2, h=64, h_kv=1, d=128, dtype="bf16", seed=63, seq_lens=[300, 90], paged=False)
+    dec["v"][0, 0, 17, 100] = -big
+    dec["v_seqs"][0][0, 17, 100] = -big
+    o_ref, lse_ref = decode_ref(dec["q"], dec["k_seqs"], dec["v_seqs"], dec["seq_lens"], dec["scale"])
+    o, lse, used = run_decode(dec)
+    _check_big_column(o, lse, o_ref, lse_ref, 100, "row-form decode with V = -2^17")
