@@ -274,6 +274,12 @@ def bench_decode_large_group(steps, warmup, dev, paged=False):
 
 
 def bench_decode_contiguous(steps, warmup, dev, copies=40):
+    """Batch-1 decode on the 70B-TP8 shard: attn_decode (split, then merge),
+    HIP-graph timed over ``copies`` distinct K/V copies in turn (671 MB,
+    beyond the 256 MB MALL, so every step reads cold data). Beside it, two
+    floors on the same rotation: a plain read of the step's 16.8 MB of K/V
+    (the copy's K and V, stored next to each other, with attn_stream_read) and
+    one tiny kernel launch."""
     import torch
     from online_softmax_tiled_amd import api
     from online_softmax_tiled_amd.workloads import make_config
@@ -281,10 +287,15 @@ def bench_decode_contiguous(steps, warmup, dev, copies=40):
     q = dec["q"].to(dev)
     sl = torch.from_numpy(dec["seq_lens"]).to(dev)
     k0, v0 = dec["k"].to(dev), dec["v"].to(dev)
-    ks = [k0] + [k0.clone() for _ in range(copies - 1)]
-    vs = [v0] + [v0.clone() for _ in range(copies - 1)]
+    kvs = []
+    for _ in range(copies):
+        kv = torch.empty((2,) + tuple(k0.shape), dtype=k0.dtype, device=dev)
+        kv[0].copy_(k0)
+        kv[1].copy_(v0)
+        kvs.append(kv)
+    del k0, v0
     B, h, d = q.shape
-    h_kv = k0.shape[1]
+    h_kv = kvs[0].shape[2]
     chunk, splits = api.decode_plan(dec["seq_lens"], h, h_kv, device=dev)
     po = torch.empty((B, h, splits, d), dtype=torch.float32, device=dev)
     pm = torch.empty((B, h, splits), dtype=torch.float32, device=dev)
@@ -292,23 +303,37 @@ def bench_decode_contiguous(steps, warmup, dev, copies=40):
     o = torch.empty((B, h, d), dtype=q.dtype, device=dev)
     lse = torch.empty((B, h), dtype=torch.float32, device=dev)
     kv_bytes = 2 * int(dec["seq_lens"].sum()) * h_kv * d * q.element_size()
+    rd = torch.empty(1024, dtype=torch.int32, device=dev)
+    tiny = torch.empty(16, dtype=torch.float32, device=dev)
 
     def split_only(i=0):
-        j = i % copies
-        api.decode_split(q, ks[j], vs[j], sl, chunk, splits, scale=dec["scale"], part_o=po, part_m=pm, part_l=pl)
+        kv = kvs[i % copies]
+        api.decode_split(q, kv[0], kv[1], sl, chunk, splits, scale=dec["scale"], part_o=po, part_m=pm, part_l=pl)
 
     def full(i=0):
-        split_only(i)
-        api.merge_states(po, pm, pl, sl, chunk, q.dtype, out=o, lse=lse)
+        kv = kvs[i % copies]
+        api.decode_call(q, kv[0], kv[1], sl, chunk, splits, scale=dec["scale"], part_o=po, part_m=pm, part_l=pl,
+                        out=o, lse=lse)
+
+    def read_floor(i=0):
+        api.stream_read(kvs[i % copies], chunks=1024, out=rd)
+
+    def launch_floor(i=0):
+        tiny.fill_(float(i))
 
     ms_eager, _ = time_loop(full, steps, warmup)
     ms_split = time_graph(split_only, copies * 5)
     ms = time_graph(full, copies * 5)
+    ms_read = time_graph(read_floor, copies * 5)
+    ms_launch = time_graph(launch_floor, copies * 5)
     return dict(workload="decode_70b_tp8_s32768", kv_bytes=kv_bytes, us_per_step=ms * 1e3,
-                split_us=ms_split * 1e3, eager_us_per_step=ms_eager * 1e3,
-                gbs=kv_bytes / (ms * 1e-3) / 1e9,
-                frac_hbm=kv_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, plan=[chunk, splits],
-                rotated_kv_copies=copies, timing="HIP graph of split+merge steps, replayed")
+                gbs=kv_bytes / (ms * 1e-3) / 1e9, frac_hbm=kv_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                split_us=ms_split * 1e3, eager_us_per_step=ms_eager * 1e3, plan=[chunk, splits],
+                read_floor_us=ms_read * 1e3, read_floor_gbs=kv_bytes / (ms_read * 1e-3) / 1e9,
+                read_floor_frac_hbm=kv_bytes / (ms_read * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                launch_floor_us=ms_launch * 1e3, rotated_kv_copies=copies,
+                timing="HIP graph of attn_decode steps (split + merge), replayed; read_floor = attn_stream_read "
+                       "over the same 16.8 MB of K/V (1024 contiguous chunks); launch_floor = one 64-byte fill kernel")
 
 
 def bench_decode_paged(steps, warmup, dev, dec, fixed_split=None, gather=True):
@@ -338,8 +363,8 @@ def bench_decode_paged(steps, warmup, dev, dec, fixed_split=None, gather=True):
                          scale=dec["scale"], part_o=po, part_m=pm, part_l=pl)
 
     def full(i=0):
-        split_only()
-        api.merge_states(po, pm, pl, sl, chunk, q.dtype, out=o, lse=lse)
+        api.decode_call(q, kp, vp, sl, chunk, splits, block_table=bt, page_size=dec["page_size"],
+                        scale=dec["scale"], part_o=po, part_m=pm, part_l=pl, out=o, lse=lse)
 
     ms_split, _ = time_loop(split_only, steps, warmup)
     ms, _ = time_loop(full, steps, warmup)
@@ -509,7 +534,9 @@ def main():
         line["prefill_other"] = other
         decode = {}
         r3 = bench_decode_contiguous(max(200, args.steps), 20, dev)
-        log(f"decode 70b-tp8: {r3['us_per_step']:.2f} us/step ({r3['split_us']:.2f} split), {r3['gbs']:.0f} GB/s")
+        log(f"decode 70b-tp8: {r3['us_per_step']:.2f} us/step ({r3['split_us']:.2f} split), {r3['gbs']:.0f} GB/s; "
+            f"read floor {r3['read_floor_us']:.2f} us ({r3['read_floor_gbs']:.0f} GB/s), "
+            f"launch floor {r3['launch_floor_us']:.2f} us")
         decode[r3.pop("workload")] = r3
         from online_softmax_tiled_amd.workloads import make_config
         log("generating the paged decode workload ...")

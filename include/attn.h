@@ -238,6 +238,30 @@ int attn_merge_states(const float* part_o, const float* part_m, const float* par
                       void* o, float* lse, int dtype, void* stream);
 
 /*
+ * Split-KV decode, both stages in one call: stage 1 as attn_decode_split
+ * into the caller's partial buffers, then the merge as attn_merge_states,
+ * both on `stream`, with the same arguments, results and empty-row rules.
+ * [DA] opening section (split-K over keys, partial O~, m, l, then a
+ * reduction of the partials) and section "CUDA graphs need the split count
+ * pinned" (producer and reducer agree on the valid split count of each
+ * sequence). With a fixed chunk_keys (attn_decode_plan_fixed) each
+ * sequence's bits do not depend on the rest of the batch.
+ *
+ *   part_o/part_m/part_l  [B, h, max_splits, d_h] / [B, h, max_splits] fp32,
+ *                caller-owned scratch; their contents on return are the
+ *                split states.
+ *   o            [B, h, d_h] dtype (written); lse [B, h] fp32 or NULL.
+ * Errors as attn_decode_split; NULL partials or o: ATTN_ERR_INVALID.
+ */
+int attn_decode(const void* q, const void* k, const void* v,
+                const int32_t* block_table, int max_pages, int page_size, int num_pages,
+                const int32_t* seq_lens, int s_max,
+                int B, int h, int h_kv, int d_h,
+                int chunk_keys, int max_splits, int dtype, float scale,
+                float* part_o, float* part_m, float* part_l,
+                void* o, float* lse, void* stream);
+
+/*
  * Two-operand merge in (O, LSE) form: the output over the union of two
  * disjoint key ranges of the same query rows, from each range's normalised
  * output and LSE (a cascade's shared prefix and per-request suffix, or two
@@ -278,6 +302,22 @@ int attn_merge_lse(const void* o_a, const float* lse_a, const void* o_b, const f
 int attn_paged_gather(const void* pool, const int32_t* block_table, const int32_t* seq_lens,
                       int B, int h_kv, int d_h, int page_size, int max_pages, int num_pages,
                       int s_max, int dtype, void* out, void* stream);
+
+/*
+ * Measurement aid, not part of the attention path: read `bytes` bytes at
+ * `src` once, as a plain stream (each of `chunks` workgroups reads one
+ * contiguous chunk with 16-byte loads), and write one uint32 per workgroup
+ * to out[0 .. chunks) (the xor of the chunk's 32-bit words, so the loads
+ * cannot be dropped). Timing it on a kernel's own byte count gives the read
+ * rate the device attains at that size -- launch, first-byte latency and
+ * drain included -- the floor an HBM-bound kernel such as the split-KV
+ * decode is compared with.
+ *
+ *   src    device pointer, 16-byte aligned; bytes a multiple of 16.
+ *   chunks 1 .. 65536 workgroups.
+ *   out    [chunks] uint32, device.
+ */
+int attn_stream_read(const void* src, uint64_t bytes, int chunks, uint32_t* out, void* stream);
 
 /* Message describing the last error returned on the calling thread ("" if
  * none). The pointer stays valid until the next call on that thread. */

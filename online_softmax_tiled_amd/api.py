@@ -31,8 +31,10 @@ _SIGNATURES = {
     "attn_decode_split": [_c_void_p] * 4 + [_c_int] * 3 + [_c_void_p] + [_c_int] * 8 + [_c_float]
                          + [_c_void_p] * 4,
     "attn_merge_states": [_c_void_p] * 4 + [_c_int] * 5 + [_c_void_p, _c_void_p, _c_int, _c_void_p],
+    "attn_decode": [_c_void_p] * 4 + [_c_int] * 3 + [_c_void_p] + [_c_int] * 8 + [_c_float] + [_c_void_p] * 6,
     "attn_merge_lse": [_c_void_p] * 4 + [_c_int] * 2 + [_c_void_p, _c_void_p, _c_int, _c_void_p],
     "attn_paged_gather": [_c_void_p] * 3 + [_c_int] * 8 + [_c_void_p, _c_void_p],
+    "attn_stream_read": [_c_void_p, ctypes.c_uint64, _c_int, _c_void_p, _c_void_p],
     "attn_last_error": [],
     "attn_version": [],
 }
@@ -265,16 +267,67 @@ def merge_states(part_o, part_m, part_l, seq_lens, chunk_keys, dtype, out=None, 
     return out, lse
 
 
+def _kv_geometry(q, k, v, block_table, page_size):
+    """(h_kv, s_max, max_pages, num_pages, page_size) of contiguous or paged K/V, checked."""
+    dev, dt = q.device, q.dtype
+    B, h, d = q.shape
+    if block_table is None:
+        h_kv, s_max = k.shape[1], k.shape[2]
+        _want(k, "k", dt, (B, h_kv, s_max, d), dev)
+        _want(v, "v", dt, (B, h_kv, s_max, d), dev)
+        return h_kv, s_max, 0, 0, page_size
+    num_pages, page_size, h_kv = k.shape[0], k.shape[1], k.shape[2]
+    _want(k, "k_pool", dt, (num_pages, page_size, h_kv, d), dev)
+    _want(v, "v_pool", dt, (num_pages, page_size, h_kv, d), dev)
+    _want(block_table, "block_table", torch.int32, None, dev)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_pages]")
+    return h_kv, 0, block_table.shape[1], num_pages, page_size
+
+
+def decode_call(q, k, v, seq_lens, chunk_keys, max_splits, block_table=None, page_size=16, scale=None,
+                part_o=None, part_m=None, part_l=None, out=None, lse=None):
+    """Both decode stages in one call of attn_decode; the partial buffers are
+    allocated with torch when not given. Returns (o [B,h,128], lse [B,h])."""
+    lib = load()
+    _want(q, "q")
+    dev, dt = q.device, q.dtype
+    B, h, d = q.shape
+    _want(seq_lens, "seq_lens", torch.int32, (B,), dev)
+    h_kv, s_max, max_pages, num_pages, page_size = _kv_geometry(q, k, v, block_table, page_size)
+    shp = (B, h, max_splits)
+    part_o = torch.empty(shp + (d,), dtype=torch.float32, device=dev) if part_o is None else part_o
+    part_m = torch.empty(shp, dtype=torch.float32, device=dev) if part_m is None else part_m
+    part_l = torch.empty(shp, dtype=torch.float32, device=dev) if part_l is None else part_l
+    _want(part_o, "part_o", torch.float32, shp + (d,), dev)
+    _want(part_m, "part_m", torch.float32, shp, dev)
+    _want(part_l, "part_l", torch.float32, shp, dev)
+    out = torch.empty((B, h, d), dtype=dt, device=dev) if out is None else out
+    _want(out, "out", dt, (B, h, d), dev)
+    lse = torch.empty((B, h), dtype=torch.float32, device=dev) if lse is None else lse
+    _want(lse, "lse", torch.float32, (B, h), dev)
+    scale = float(np.float32(1.0 / np.sqrt(d))) if scale is None else float(scale)
+    _check("attn_decode", lib.attn_decode(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(block_table), max_pages, page_size, num_pages,
+        _ptr(seq_lens), s_max, B, h, h_kv, d, int(chunk_keys), int(max_splits), _dtype_code(q),
+        scale, _ptr(part_o), _ptr(part_m), _ptr(part_l), _ptr(out), _ptr(lse), _stream(dev)))
+    return out, lse
+
+
 def decode(q, k, v, seq_lens, seq_lens_host=None, block_table=None, page_size=16, scale=None,
-           plan=None, num_cus=None):
-    """Split-KV decode: plan (host), stage 1 and stage 2 (device).
-    Returns (o [B,h,128], lse [B,h], (chunk_keys, max_splits))."""
+           plan=None, num_cus=None, one_call=True):
+    """Split-KV decode: plan (host), then both stages on the device -- in one
+    call of attn_decode (``one_call``) or as attn_decode_split followed by
+    attn_merge_states. Returns (o [B,h,128], lse [B,h], (chunk_keys, max_splits))."""
     B, h, _ = q.shape
     h_kv = k.shape[1] if block_table is None else k.shape[2]
     if plan is None:
         lens = seq_lens.cpu().numpy() if seq_lens_host is None else seq_lens_host
         plan = decode_plan(lens, h, h_kv, num_cus=num_cus, device=q.device)
     chunk, splits = plan
+    if one_call:
+        o, lse = decode_call(q, k, v, seq_lens, chunk, splits, block_table, page_size, scale)
+        return o, lse, plan
     po, pm, pl = decode_split(q, k, v, seq_lens, chunk, splits, block_table, page_size, scale)
     o, lse = merge_states(po, pm, pl, seq_lens, chunk, q.dtype)
     return o, lse, plan
@@ -318,4 +371,16 @@ def paged_gather(pool, block_table, seq_lens, s_max, out=None):
     _check("attn_paged_gather", lib.attn_paged_gather(
         _ptr(pool), _ptr(block_table), _ptr(seq_lens), B, h_kv, d, page_size, max_pages, num_pages,
         s_max, _dtype_code(pool), _ptr(out), _stream(dev)))
+    return out
+
+
+def stream_read(src, chunks=1024, out=None):
+    """Read ``src`` (a contiguous device tensor) once via attn_stream_read, a
+    measurement aid for the attainable read rate; returns out [chunks] int32."""
+    lib = load()
+    _want(src, "src")
+    nbytes = src.numel() * src.element_size()
+    out = torch.empty(chunks, dtype=torch.int32, device=src.device) if out is None else out
+    _want(out, "out", torch.int32, (chunks,), src.device)
+    _check("attn_stream_read", lib.attn_stream_read(_ptr(src), nbytes, int(chunks), _ptr(out), _stream(src.device)))
     return out

@@ -44,6 +44,7 @@ hipError_t merge_lse(const void* o_a, const float* lse_a, const void* o_b, const
                      float* lse, int rows, int dtype, hipStream_t stream);
 int decode_plan(int B, const int32_t* seq_lens, int units_per_split, int wgs_per_cu, int num_cus, int32_t* chunk_keys,
                 int32_t* max_splits);
+hipError_t stream_read(const void* src, uint64_t bytes, int chunks, uint32_t* out, hipStream_t stream);
 }  // namespace attn
 
 namespace {
@@ -114,6 +115,53 @@ int check_scale(const char* fn, float scale) {
   REQUIRE(std::isfinite(scale) && scale > 0.f, ATTN_ERR_INVALID, "%s: scale must be finite and > 0 (got %g)", fn,
           (double)scale);
   return ATTN_OK;
+}
+
+// Arguments of a split-KV decode stage 1 (attn_decode_split, attn_decode).
+int check_decode(const char* fn, const void* q, const void* k, const void* v, const int32_t* block_table,
+                 int max_pages, int page_size, int num_pages, const int32_t* seq_lens, int s_max, int B, int h,
+                 int h_kv, int d_h, int chunk_keys, int max_splits, int dtype, float scale) {
+  if (int e = check_common(fn, dtype, d_h)) return e;
+  if (int e = check_heads(fn, h, h_kv)) return e;
+  if (int e = check_scale(fn, scale)) return e;
+  REQUIRE(h / h_kv <= kMaxGroup, ATTN_ERR_UNSUPPORTED, "%s: %d query heads per KV head (at most %d supported)",
+          fn, h / h_kv, kMaxGroup);
+  REQUIRE((long)max_splits * h_kv * B < (1L << 31), ATTN_ERR_UNSUPPORTED, "%s: grid too large", fn);
+  REQUIRE(B >= 0, ATTN_ERR_INVALID, "%s: negative batch %d", fn, B);
+  REQUIRE(chunk_keys > 0 && chunk_keys % 16 == 0, ATTN_ERR_INVALID,
+          "%s: chunk_keys must be a positive multiple of 16 (got %d)", fn, chunk_keys);
+  REQUIRE(max_splits >= 1 && max_splits <= 65535, ATTN_ERR_INVALID, "%s: max_splits must be in [1, 65535] (got %d)",
+          fn, max_splits);
+  REQUIRE(h_kv <= 65535 && B <= 65535, ATTN_ERR_UNSUPPORTED, "%s: grid too large", fn);
+  if (block_table) {
+    REQUIRE(page_size > 0 && page_size % 16 == 0, ATTN_ERR_UNSUPPORTED,
+            "%s: page_size must be a positive multiple of 16 (got %d)", fn, page_size);
+    REQUIRE(max_pages > 0 && num_pages > 0, ATTN_ERR_INVALID, "%s: max_pages and num_pages must be positive", fn);
+    REQUIRE((long)max_pages * page_size <= kMaxSeq, ATTN_ERR_UNSUPPORTED,
+            "%s: max_pages * page_size = %ld keys (at most %d supported)", fn, (long)max_pages * page_size, kMaxSeq);
+  } else {
+    REQUIRE(s_max >= 0, ATTN_ERR_INVALID, "%s: negative s_max %d", fn, s_max);
+    REQUIRE(s_max <= kMaxSeq, ATTN_ERR_UNSUPPORTED, "%s: s_max = %d keys (at most %d supported)", fn, s_max, kMaxSeq);
+  }
+  if (B == 0) return ATTN_OK;
+  REQUIRE(q && seq_lens, ATTN_ERR_INVALID, "%s: a required pointer is NULL", fn);
+  // Contiguous K/V with s_max = 0 hold no key (every sequence is empty), so
+  // they may be NULL; a paged pool always holds num_pages > 0 pages.
+  REQUIRE((k && v) || (!block_table && s_max == 0), ATTN_ERR_INVALID, "%s: k and v must not be NULL", fn);
+  return ATTN_OK;
+}
+
+// Stage 1 on the kernel the group size selects.
+hipError_t launch_split(const void* q, const void* k, const void* v, const int32_t* block_table, int max_pages,
+                        int page_size, int num_pages, const int32_t* seq_lens, int s_max, int B, int h, int h_kv,
+                        int chunk_keys, int max_splits, int dtype, float scale, float* part_o, float* part_m,
+                        float* part_l, hipStream_t stream) {
+  const int shift = block_table ? log2_exact(page_size) : 0;
+  if (h / h_kv >= kRowsMinGroup && shift >= 0)
+    return attn::decode_split_rows(q, k, v, block_table, max_pages, shift, num_pages, seq_lens, s_max, B, h, h_kv,
+                                   chunk_keys, max_splits, dtype, scale, part_o, part_m, part_l, stream);
+  return attn::decode_split(q, k, v, block_table, max_pages, page_size, num_pages, seq_lens, s_max, B, h, h_kv,
+                            chunk_keys, max_splits, dtype, scale, part_o, part_m, part_l, stream);
 }
 
 }  // namespace
@@ -224,42 +272,33 @@ int attn_decode_split(const void* q, const void* k, const void* v, const int32_t
                       int d_h, int chunk_keys, int max_splits, int dtype, float scale, float* part_o,
                       float* part_m, float* part_l, void* stream) {
   const char* fn = "attn_decode_split";
-  if (int e = check_common(fn, dtype, d_h)) return e;
-  if (int e = check_heads(fn, h, h_kv)) return e;
-  if (int e = check_scale(fn, scale)) return e;
-  REQUIRE(h / h_kv <= kMaxGroup, ATTN_ERR_UNSUPPORTED, "%s: %d query heads per KV head (at most %d supported)",
-          fn, h / h_kv, kMaxGroup);
-  REQUIRE((long)max_splits * h_kv * B < (1L << 31), ATTN_ERR_UNSUPPORTED, "%s: grid too large", fn);
-  REQUIRE(B >= 0, ATTN_ERR_INVALID, "%s: negative batch %d", fn, B);
-  REQUIRE(chunk_keys > 0 && chunk_keys % 16 == 0, ATTN_ERR_INVALID,
-          "%s: chunk_keys must be a positive multiple of 16 (got %d)", fn, chunk_keys);
-  REQUIRE(max_splits >= 1 && max_splits <= 65535, ATTN_ERR_INVALID, "%s: max_splits must be in [1, 65535] (got %d)",
-          fn, max_splits);
-  REQUIRE(h_kv <= 65535 && B <= 65535, ATTN_ERR_UNSUPPORTED, "%s: grid too large", fn);
-  if (block_table) {
-    REQUIRE(page_size > 0 && page_size % 16 == 0, ATTN_ERR_UNSUPPORTED,
-            "%s: page_size must be a positive multiple of 16 (got %d)", fn, page_size);
-    REQUIRE(max_pages > 0 && num_pages > 0, ATTN_ERR_INVALID, "%s: max_pages and num_pages must be positive", fn);
-    REQUIRE((long)max_pages * page_size <= kMaxSeq, ATTN_ERR_UNSUPPORTED,
-            "%s: max_pages * page_size = %ld keys (at most %d supported)", fn, (long)max_pages * page_size, kMaxSeq);
-  } else {
-    REQUIRE(s_max >= 0, ATTN_ERR_INVALID, "%s: negative s_max %d", fn, s_max);
-    REQUIRE(s_max <= kMaxSeq, ATTN_ERR_UNSUPPORTED, "%s: s_max = %d keys (at most %d supported)", fn, s_max, kMaxSeq);
-  }
+  if (int e = check_decode(fn, q, k, v, block_table, max_pages, page_size, num_pages, seq_lens, s_max, B, h, h_kv,
+                           d_h, chunk_keys, max_splits, dtype, scale))
+    return e;
   if (B == 0) return ok();
-  REQUIRE(q && seq_lens && part_o && part_m && part_l, ATTN_ERR_INVALID, "%s: a required pointer is NULL", fn);
-  // Contiguous K/V with s_max = 0 hold no key (every sequence is empty), so
-  // they may be NULL; a paged pool always holds num_pages > 0 pages.
-  REQUIRE((k && v) || (!block_table && s_max == 0), ATTN_ERR_INVALID, "%s: k and v must not be NULL", fn);
-  const int shift = block_table ? log2_exact(page_size) : 0;
-  if (h / h_kv >= kRowsMinGroup && shift >= 0)
-    return from_hip(attn::decode_split_rows(q, k, v, block_table, max_pages, shift, num_pages, seq_lens, s_max, B, h,
-                                            h_kv, chunk_keys, max_splits, dtype, scale, part_o, part_m, part_l,
-                                            static_cast<hipStream_t>(stream)),
-                    fn);
-  return from_hip(attn::decode_split(q, k, v, block_table, max_pages, page_size, num_pages, seq_lens, s_max, B, h,
-                                     h_kv, chunk_keys, max_splits, dtype, scale, part_o, part_m, part_l,
-                                     static_cast<hipStream_t>(stream)),
+  REQUIRE(part_o && part_m && part_l, ATTN_ERR_INVALID, "%s: a required pointer is NULL", fn);
+  return from_hip(launch_split(q, k, v, block_table, max_pages, page_size, num_pages, seq_lens, s_max, B, h, h_kv,
+                               chunk_keys, max_splits, dtype, scale, part_o, part_m, part_l,
+                               static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+int attn_decode(const void* q, const void* k, const void* v, const int32_t* block_table, int max_pages,
+                int page_size, int num_pages, const int32_t* seq_lens, int s_max, int B, int h, int h_kv, int d_h,
+                int chunk_keys, int max_splits, int dtype, float scale, float* part_o, float* part_m,
+                float* part_l, void* o, float* lse, void* stream) {
+  const char* fn = "attn_decode";
+  if (int e = check_decode(fn, q, k, v, block_table, max_pages, page_size, num_pages, seq_lens, s_max, B, h, h_kv,
+                           d_h, chunk_keys, max_splits, dtype, scale))
+    return e;
+  if (B == 0) return ok();
+  REQUIRE(part_o && part_m && part_l && o, ATTN_ERR_INVALID, "%s: a required pointer is NULL", fn);
+  REQUIRE((long)B * h < (1L << 31), ATTN_ERR_UNSUPPORTED, "%s: grid too large", fn);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = launch_split(q, k, v, block_table, max_pages, page_size, num_pages, seq_lens, s_max, B, h,
+                                    h_kv, chunk_keys, max_splits, dtype, scale, part_o, part_m, part_l, s);
+  if (e != hipSuccess) return from_hip(e, fn);
+  return from_hip(attn::merge_states(part_o, part_m, part_l, seq_lens, chunk_keys, B, h, max_splits, o, lse, dtype, s),
                   fn);
 }
 
@@ -306,6 +345,15 @@ int attn_paged_gather(const void* pool, const int32_t* block_table, const int32_
   return from_hip(attn::paged_gather(pool, block_table, seq_lens, B, h_kv, page_size, max_pages, num_pages, s_max,
                                      out, static_cast<hipStream_t>(stream)),
                   fn);
+}
+
+int attn_stream_read(const void* src, uint64_t bytes, int chunks, uint32_t* out, void* stream) {
+  const char* fn = "attn_stream_read";
+  REQUIRE(chunks >= 1 && chunks <= 65536, ATTN_ERR_INVALID, "%s: chunks must be in [1, 65536] (got %d)", fn, chunks);
+  REQUIRE(bytes % 16 == 0, ATTN_ERR_INVALID, "%s: bytes must be a multiple of 16", fn);
+  REQUIRE(src && out, ATTN_ERR_INVALID, "%s: a required pointer is NULL", fn);
+  REQUIRE(((uintptr_t)src & 15) == 0, ATTN_ERR_INVALID, "%s: src must be 16-byte aligned", fn);
+  return from_hip(attn::stream_read(src, bytes, chunks, out, static_cast<hipStream_t>(stream)), fn);
 }
 
 const char* attn_last_error(void) { return g_last_error.c_str(); }

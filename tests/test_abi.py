@@ -125,6 +125,41 @@ def test_decode_split_rejects_before_launch(lib, kw, code):
     assert split_call(lib, **kw) == code
 
 
+def decode_call(lib, **kw):
+    args = dict(q=1, k=1, v=1, bt=NULL, max_pages=0, page_size=16, num_pages=0, sl=1, s_max=64, B=1,
+                h=8, h_kv=1, d=128, chunk=64, splits=1, dtype=1, scale=0.088, po=1, pm=1, pl=1, o=1,
+                lse=NULL)
+    args.update(kw)
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.attn_decode(p(args["q"]), p(args["k"]), p(args["v"]), p(args["bt"]), args["max_pages"],
+                           args["page_size"], args["num_pages"], p(args["sl"]), args["s_max"], args["B"],
+                           args["h"], args["h_kv"], args["d"], args["chunk"], args["splits"], args["dtype"],
+                           args["scale"], p(args["po"]), p(args["pm"]), p(args["pl"]), p(args["o"]),
+                           p(args["lse"]), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(h=514, h_kv=2), 2),
+    (dict(chunk=40), 1),
+    (dict(splits=0), 1),
+    (dict(bt=1, page_size=8, max_pages=4, num_pages=4), 2),
+    (dict(d=96), 2),
+    (dict(dtype=2), 2),
+    (dict(scale=0.0), 1),
+    (dict(o=None), 1),
+    (dict(po=None), 1),
+    (dict(sl=None), 1),
+    (dict(s_max=(1 << 23) + 1), 2),
+])
+def test_decode_rejects_before_launch(lib, kw, code):
+    assert decode_call(lib, **kw) == code
+    assert "attn_decode" in lib.attn_last_error().decode()
+
+
+def test_decode_empty_batch_is_ok_without_launch(lib):
+    assert decode_call(lib, B=0, q=None, k=None, v=None, sl=None, po=None, pm=None, pl=None, o=None) == 0
+
+
 def test_merge_and_gather_reject_before_launch(lib):
     p = ctypes.c_void_p
     assert lib.attn_merge_lse(p(1), p(1), p(1), p(1), -1, 128, p(1), None, 1, None) == 1
@@ -308,3 +343,14 @@ def test_fixed_decode_plan_is_batch_independent(lib):
     assert api.decode_plan_fixed([3000, 20000, 5], 256) == (256, 79)
     with pytest.raises(api.AttnError):
         api.decode_plan_fixed([10], 100)
+
+
+def test_stream_read_rejects_before_launch(lib):
+    p = ctypes.c_void_p
+    assert lib.attn_stream_read(p(16), 64, 0, p(16), None) == 1          # no workgroup
+    assert lib.attn_stream_read(p(16), 64, 65537, p(16), None) == 1
+    assert lib.attn_stream_read(p(16), 60, 4, p(16), None) == 1          # not a multiple of 16 bytes
+    assert lib.attn_stream_read(None, 64, 4, p(16), None) == 1
+    assert lib.attn_stream_read(p(16), 64, 4, None, None) == 1
+    assert lib.attn_stream_read(p(24), 64, 4, p(16), None) == 1          # misaligned source
+    assert "attn_stream_read" in lib.attn_last_error().decode()

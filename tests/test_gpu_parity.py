@@ -310,7 +310,7 @@ def test_merge_many_splits():
 
 # ------------------------------------------------------------------ decode
 
-def run_decode(dec, plan=None):
+def run_decode(dec, plan=None, one_call=True):
     paged = dec["paged"]
     q = to_dev(dec["q"])
     sl = to_dev(dec["seq_lens"])
@@ -320,21 +320,24 @@ def run_decode(dec, plan=None):
     else:
         k, v, bt, ps = to_dev(dec["k"]), to_dev(dec["v"]), None, 16
     o, lse, plan = api.decode(q, k, v, sl, seq_lens_host=dec["seq_lens"], block_table=bt, page_size=ps,
-                              scale=dec["scale"], plan=plan)
+                              scale=dec["scale"], plan=plan, one_call=one_call)
     torch.cuda.synchronize()
     return o, lse.cpu().numpy().astype(np.float64), plan
 
 
+@pytest.mark.parametrize("one_call", [True, False])
 @pytest.mark.parametrize("paged,page_size", [(False, 16), (True, 16), (True, 32)])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-def test_decode_small(paged, page_size, dtype):
+def test_decode_small(paged, page_size, dtype, one_call):
+    # one_call: attn_decode; else attn_decode_split + attn_merge_states
     lens = [1, 5, 16, 17, 63, 64, 65, 300, 1000, 0]
     dec = make_decode(B=len(lens), h=16, h_kv=4, d=128, dtype=dtype, seed=11 + page_size, seq_lens=lens,
                       paged=paged, page_size=page_size, spare_pages=3)
     o_ref, lse_ref = decode_ref(dec["q"], dec["k_seqs"], dec["v_seqs"], dec["seq_lens"], dec["scale"])
-    for plan in (None, (64, 16), (1024, 1), (64, 2)):     # includes last split taking the rest
-        o, lse, used = run_decode(dec, plan)
-        assert_outputs(o, lse, o_ref, lse_ref, dtype, f"decode paged={paged} plan={used}")
+    # includes the last split taking the rest
+    for plan in (None, (64, 16), (1024, 1), (64, 2), (16, 63)):
+        o, lse, used = run_decode(dec, plan, one_call)
+        assert_outputs(o, lse, o_ref, lse_ref, dtype, f"decode paged={paged} plan={used} one_call={one_call}")
 
 
 @pytest.mark.parametrize("h", [8, 64])
@@ -377,41 +380,44 @@ def test_decode_split_partials_match_slices():
 def test_decode_70b_tp8_s32768():
     dec = make_config("decode_70b_tp8_s32768")
     o_ref, lse_ref = decode_ref(dec["q"], dec["k_seqs"], dec["v_seqs"], dec["seq_lens"], dec["scale"])
-    for plan in (None, (32768, 1), (64, 512)):
-        o, lse, used = run_decode(dec, plan)
-        assert_outputs(o, lse, o_ref, lse_ref, "bf16", f"70b-tp8 decode plan={used}")
+    for one_call in (True, False):
+        for plan in (None, (32768, 1), (64, 512), (16, 2048)):
+            o, lse, used = run_decode(dec, plan, one_call)
+            assert_outputs(o, lse, o_ref, lse_ref, "bf16", f"70b-tp8 decode plan={used} one_call={one_call}")
 
 
 def test_decode_llama3_8b_b64_paged(paged_llama):
     dec = paged_llama
     o_ref, lse_ref = decode_ref(dec["q"], dec["k_seqs"], dec["v_seqs"], dec["seq_lens"], dec["scale"])
-    o, lse, used = run_decode(dec)
-    assert_outputs(o, lse, o_ref, lse_ref, "bf16", f"paged decode B=64 plan={used}")
+    for one_call in (True, False):
+        o, lse, used = run_decode(dec, None, one_call)
+        assert_outputs(o, lse, o_ref, lse_ref, "bf16", f"paged decode B=64 plan={used} one_call={one_call}")
 
 
-def test_decode_graph_replay_matches_eager():
-    # split + merge captured in one HIP graph; every replay, with eager work
-    # and synchronisations in between, must reproduce the eager result bit
-    # for bit (same kernels, same inputs).
-    dec = make_decode(B=4, h=16, h_kv=2, d=128, dtype="bf16", seed=21, seq_lens=[7, 640, 2000, 129],
+def test_decode_one_call_graph_replay():
+    # attn_decode (split and merge on the caller's partial buffers) captured
+    # in a HIP graph: every replay, with eager calls and synchronisations
+    # between, reproduces the eager bits
+    dec = make_decode(B=4, h=8, h_kv=2, d=128, dtype="bf16", seed=27, seq_lens=[7, 6000, 2000, 129],
                       paged=True, page_size=16)
     q, sl = to_dev(dec["q"]), to_dev(dec["seq_lens"])
     kp, vp, bt = to_dev(dec["k_pool"]), to_dev(dec["v_pool"]), to_dev(dec["block_table"])
-    chunk, splits = api.decode_plan(dec["seq_lens"], 16, 2)
-    po = torch.empty((4, 16, splits, 128), dtype=torch.float32, device=DEV)
-    pm = torch.empty((4, 16, splits), dtype=torch.float32, device=DEV)
+    chunk, splits = 64, 94
+    po = torch.empty((4, 8, splits, 128), dtype=torch.float32, device=DEV)
+    pm = torch.empty((4, 8, splits), dtype=torch.float32, device=DEV)
     pl = torch.empty_like(pm)
-    o = torch.empty((4, 16, 128), dtype=torch.bfloat16, device=DEV)
-    lse = torch.empty((4, 16), dtype=torch.float32, device=DEV)
+    o = torch.empty((4, 8, 128), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((4, 8), dtype=torch.float32, device=DEV)
 
     def step():
-        api.decode_split(q, kp, vp, sl, chunk, splits, block_table=bt, scale=dec["scale"],
-                         part_o=po, part_m=pm, part_l=pl)
-        api.merge_states(po, pm, pl, sl, chunk, torch.bfloat16, out=o, lse=lse)
+        api.decode_call(q, kp, vp, sl, chunk, splits, block_table=bt, scale=dec["scale"], part_o=po, part_m=pm,
+                        part_l=pl, out=o, lse=lse)
 
     step()
     torch.cuda.synchronize()
     o_eager, lse_eager = o.clone(), lse.clone()
+    o_ref, lse_ref = decode_ref(dec["q"], dec["k_seqs"], dec["v_seqs"], dec["seq_lens"], dec["scale"])
+    assert_outputs(o, lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16", "attn_decode, eager")
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -429,69 +435,8 @@ def test_decode_graph_replay_matches_eager():
         torch.cuda.synchronize()
         assert torch.equal(o.view(torch.int16), o_eager.view(torch.int16)), rep
         assert torch.equal(lse, lse_eager), rep
-        step()                              # eager work between replays
-        torch.cuda.synchronize()
-    o_ref, lse_ref = decode_ref(dec["q"], dec["k_seqs"], dec["v_seqs"], dec["seq_lens"], dec["scale"])
-    assert_outputs(o, lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16", "graph decode")
-
-
-def test_prefill_and_row_decode_graph_replay_matches_eager():
-    # key-masked prefill (tile list), paged prefill (launch order in the
-    # kernel arguments) and a 64-head-group decode (the row form, with its
-    # prefetching waves) captured in one HIP graph; every replay, with eager
-    # work and synchronisations between replays, reproduces the eager bits
-    from online_softmax_tiled_amd.workloads import make_chunked_prefill
-    inp = make_prefill(1, 8, 2, 200, 200, 128, "bf16", seed=23, causal=True, key_tile_p=0.3)
-    q, k, v, km = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"]), to_dev(inp["key_mask"])
-    o1 = torch.empty_like(q)
-    l1 = torch.empty((1, 8, 200), dtype=torch.float32, device=DEV)
-    c = make_chunked_prefill(3, 8, 2, 128, "bf16", seed=24, ctx_range=(100, 400), new_range=(10, 90))
-    cq, cu, kp, vp = to_dev(c["q"]), to_dev(c["cu_seqlens_q"]), to_dev(c["k_pool"]), to_dev(c["v_pool"])
-    bt, slk = to_dev(c["block_table"]), to_dev(c["seq_lens_k"])
-    o2 = torch.empty_like(cq)
-    l2 = torch.empty(cq.shape[:2], dtype=torch.float32, device=DEV)
-    dec = make_decode(B=2, h=64, h_kv=1, d=128, dtype="bf16", seed=25, seq_lens=[300, 1100], paged=False)
-    dq, dk, dv, dsl = to_dev(dec["q"]), to_dev(dec["k"]), to_dev(dec["v"]), to_dev(dec["seq_lens"])
-    chunk, splits = api.decode_plan(dec["seq_lens"], 64, 1)
-    po = torch.empty((2, 64, splits, 128), dtype=torch.float32, device=DEV)
-    pm = torch.empty((2, 64, splits), dtype=torch.float32, device=DEV)
-    pl = torch.empty_like(pm)
-    o3 = torch.empty((2, 64, 128), dtype=torch.bfloat16, device=DEV)
-    l3 = torch.empty((2, 64), dtype=torch.float32, device=DEV)
-    outs = (o1, l1, o2, l2, o3, l3)
-
-    def step():
-        api.prefill(q, k, v, causal=True, scale=inp["scale"], key_mask=km, out=o1, lse=l1)
-        api.prefill_paged(cq, cu, c["max_q"], kp, vp, bt, slk, causal=True, scale=c["scale"], out=o2, lse=l2,
-                          seq_lens_k_host=c["seq_lens_k"])
-        api.decode_split(dq, dk, dv, dsl, chunk, splits, scale=dec["scale"], part_o=po, part_m=pm, part_l=pl)
-        api.merge_states(po, pm, pl, dsl, chunk, torch.bfloat16, out=o3, lse=l3)
-
-    step()
-    torch.cuda.synchronize()
-    eager = [t.clone() for t in outs]
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
         step()
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        step()
-    for rep in range(4):
-        for t in outs:
-            t.fill_(3.0)
         torch.cuda.synchronize()
-        graph.replay()
-        torch.cuda.synchronize()
-        for t, e in zip(outs, eager):
-            assert torch.equal(t.view(torch.int16) if t.dtype == torch.bfloat16 else t,
-                               e.view(torch.int16) if e.dtype == torch.bfloat16 else e), rep
-        step()                              # eager work between replays
-        torch.cuda.synchronize()
-    o_ref, lse_ref = decode_ref(dec["q"], dec["k_seqs"], dec["v_seqs"], dec["seq_lens"], dec["scale"])
-    assert_outputs(o3, l3.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16", "graph row-form decode")
 
 
 # ------------------------------------------------------------------ (O, LSE) merge
@@ -722,9 +667,9 @@ def test_paged_prefill_matches_contiguous_prefill():
 
 # ------------------------------------------------------------------ batch-invariant decode
 
-@pytest.mark.parametrize("h", [8, 64])
+@pytest.mark.parametrize("h,one_call", [(8, True), (8, False), (64, True)])
 @pytest.mark.parametrize("paged", [False, True])
-def test_decode_batch_invariant_with_fixed_split(paged, h):
+def test_decode_batch_invariant_with_fixed_split(paged, h, one_call):
     # One sequence decoded alone and inside a batch whose longest sequence
     # needs >= 64 splits (the merge then runs its 4-slice layout): with the
     # same fixed split length its output bits are identical, for 8 heads per
@@ -750,9 +695,11 @@ def test_decode_batch_invariant_with_fixed_split(paged, h):
         plan = api.decode_plan_fixed(c["seq_lens"], split)
         if paged:
             o, lse, _ = api.decode(to_dev(c["q"]), to_dev(c["k_pool"]), to_dev(c["v_pool"]), sl,
-                                   block_table=to_dev(c["block_table"]), page_size=16, scale=c["scale"], plan=plan)
+                                   block_table=to_dev(c["block_table"]), page_size=16, scale=c["scale"], plan=plan,
+                                   one_call=one_call)
         else:
-            o, lse, _ = api.decode(to_dev(c["q"]), to_dev(c["k"]), to_dev(c["v"]), sl, scale=c["scale"], plan=plan)
+            o, lse, _ = api.decode(to_dev(c["q"]), to_dev(c["k"]), to_dev(c["v"]), sl, scale=c["scale"], plan=plan,
+                                   one_call=one_call)
         torch.cuda.synchronize()
         return o, lse, plan
 
@@ -973,3 +920,21 @@ def test_bf16_values_beyond_fp16_range_take_the_bf16_pass():
     o_ref, lse_ref = decode_ref(dec["q"], dec["k_seqs"], dec["v_seqs"], dec["seq_lens"], dec["scale"])
     o, lse, used = run_decode(dec)
     _check_big_column(o, lse, o_ref, lse_ref, 100, "row-form decode with V = -2^17")
+
+
+def test_stream_read_reads_every_word_once():
+    # the read-rate calibration kernel: chunk c's output is the xor of the
+    # 32-bit words of its contiguous chunk (bit for bit), for sizes that do
+    # and do not divide into the chunks
+    for n_words, chunks in ((1 << 20, 1024), (4 * 1001, 7), (4 * 3, 5)):
+        g = torch.Generator().manual_seed(n_words)
+        src = torch.randint(-2 ** 31, 2 ** 31 - 1, (n_words,), generator=g, dtype=torch.int64).to(torch.int32)
+        out = api.stream_read(to_dev(src), chunks=chunks)
+        torch.cuda.synchronize()
+        words = src.numpy().view(np.uint32)
+        per16 = -(-(n_words // 4) // chunks)                  # 16-byte units per chunk
+        want = np.zeros(chunks, dtype=np.uint32)
+        for c in range(chunks):
+            part = words[c * per16 * 4:(c + 1) * per16 * 4]
+            want[c] = np.bitwise_xor.reduce(part) if part.size else 0
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), want)

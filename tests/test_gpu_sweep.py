@@ -75,6 +75,8 @@ def test_decode_random(case):
         need = max(1, -(-int(lens.max()) // chunk))
         plan = (chunk, int(rng.integers(max(1, need // 2), need + 1)))   # fewer splits: the last takes the rest
     o_ref, lse_ref = decode_ref(dec["q"], dec["k_seqs"], dec["v_seqs"], dec["seq_lens"], dec["scale"])
-    o, lse, used = run_decode(dec, plan)
+    one_call = bool(np.random.default_rng(9500 + case).integers(2))    # attn_decode, or split + merge
+    o, lse, used = run_decode(dec, plan, one_call)
     assert_outputs(o, lse, o_ref, lse_ref, dtype,
-                   f"random decode {case}: h={h_kv * g}/{h_kv} paged={paged} P={page} lens={lens.tolist()} plan={used}")
+                   f"random decode {case}: h={h_kv * g}/{h_kv} paged={paged} P={page} lens={lens.tolist()} plan={used} "
+                   f"one_call={one_call}")
