@@ -262,6 +262,30 @@ int attn_decode(const void* q, const void* k, const void* v,
                 void* o, float* lse, void* stream);
 
 /*
+ * attn_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops that forbid allocation): the same two
+ * stages and results, with the split-KV partial states kept in a scratch
+ * array of device memory that the library owns -- 32 MiB, one per GPU,
+ * held from the first call on that GPU until the process ends. The call
+ * itself allocates nothing. The caller still passes the inputs and o / lse.
+ *
+ *   Arguments as attn_decode, without part_o / part_m / part_l.
+ *   B * h * max_splits * (d_h + 2) * 4 bytes of partial states must fit in
+ *   the 32 MiB (e.g. B * h * max_splits <= 64528 for d_h = 128); larger
+ *   problems return ATTN_ERR_UNSUPPORTED before anything is launched.
+ * Nothing in the scratch needs to start at zero: stage 1 writes every state
+ * the merge uses. All calls on one GPU share its scratch: calls that overlap
+ * in time on one GPU (different streams, host threads or processes' graphs
+ * replayed concurrently) race on it and must be serialised by the caller.
+ */
+int attn_decode_noalloc(const void* q, const void* k, const void* v,
+                        const int32_t* block_table, int max_pages, int page_size, int num_pages,
+                        const int32_t* seq_lens, int s_max,
+                        int B, int h, int h_kv, int d_h,
+                        int chunk_keys, int max_splits, int dtype, float scale,
+                        void* o, float* lse, void* stream);
+
+/*
  * Two-operand merge in (O, LSE) form: the output over the union of two
  * disjoint key ranges of the same query rows, from each range's normalised
  * output and LSE (a cascade's shared prefix and per-request suffix, or two

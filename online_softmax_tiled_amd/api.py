@@ -32,6 +32,7 @@ _SIGNATURES = {
                          + [_c_void_p] * 4,
     "attn_merge_states": [_c_void_p] * 4 + [_c_int] * 5 + [_c_void_p, _c_void_p, _c_int, _c_void_p],
     "attn_decode": [_c_void_p] * 4 + [_c_int] * 3 + [_c_void_p] + [_c_int] * 8 + [_c_float] + [_c_void_p] * 6,
+    "attn_decode_noalloc": [_c_void_p] * 4 + [_c_int] * 3 + [_c_void_p] + [_c_int] * 8 + [_c_float] + [_c_void_p] * 3,
     "attn_merge_lse": [_c_void_p] * 4 + [_c_int] * 2 + [_c_void_p, _c_void_p, _c_int, _c_void_p],
     "attn_paged_gather": [_c_void_p] * 3 + [_c_int] * 8 + [_c_void_p, _c_void_p],
     "attn_stream_read": [_c_void_p, ctypes.c_uint64, _c_int, _c_void_p, _c_void_p],
@@ -311,6 +312,29 @@ def decode_call(q, k, v, seq_lens, chunk_keys, max_splits, block_table=None, pag
         _ptr(q), _ptr(k), _ptr(v), _ptr(block_table), max_pages, page_size, num_pages,
         _ptr(seq_lens), s_max, B, h, h_kv, d, int(chunk_keys), int(max_splits), _dtype_code(q),
         scale, _ptr(part_o), _ptr(part_m), _ptr(part_l), _ptr(out), _ptr(lse), _stream(dev)))
+    return out, lse
+
+
+def decode_noalloc(q, k, v, seq_lens, chunk_keys, max_splits, block_table=None, page_size=16, scale=None,
+                   out=None, lse=None):
+    """Both decode stages via attn_decode_noalloc: the partial states live in
+    the library's per-GPU device scratch (the call allocates nothing; ``out``
+    and ``lse`` are allocated here only when not given). Returns (o, lse)."""
+    lib = load()
+    _want(q, "q")
+    dev, dt = q.device, q.dtype
+    B, h, d = q.shape
+    _want(seq_lens, "seq_lens", torch.int32, (B,), dev)
+    h_kv, s_max, max_pages, num_pages, page_size = _kv_geometry(q, k, v, block_table, page_size)
+    out = torch.empty((B, h, d), dtype=dt, device=dev) if out is None else out
+    _want(out, "out", dt, (B, h, d), dev)
+    lse = torch.empty((B, h), dtype=torch.float32, device=dev) if lse is None else lse
+    _want(lse, "lse", torch.float32, (B, h), dev)
+    scale = float(np.float32(1.0 / np.sqrt(d))) if scale is None else float(scale)
+    _check("attn_decode_noalloc", lib.attn_decode_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(block_table), max_pages, page_size, num_pages,
+        _ptr(seq_lens), s_max, B, h, h_kv, d, int(chunk_keys), int(max_splits), _dtype_code(q),
+        scale, _ptr(out), _ptr(lse), _stream(dev)))
     return out, lse
 
 

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libattn.so")
 
-SOURCES = ["api.cpp", "prefill.hip", "decode.hip", "merge.hip", "merge_lse.hip", "gather.hip", "stream.hip"]
+SOURCES = ["api.cpp", "prefill.hip", "decode.hip", "merge.hip", "merge_lse.hip", "gather.hip", "stream.hip", "noalloc.hip"]
 # Per-source extra flags. The prefill kernel never compares against NaN and
 # treats no NaN operand specially, so NaN-quieting of fmax inputs is not
 # needed (it costs a v_max per score); infinities keep their IEEE meaning.

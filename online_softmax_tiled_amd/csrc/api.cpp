@@ -45,6 +45,8 @@ hipError_t merge_lse(const void* o_a, const float* lse_a, const void* o_b, const
 int decode_plan(int B, const int32_t* seq_lens, int units_per_split, int wgs_per_cu, int num_cus, int32_t* chunk_keys,
                 int32_t* max_splits);
 hipError_t stream_read(const void* src, uint64_t bytes, int chunks, uint32_t* out, hipStream_t stream);
+size_t decode_scratch_bytes();
+hipError_t decode_scratch(void** ptr);
 }  // namespace attn
 
 namespace {
@@ -294,6 +296,37 @@ int attn_decode(const void* q, const void* k, const void* v, const int32_t* bloc
   if (B == 0) return ok();
   REQUIRE(part_o && part_m && part_l && o, ATTN_ERR_INVALID, "%s: a required pointer is NULL", fn);
   REQUIRE((long)B * h < (1L << 31), ATTN_ERR_UNSUPPORTED, "%s: grid too large", fn);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = launch_split(q, k, v, block_table, max_pages, page_size, num_pages, seq_lens, s_max, B, h,
+                                    h_kv, chunk_keys, max_splits, dtype, scale, part_o, part_m, part_l, s);
+  if (e != hipSuccess) return from_hip(e, fn);
+  return from_hip(attn::merge_states(part_o, part_m, part_l, seq_lens, chunk_keys, B, h, max_splits, o, lse, dtype, s),
+                  fn);
+}
+
+int attn_decode_noalloc(const void* q, const void* k, const void* v, const int32_t* block_table, int max_pages,
+                        int page_size, int num_pages, const int32_t* seq_lens, int s_max, int B, int h, int h_kv,
+                        int d_h, int chunk_keys, int max_splits, int dtype, float scale, void* o, float* lse,
+                        void* stream) {
+  const char* fn = "attn_decode_noalloc";
+  if (int e = check_decode(fn, q, k, v, block_table, max_pages, page_size, num_pages, seq_lens, s_max, B, h, h_kv,
+                           d_h, chunk_keys, max_splits, dtype, scale))
+    return e;
+  if (B == 0) return ok();
+  REQUIRE(o, ATTN_ERR_INVALID, "%s: a required pointer is NULL", fn);
+  REQUIRE((long)B * h < (1L << 31), ATTN_ERR_UNSUPPORTED, "%s: grid too large", fn);
+  // partial states: part_o [B, h, S, d], then part_m and part_l [B, h, S]
+  const size_t rows = (size_t)B * h * max_splits;
+  const size_t need = rows * (kHeadDim + 2) * sizeof(float);
+  REQUIRE(need <= attn::decode_scratch_bytes(), ATTN_ERR_UNSUPPORTED,
+          "%s: B * h * max_splits = %zu partial states need %zu bytes; the device scratch holds %zu", fn, rows, need,
+          attn::decode_scratch_bytes());
+  void* base = nullptr;
+  const hipError_t es = attn::decode_scratch(&base);
+  if (es != hipSuccess) return from_hip(es, fn);
+  float* part_o = static_cast<float*>(base);
+  float* part_m = part_o + rows * kHeadDim;
+  float* part_l = part_m + rows;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = launch_split(q, k, v, block_table, max_pages, page_size, num_pages, seq_lens, s_max, B, h,
                                     h_kv, chunk_keys, max_splits, dtype, scale, part_o, part_m, part_l, s);
