@@ -450,6 +450,9 @@ def run_only(args, dev):
     elif args.only == "stress":
         r = bench_prefill("stress_prefill_t4096", args.steps, args.warmup, dev)
         print(json.dumps({"workload": "stress_prefill_t4096", "ms": r["ms"], "tflops": r["tflops"]}))
+    elif args.only == "chunked":
+        r = bench_chunked_prefill(args.steps, args.warmup, dev)
+        print(json.dumps({"workload": "chunked_prefill_llama3_8b_b8", "ms": r["ms"], "tflops": r["tflops"]}))
     elif args.only == "decode_70b":
         r = bench_decode_contiguous(args.steps, args.warmup, dev)
         print(json.dumps(r))
@@ -476,8 +479,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="only the headline prefill")
-    ap.add_argument("--only", choices=["prefill", "stress", "decode_70b", "decode_paged", "decode_g128", "merge_lse",
-                                       "copy"],
+    ap.add_argument("--only", choices=["prefill", "stress", "chunked", "decode_70b", "decode_paged", "decode_g128",
+                                       "merge_lse", "copy"],
                     default=None,
                     help="run one workload only (for profiler counter runs) and print its timing")
     ap.add_argument("--copy-mb", type=int, default=1024,
