@@ -108,9 +108,32 @@ __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t 
 __device__ __forceinline__ uint32_t pack_lo16(uint32_t a, uint32_t b) { return perm_b32(b, a, 0x05040100u); }
 __device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) { return perm_b32(b, a, 0x07060302u); }
 
-// Max / sum of x over lanes l and l ^ 32 (the two halves of a wave64).
-__device__ __forceinline__ float max_halves(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
-__device__ __forceinline__ float sum_halves(float x) { return x + __shfl_xor(x, 32); }
+// The values of x on lanes l % 32 and l % 32 + 32, on every lane l: gfx950's
+// v_permlane32_swap exchanges the upper 32 lanes of its first operand with
+// the lower 32 lanes of its second, a vector-ALU exchange with no LDS round
+// trip. Written as assembly with both operands read-write: with the compiler
+// builtin and the same value in both operands, this compiler folds a
+// combination of the two results into the first result alone (a kernel
+// returning their sum emits v_add_f32 v1, v1, v1). The s_nop gives the two
+// wait states between a vector write of an operand and the swap reading it.
+__device__ __forceinline__ void swap_halves(float x, float& lo, float& hi) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  lo = __builtin_bit_cast(float, a);
+  hi = __builtin_bit_cast(float, b);
+}
+// Max / sum of x over lanes l and l ^ 32 (the two halves of a wave64); both
+// lanes of a pair get the same bits (the lower lane's value first).
+__device__ __forceinline__ float max_halves(float x) {
+  float lo, hi;
+  swap_halves(x, lo, hi);
+  return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  float lo, hi;
+  swap_halves(x, lo, hi);
+  return lo + hi;
+}
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 // Streaming load: non-temporal hint, for data read exactly once (decode K/V),

@@ -223,6 +223,29 @@ def test_prefill_causal_single_key_row_is_exact():
         assert torch.equal(o[0, i, 0].cpu(), inp["v"][0, i // 4, 0])
 
 
+@pytest.mark.parametrize("upper", [False, True])
+def test_prefill_row_max_on_either_half_wave(upper):
+    # In the kernel's transposed score layout a row's scores are split
+    # between two lanes of a wave: keys 0-3 of every aligned group of 8 on
+    # one, keys 4-7 on the other. Here each row has two dominant keys (18
+    # log2 units above the rest) at offsets of one kind only, so the row
+    # maximum and the final sums must cross between the lanes: a half that
+    # kept its own maximum would hold its sums at another reference.
+    T, h, h_kv, d = 256, 4, 1, 128
+    inp = make_prefill(1, h, h_kv, T, T, d, "bf16", seed=77 + upper, causal=False, qk_std=0.05)
+    q, k = inp["q"].clone(), inp["k"].clone()
+    for p in range(T):
+        k[0, 0, p, p % d] = 12.0                 # key p points along e_(p mod 128)
+    off = 4 if upper else 0
+    for j in range(h):
+        for i in range(T):
+            p = 8 * ((i + 5 * j) % 16) + off + (i % 4)   # p % 8 in the chosen half; p + 128 shares e_p
+            q[0, j, i, p] = 12.0
+    inp = dict(inp, q=q, k=k)
+    o, lse, o_ref, lse_ref = run_prefill(inp)
+    assert_outputs(o, lse, o_ref, lse_ref, "bf16", f"dominant keys on the {'upper' if upper else 'lower'} lanes")
+
+
 # ------------------------------------------------------------------ gather
 
 @pytest.mark.parametrize("page_size,spare", [(16, 0), (16, 5), (32, 3), (48, 1)])
