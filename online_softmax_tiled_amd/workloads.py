@@ -105,8 +105,24 @@ def make_prefill(B, h, h_kv, T_q, T_k, d, dtype, seed, causal=True, qk_std=None,
                 B=B, h=h, h_kv=h_kv, T_q=T_q, T_k=T_k, d=d)
 
 
+def _e4m3_codes(rng, shape):
+    """Random 8-bit E4M3 codes (uint8, OCP layout: sign, 4 exponent bits, 3
+    mantissa bits) with the sign and the mantissa uniform and the exponent
+    field uniform in 4..9 (magnitudes in [2^-3, 2^3)); never a NaN code.
+    One integer in [0, 96) per element, in C order."""
+    out = torch.empty(shape, dtype=torch.uint8)
+    flat = out.view(-1)
+    n = flat.numel()
+    for lo in range(0, n, _CHUNK):
+        hi = min(n, lo + _CHUNK)
+        r = rng.integers(0, 96, size=hi - lo, dtype=np.int64)
+        codes = ((r // 48) << 7) | ((4 + (r % 48) // 8) << 3) | (r % 8)
+        flat[lo:hi] = torch.from_numpy(codes.astype(np.uint8))
+    return out
+
+
 def make_decode(B, h, h_kv, d, dtype, seed, seq_lens=None, len_range=None, paged=False,
-                page_size=16, spare_pages=0, poison=True):
+                page_size=16, spare_pages=0, poison=True, kv_codes=False):
     """Decode inputs: one query token per sequence, q [B,h,d].
 
     Lengths: ``seq_lens`` (list) or drawn uniformly from ``len_range``
@@ -120,6 +136,8 @@ def make_decode(B, h, h_kv, d, dtype, seed, seq_lens=None, len_range=None, paged
     sequences need + ``spare_pages``.
     Always: k_seqs / v_seqs, per-sequence views [h_kv, s_b, d] of the drawn
     (ground-truth) keys and values.
+    kv_codes: K and V are 8-bit E4M3 codes (uint8, see ``_e4m3_codes``)
+    instead of ``dtype`` values, and the poison is the NaN code 0x7F.
     """
     rv, ri = _streams(seed)
     if seq_lens is None:
@@ -128,19 +146,24 @@ def make_decode(B, h, h_kv, d, dtype, seed, seq_lens=None, len_range=None, paged
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
     q = _normal(rv, (B, h, d), dtype)
     total = int(seq_lens.sum())
-    k_tok = _normal(rv, (total, h_kv, d), dtype)
-    v_tok = _normal(rv, (total, h_kv, d), dtype)
+    if kv_codes:
+        k_tok = _e4m3_codes(rv, (total, h_kv, d))
+        v_tok = _e4m3_codes(rv, (total, h_kv, d))
+    else:
+        k_tok = _normal(rv, (total, h_kv, d), dtype)
+        v_tok = _normal(rv, (total, h_kv, d), dtype)
+    kv_dtype = torch.uint8 if kv_codes else DTYPES[dtype]
     offs = np.concatenate([[0], np.cumsum(seq_lens.astype(np.int64))])
     k_seqs = [k_tok[offs[b]:offs[b + 1]].permute(1, 0, 2) for b in range(B)]
     v_seqs = [v_tok[offs[b]:offs[b + 1]].permute(1, 0, 2) for b in range(B)]
     out = dict(kind="decode", q=q, k_seqs=k_seqs, v_seqs=v_seqs, seq_lens=seq_lens,
                scale=default_scale(d), dtype=dtype, B=B, h=h, h_kv=h_kv, d=d,
-               paged=bool(paged))
-    fill = float("nan") if poison else 0.0
+               paged=bool(paged), kv_codes=bool(kv_codes))
+    fill = (0x7F if kv_codes else float("nan")) if poison else 0
     if not paged:
         s_max = int(seq_lens.max()) if B else 0
-        k = torch.full((B, h_kv, s_max, d), fill, dtype=DTYPES[dtype])
-        v = torch.full((B, h_kv, s_max, d), fill, dtype=DTYPES[dtype])
+        k = torch.full((B, h_kv, s_max, d), fill, dtype=kv_dtype)
+        v = torch.full((B, h_kv, s_max, d), fill, dtype=kv_dtype)
         for b in range(B):
             k[b, :, :seq_lens[b]] = k_seqs[b]
             v[b, :, :seq_lens[b]] = v_seqs[b]
@@ -161,8 +184,8 @@ def make_decode(B, h, h_kv, d, dtype, seed, seq_lens=None, len_range=None, paged
         t = np.arange(seq_lens[b], dtype=np.int64)
         rows[offs[b]:offs[b + 1]] = bt[b, t // page_size].astype(np.int64) * page_size + t % page_size
     rows_t = torch.from_numpy(rows)
-    k_pool = torch.full((n_pages, page_size, h_kv, d), fill, dtype=DTYPES[dtype])
-    v_pool = torch.full((n_pages, page_size, h_kv, d), fill, dtype=DTYPES[dtype])
+    k_pool = torch.full((n_pages, page_size, h_kv, d), fill, dtype=kv_dtype)
+    v_pool = torch.full((n_pages, page_size, h_kv, d), fill, dtype=kv_dtype)
     k_pool.view(-1, h_kv, d)[rows_t] = k_tok
     v_pool.view(-1, h_kv, d)[rows_t] = v_tok
     out.update(k_pool=k_pool, v_pool=v_pool, block_table=bt, page_size=page_size,

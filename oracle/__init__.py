@@ -32,6 +32,9 @@ Modules:
   two-operand merge in (O, LSE) form.
 * :mod:`oracle.brute` -- pure-Python loops (``math.exp``/``math.fsum``) for
   tiny inputs, used only to pin the materialised oracle.
+* :mod:`oracle.fp8` -- the values of 8-bit E4M3 K/V codes (OCP format) with
+  their per-tensor scales, so that fp8-KV decode is checked as the float64
+  decode of those values.
 
 Every function here is pinned by ``-m "not gpu"`` tests against values the
 pages print, closed forms, invariants, or brute force (``tests/test_oracle*``).
@@ -49,8 +52,12 @@ from .state import (
     merge_lse_ref,
 )
 from .brute import brute_attention
+from .fp8 import e4m3_decode, e4m3_value, E4M3_VALUES
 
 __all__ = [
+    "e4m3_decode",
+    "e4m3_value",
+    "E4M3_VALUES",
     "attention_ref",
     "decode_ref",
     "paged_gather_ref",
