@@ -336,6 +336,52 @@ def bench_decode_contiguous(steps, warmup, dev, copies=40):
                        "over the same 16.8 MB of K/V (1024 contiguous chunks); launch_floor = one 64-byte fill kernel")
 
 
+def bench_decode_fp8kv(steps, warmup, dev, name, copies=1, scales=(0.37, 0.29)):
+    """Split-KV decode over 8-bit E4M3 K/V (attn_decode_fp8kv, split then
+    merge) on a named decode workload with its K/V drawn as E4M3 codes. KV
+    bytes = one byte per element. ``copies`` > 1 rotates that many K/V copies
+    and times a HIP graph of the steps (batch-1 shape); else eager launches."""
+    import torch
+    from online_softmax_tiled_amd import api
+    from online_softmax_tiled_amd.workloads import make_config
+    dec = make_config(name, kv_codes=True)
+    q = dec["q"].to(dev)
+    sl = torch.from_numpy(dec["seq_lens"]).to(dev)
+    B, h, d = q.shape
+    paged = dec["paged"]
+    if paged:
+        kvs = [(dec["k_pool"].to(dev), dec["v_pool"].to(dev))]
+        bt = torch.from_numpy(dec["block_table"]).to(dev)
+        h_kv, ps = kvs[0][0].shape[2], dec["page_size"]
+    else:
+        k0, v0 = dec["k"].to(dev), dec["v"].to(dev)
+        kvs = [(k0.clone(), v0.clone()) for _ in range(copies)]
+        del k0, v0
+        bt, h_kv, ps = None, dec["k"].shape[1], 16
+    chunk, splits = api.decode_plan(dec["seq_lens"], h, h_kv, device=dev)
+    po = torch.empty((B, h, splits, d), dtype=torch.float32, device=dev)
+    pm = torch.empty((B, h, splits), dtype=torch.float32, device=dev)
+    pl = torch.empty_like(pm)
+    o = torch.empty((B, h, d), dtype=q.dtype, device=dev)
+    lse = torch.empty((B, h), dtype=torch.float32, device=dev)
+    kv_bytes = 2 * int(dec["seq_lens"].sum()) * h_kv * d
+
+    def full(i=0):
+        k, v = kvs[i % len(kvs)]
+        api.decode_fp8kv_call(q, k, v, sl, chunk, splits, scales[0], scales[1], block_table=bt, page_size=ps,
+                              scale=dec["scale"], part_o=po, part_m=pm, part_l=pl, out=o, lse=lse)
+
+    if copies > 1:
+        ms = time_graph(full, copies * 5)
+        timing = f"HIP graph of attn_decode_fp8kv steps over {copies} rotated K/V copies"
+    else:
+        ms, _ = time_loop(full, steps, warmup)
+        timing = "eager attn_decode_fp8kv steps"
+    return dict(kv_bytes=kv_bytes, kv_format="E4M3 bytes, per-tensor fp32 scales", us_per_step=ms * 1e3,
+                gbs=kv_bytes / (ms * 1e-3) / 1e9, frac_hbm=kv_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                plan=[chunk, splits], timing=timing)
+
+
 def bench_decode_paged(steps, warmup, dev, dec, fixed_split=None, gather=True):
     """Paged split-KV decode on the 64-sequence workload, with the adaptive
     plan or (``fixed_split``) a batch-invariant fixed split length."""
@@ -453,6 +499,9 @@ def run_only(args, dev):
     elif args.only == "chunked":
         r = bench_chunked_prefill(args.steps, args.warmup, dev)
         print(json.dumps({"workload": "chunked_prefill_llama3_8b_b8", "ms": r["ms"], "tflops": r["tflops"]}))
+    elif args.only == "decode_fp8":
+        r = bench_decode_fp8kv(args.steps, args.warmup, dev, "paged_decode_llama3_8b_b64")
+        print(json.dumps(r))
     elif args.only == "decode_70b":
         r = bench_decode_contiguous(args.steps, args.warmup, dev)
         print(json.dumps(r))
@@ -480,7 +529,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="only the headline prefill")
     ap.add_argument("--only", choices=["prefill", "stress", "chunked", "decode_70b", "decode_paged", "decode_g128",
-                                       "merge_lse", "copy"],
+                                       "decode_fp8", "merge_lse", "copy"],
                     default=None,
                     help="run one workload only (for profiler counter runs) and print its timing")
     ap.add_argument("--copy-mb", type=int, default=1024,
@@ -557,6 +606,12 @@ def main():
         r7 = bench_decode_large_group(max(20, args.steps), 3, dev, paged=True)
         log(f"decode g=128 b32 s32768 paged: {r7['us_per_step']:.1f} us/step, {r7['gbs']:.0f} GB/s, plan {r7['plan']}")
         decode["decode_g128_b32_s32768_paged"] = r7
+        r8 = bench_decode_fp8kv(max(200, args.steps), 20, dev, "decode_70b_tp8_s32768", copies=40)
+        log(f"decode 70b tp8 fp8 KV: {r8['us_per_step']:.2f} us/step, {r8['gbs']:.0f} GB/s")
+        decode["decode_70b_tp8_s32768_fp8kv"] = r8
+        r9 = bench_decode_fp8kv(max(20, args.steps), 3, dev, "paged_decode_llama3_8b_b64")
+        log(f"decode paged b64 fp8 KV: {r9['us_per_step']:.1f} us/step, {r9['gbs']:.0f} GB/s")
+        decode["paged_decode_llama3_8b_b64_fp8kv"] = r9
         for v in decode.values():
             for key in list(v):
                 if isinstance(v[key], float):

@@ -262,6 +262,52 @@ int attn_decode(const void* q, const void* k, const void* v,
                 void* o, float* lse, void* stream);
 
 /*
+ * Split-KV decode over 8-bit K/V: K and V hold one OCP E4M3 byte per
+ * element (sign, 4 exponent bits with bias 7, 3 mantissa bits; the codes
+ * 0x7F and 0xFF are NaN), and each tensor has one fp32 scale: the key and
+ * value with codes c stand for e4m3(c) * k_scale and e4m3(c) * v_scale.
+ * [OR] section "Where it breaks" (with FP8 K and V the statistics m and l
+ * stay fp32); the byte format and the per-tensor scales are this library's
+ * choice, the pages fixing none. The products run on the query's 16-bit
+ * type (every E4M3 value is exact in fp16 and bf16), the statistics and the
+ * partial states in fp32, as attn_decode_split.
+ *
+ *   q            [B, h, d_h] dtype (ATTN_DTYPE_F16 or ATTN_DTYPE_BF16).
+ *   k, v         uint8 codes: contiguous [B, h_kv, s_max, d_h]
+ *                (block_table == NULL) or paged pools
+ *                [num_pages, page_size, h_kv, d_h]; addressed as in
+ *                attn_decode_split with one byte per element.
+ *   k_scale, v_scale  finite and > 0 (else ATTN_ERR_INVALID).
+ * Everything else (sizes, plans, partial buffers, the written splits,
+ * errors) as attn_decode_split; the partials merge with attn_merge_states.
+ * Up to 256 query heads per KV head, in blocks of 16; page sizes any
+ * multiple of 16.
+ */
+int attn_decode_split_fp8kv(const void* q, const void* k, const void* v,
+                            const int32_t* block_table, int max_pages, int page_size, int num_pages,
+                            const int32_t* seq_lens, int s_max,
+                            int B, int h, int h_kv, int d_h,
+                            int chunk_keys, int max_splits, int dtype, float scale,
+                            float k_scale, float v_scale,
+                            float* part_o, float* part_m, float* part_l, void* stream);
+
+/*
+ * Both decode stages over 8-bit K/V in one call: attn_decode_split_fp8kv
+ * into the caller's partial buffers, then attn_merge_states, on `stream`
+ * (as attn_decode does for 16-bit K/V).
+ *   o            [B, h, d_h] dtype (written); lse [B, h] fp32 or NULL.
+ * Errors as attn_decode_split_fp8kv; NULL partials or o: ATTN_ERR_INVALID.
+ */
+int attn_decode_fp8kv(const void* q, const void* k, const void* v,
+                      const int32_t* block_table, int max_pages, int page_size, int num_pages,
+                      const int32_t* seq_lens, int s_max,
+                      int B, int h, int h_kv, int d_h,
+                      int chunk_keys, int max_splits, int dtype, float scale,
+                      float k_scale, float v_scale,
+                      float* part_o, float* part_m, float* part_l,
+                      void* o, float* lse, void* stream);
+
+/*
  * attn_decode for callers that cannot allocate device memory (code under
  * HIP graph capture, serving loops that forbid allocation): the same two
  * stages and results, with the split-KV partial states kept in a scratch

@@ -33,6 +33,10 @@ _SIGNATURES = {
     "attn_merge_states": [_c_void_p] * 4 + [_c_int] * 5 + [_c_void_p, _c_void_p, _c_int, _c_void_p],
     "attn_decode": [_c_void_p] * 4 + [_c_int] * 3 + [_c_void_p] + [_c_int] * 8 + [_c_float] + [_c_void_p] * 6,
     "attn_decode_noalloc": [_c_void_p] * 4 + [_c_int] * 3 + [_c_void_p] + [_c_int] * 8 + [_c_float] + [_c_void_p] * 3,
+    "attn_decode_split_fp8kv": [_c_void_p] * 4 + [_c_int] * 3 + [_c_void_p] + [_c_int] * 8 + [_c_float] * 3
+                               + [_c_void_p] * 4,
+    "attn_decode_fp8kv": [_c_void_p] * 4 + [_c_int] * 3 + [_c_void_p] + [_c_int] * 8 + [_c_float] * 3
+                         + [_c_void_p] * 6,
     "attn_merge_lse": [_c_void_p] * 4 + [_c_int] * 2 + [_c_void_p, _c_void_p, _c_int, _c_void_p],
     "attn_paged_gather": [_c_void_p] * 3 + [_c_int] * 8 + [_c_void_p, _c_void_p],
     "attn_stream_read": [_c_void_p, ctypes.c_uint64, _c_int, _c_void_p, _c_void_p],
@@ -268,9 +272,11 @@ def merge_states(part_o, part_m, part_l, seq_lens, chunk_keys, dtype, out=None, 
     return out, lse
 
 
-def _kv_geometry(q, k, v, block_table, page_size):
-    """(h_kv, s_max, max_pages, num_pages, page_size) of contiguous or paged K/V, checked."""
-    dev, dt = q.device, q.dtype
+def _kv_geometry(q, k, v, block_table, page_size, kv_dtype=None):
+    """(h_kv, s_max, max_pages, num_pages, page_size) of contiguous or paged K/V, checked
+    (K/V elements of q's dtype, or of ``kv_dtype``)."""
+    dev = q.device
+    dt = q.dtype if kv_dtype is None else kv_dtype
     B, h, d = q.shape
     if block_table is None:
         h_kv, s_max = k.shape[1], k.shape[2]
@@ -313,6 +319,76 @@ def decode_call(q, k, v, seq_lens, chunk_keys, max_splits, block_table=None, pag
         _ptr(seq_lens), s_max, B, h, h_kv, d, int(chunk_keys), int(max_splits), _dtype_code(q),
         scale, _ptr(part_o), _ptr(part_m), _ptr(part_l), _ptr(out), _ptr(lse), _stream(dev)))
     return out, lse
+
+
+def _partials(B, h, max_splits, d, dev, part_o, part_m, part_l):
+    shp = (B, h, max_splits)
+    part_o = torch.empty(shp + (d,), dtype=torch.float32, device=dev) if part_o is None else part_o
+    part_m = torch.empty(shp, dtype=torch.float32, device=dev) if part_m is None else part_m
+    part_l = torch.empty(shp, dtype=torch.float32, device=dev) if part_l is None else part_l
+    _want(part_o, "part_o", torch.float32, shp + (d,), dev)
+    _want(part_m, "part_m", torch.float32, shp, dev)
+    _want(part_l, "part_l", torch.float32, shp, dev)
+    return part_o, part_m, part_l
+
+
+def decode_split_fp8kv(q, k, v, seq_lens, chunk_keys, max_splits, k_scale, v_scale, block_table=None,
+                       page_size=16, scale=None, part_o=None, part_m=None, part_l=None):
+    """Stage 1 of split-KV decode over 8-bit E4M3 K/V (uint8 codes, layouts
+    as decode_split) with per-tensor scales, via attn_decode_split_fp8kv.
+    Returns (part_o, part_m, part_l) fp32."""
+    lib = load()
+    _want(q, "q")
+    dev = q.device
+    B, h, d = q.shape
+    _want(seq_lens, "seq_lens", torch.int32, (B,), dev)
+    h_kv, s_max, max_pages, num_pages, page_size = _kv_geometry(q, k, v, block_table, page_size, torch.uint8)
+    part_o, part_m, part_l = _partials(B, h, max_splits, d, dev, part_o, part_m, part_l)
+    scale = float(np.float32(1.0 / np.sqrt(d))) if scale is None else float(scale)
+    _check("attn_decode_split_fp8kv", lib.attn_decode_split_fp8kv(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(block_table), max_pages, page_size, num_pages,
+        _ptr(seq_lens), s_max, B, h, h_kv, d, int(chunk_keys), int(max_splits), _dtype_code(q),
+        scale, float(k_scale), float(v_scale), _ptr(part_o), _ptr(part_m), _ptr(part_l), _stream(dev)))
+    return part_o, part_m, part_l
+
+
+def decode_fp8kv_call(q, k, v, seq_lens, chunk_keys, max_splits, k_scale, v_scale, block_table=None,
+                      page_size=16, scale=None, part_o=None, part_m=None, part_l=None, out=None, lse=None):
+    """Both decode stages over 8-bit E4M3 K/V in one call of
+    attn_decode_fp8kv. Returns (o [B,h,128], lse [B,h])."""
+    lib = load()
+    _want(q, "q")
+    dev, dt = q.device, q.dtype
+    B, h, d = q.shape
+    _want(seq_lens, "seq_lens", torch.int32, (B,), dev)
+    h_kv, s_max, max_pages, num_pages, page_size = _kv_geometry(q, k, v, block_table, page_size, torch.uint8)
+    part_o, part_m, part_l = _partials(B, h, max_splits, d, dev, part_o, part_m, part_l)
+    out = torch.empty((B, h, d), dtype=dt, device=dev) if out is None else out
+    _want(out, "out", dt, (B, h, d), dev)
+    lse = torch.empty((B, h), dtype=torch.float32, device=dev) if lse is None else lse
+    _want(lse, "lse", torch.float32, (B, h), dev)
+    scale = float(np.float32(1.0 / np.sqrt(d))) if scale is None else float(scale)
+    _check("attn_decode_fp8kv", lib.attn_decode_fp8kv(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(block_table), max_pages, page_size, num_pages,
+        _ptr(seq_lens), s_max, B, h, h_kv, d, int(chunk_keys), int(max_splits), _dtype_code(q),
+        scale, float(k_scale), float(v_scale), _ptr(part_o), _ptr(part_m), _ptr(part_l), _ptr(out), _ptr(lse),
+        _stream(dev)))
+    return out, lse
+
+
+def decode_fp8kv(q, k, v, seq_lens, k_scale, v_scale, seq_lens_host=None, block_table=None, page_size=16,
+                 scale=None, plan=None, num_cus=None):
+    """Split-KV decode over 8-bit E4M3 K/V: plan (host, as decode), then
+    attn_decode_fp8kv. Returns (o, lse, (chunk_keys, max_splits))."""
+    B, h, _ = q.shape
+    h_kv = k.shape[2] if block_table is not None else k.shape[1]
+    if plan is None:
+        lens = seq_lens.cpu().numpy() if seq_lens_host is None else np.asarray(seq_lens_host)
+        plan = decode_plan(lens, h, h_kv, num_cus=num_cus, device=q.device)
+    chunk, splits = plan
+    o, lse = decode_fp8kv_call(q, k, v, seq_lens, chunk, splits, k_scale, v_scale, block_table=block_table,
+                               page_size=page_size, scale=scale)
+    return o, lse, plan
 
 
 def decode_noalloc(q, k, v, seq_lens, chunk_keys, max_splits, block_table=None, page_size=16, scale=None,

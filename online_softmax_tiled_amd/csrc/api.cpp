@@ -25,6 +25,11 @@ hipError_t decode_split(const void* q, const void* k, const void* v, const int32
                         int s_max, int B, int h, int h_kv, int chunk_keys, int max_splits,
                         int dtype, float scale, float* part_o, float* part_m, float* part_l,
                         hipStream_t stream);
+hipError_t decode_split_fp8kv(const void* q, const void* k, const void* v, const int32_t* block_table,
+                             int max_pages, int page_size, int num_pages, const int32_t* seq_lens, int s_max,
+                             int B, int h, int h_kv, int chunk_keys, int max_splits, int dtype, float scale,
+                             float k_scale, float v_scale, float* part_o, float* part_m, float* part_l,
+                             hipStream_t stream);
 hipError_t decode_split_rows(const void* q, const void* k, const void* v, const int32_t* block_table,
                              int max_pages, int page_shift, int num_pages, const int32_t* seq_lens, int s_max,
                              int B, int h, int h_kv, int chunk_keys, int max_splits, int dtype, float scale,
@@ -150,6 +155,13 @@ int check_decode(const char* fn, const void* q, const void* k, const void* v, co
   // Contiguous K/V with s_max = 0 hold no key (every sequence is empty), so
   // they may be NULL; a paged pool always holds num_pages > 0 pages.
   REQUIRE((k && v) || (!block_table && s_max == 0), ATTN_ERR_INVALID, "%s: k and v must not be NULL", fn);
+  return ATTN_OK;
+}
+
+// The per-tensor scales of 8-bit K/V.
+int check_kv_scales(const char* fn, float k_scale, float v_scale) {
+  REQUIRE(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f, ATTN_ERR_INVALID,
+          "%s: k_scale and v_scale must be finite and > 0 (got %g, %g)", fn, (double)k_scale, (double)v_scale);
   return ATTN_OK;
 }
 
@@ -282,6 +294,46 @@ int attn_decode_split(const void* q, const void* k, const void* v, const int32_t
   return from_hip(launch_split(q, k, v, block_table, max_pages, page_size, num_pages, seq_lens, s_max, B, h, h_kv,
                                chunk_keys, max_splits, dtype, scale, part_o, part_m, part_l,
                                static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+int attn_decode_split_fp8kv(const void* q, const void* k, const void* v, const int32_t* block_table,
+                             int max_pages, int page_size, int num_pages, const int32_t* seq_lens, int s_max, int B,
+                             int h, int h_kv, int d_h, int chunk_keys, int max_splits, int dtype, float scale,
+                             float k_scale, float v_scale, float* part_o, float* part_m, float* part_l,
+                             void* stream) {
+  const char* fn = "attn_decode_split_fp8kv";
+  if (int e = check_decode(fn, q, k, v, block_table, max_pages, page_size, num_pages, seq_lens, s_max, B, h, h_kv,
+                           d_h, chunk_keys, max_splits, dtype, scale))
+    return e;
+  if (int e = check_kv_scales(fn, k_scale, v_scale)) return e;
+  if (B == 0) return ok();
+  REQUIRE(part_o && part_m && part_l, ATTN_ERR_INVALID, "%s: a required pointer is NULL", fn);
+  return from_hip(attn::decode_split_fp8kv(q, k, v, block_table, max_pages, page_size, num_pages, seq_lens, s_max, B,
+                                           h, h_kv, chunk_keys, max_splits, dtype, scale, k_scale, v_scale, part_o,
+                                           part_m, part_l, static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+int attn_decode_fp8kv(const void* q, const void* k, const void* v, const int32_t* block_table, int max_pages,
+                      int page_size, int num_pages, const int32_t* seq_lens, int s_max, int B, int h, int h_kv,
+                      int d_h, int chunk_keys, int max_splits, int dtype, float scale, float k_scale,
+                      float v_scale, float* part_o, float* part_m, float* part_l, void* o, float* lse,
+                      void* stream) {
+  const char* fn = "attn_decode_fp8kv";
+  if (int e = check_decode(fn, q, k, v, block_table, max_pages, page_size, num_pages, seq_lens, s_max, B, h, h_kv,
+                           d_h, chunk_keys, max_splits, dtype, scale))
+    return e;
+  if (int e = check_kv_scales(fn, k_scale, v_scale)) return e;
+  if (B == 0) return ok();
+  REQUIRE(part_o && part_m && part_l && o, ATTN_ERR_INVALID, "%s: a required pointer is NULL", fn);
+  REQUIRE((long)B * h < (1L << 31), ATTN_ERR_UNSUPPORTED, "%s: grid too large", fn);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = attn::decode_split_fp8kv(q, k, v, block_table, max_pages, page_size, num_pages, seq_lens,
+                                                s_max, B, h, h_kv, chunk_keys, max_splits, dtype, scale, k_scale,
+                                                v_scale, part_o, part_m, part_l, s);
+  if (e != hipSuccess) return from_hip(e, fn);
+  return from_hip(attn::merge_states(part_o, part_m, part_l, seq_lens, chunk_keys, B, h, max_splits, o, lse, dtype, s),
                   fn);
 }
 

@@ -43,6 +43,8 @@
 // Keys outside the split, past the sequence, or on a page id outside the
 // pool are excluded (score -inf) and their V rows are zeroed before use, so
 // poisoned (NaN) slots never reach the result.
+#include <type_traits>
+
 #include "common.h"
 
 namespace attn {
@@ -68,8 +70,29 @@ struct DecodeParams {
   int B, h, h_kv, g;
   int n_hb;    // head blocks of 16 per KV head = ceil(g / 16)
   int chunk, max_splits;
-  float c;     // scale * log2(e)
+  float c;     // scale * log2(e) (times k_scale for 8-bit K/V)
+  float v_scale;   // 8-bit K/V: V's tensor scale, applied to O~ as it is written
 };
+
+// Eight E4M3 codes (two words, code e in byte e % 4 of word e / 4) as eight
+// 16-bit operands of type DT, with gfx950's packed fp8 conversion at scale
+// 1, which is exact (every E4M3 value is an fp16 and a bf16 value); element
+// e lands in half e % 2 of word e / 2, as a 16-bit load would put it.
+template <int DT>
+__device__ __forceinline__ u32x4 cvt8(u32x2 x) {
+  // (the half-word select of the conversion is an immediate)
+  if constexpr (DT == ATTN_DTYPE_BF16)
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[0], 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[0], 1.0f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[1], 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[1], 1.0f, true))};
+  else
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[0], 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[0], 1.0f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[1], 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[1], 1.0f, true))};
+}
+
 
 // Max / sum of x over the four 16-lane rows of a wave (lanes l, l^16,
 // l^32, l^48).
@@ -90,9 +113,17 @@ __device__ __forceinline__ int vt_pos(int kk) { return ((kk & 12) << 1) | ((kk &
 // head mode the waves of a workgroup (and, beyond 4 head blocks, several
 // workgroups) read the same keys, and the loads must leave them in the
 // caches.
-template <int DT, bool PAGED, bool STREAM>
+template <int DT, bool PAGED, bool STREAM, bool KV8>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
   using E = Elem<DT>;
+  // The PV product: on the operand type with 8-bit V it is fp16 whatever the
+  // query type (E4M3 codes, at most 448 in magnitude, are exact fp16 values,
+  // and P rounded to fp16 keeps 3 more bits than bf16).
+  constexpr int PDT = KV8 ? ATTN_DTYPE_F16 : DT;
+  using EP = Elem<PDT>;
+  using KE = std::conditional_t<KV8, uint8_t, uint16_t>;   // stored K/V element
+  const KE* const k_el = reinterpret_cast<const KE*>(p.k);
+  const KE* const v_el = reinterpret_cast<const KE*>(p.v);
   __shared__ __attribute__((aligned(16))) uint16_t lds[kWaves * kWaveLds];
 
   // Consecutive workgroups (dealt round-robin to the 8 XCDs) take
@@ -141,13 +172,19 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
   const int col = lane & 15;   // query head inside the group
   const int row = lane >> 4;   // 16-lane row 0..3
 
-  // Q^T as B operands: lane holds head col, d in [8*row + 32c, +8).
+  // Q^T as B operands: lane holds head col and one d-chunk of 8 per step.
   u32x4 qf[4];
   {
     const bool ok = col < hn;
-    const uint16_t* qp = p.q + ((size_t)b * p.h + kvh * p.g + hb0 + (ok ? col : 0)) * kD + row * 8;
+    const uint16_t* qh = p.q + ((size_t)b * p.h + kvh * p.g + hb0 + (ok ? col : 0)) * kD;
+    // MFMA step c sums over d-chunk row + 4c (8-bit K/V: 2 row + (c & 1) +
+    // 8 (c >> 1), the chunks a lane's 16-byte K loads hold); the order of
+    // the d-chunks over the steps does not change the sum's terms
 #pragma unroll
-    for (int c = 0; c < 4; ++c) qf[c] = ok ? load16(qp + c * 32) : u32x4{0, 0, 0, 0};
+    for (int c = 0; c < 4; ++c) {
+      const int chunk = KV8 ? 2 * row + (c & 1) + 8 * (c >> 1) : row + 4 * c;
+      qf[c] = ok ? load16(qh + chunk * 8) : u32x4{0, 0, 0, 0};
+    }
   }
 
   const long kstride = PAGED ? p.h_kv : 1;   // rows between consecutive keys
@@ -158,17 +195,19 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
   for (int i = 0; i < 8; ++i) acc[i] = f32x4{};
   float m_run = -INFINITY;
   float l_run = 0.f;   // replicated across the 4 rows after reduction
+  // Sum of the weights as rounded for the PV product. The split's O~ is
+  // written scaled by l / l~, so that with part_l = l (fp32 weights, for the
+  // LSE) the merge divides the rounded-weight products by their own sum.
+  float lr_run = 0.f;
 
   const int n_tiles = (k_hi - k_lo + kTile - 1) / kTile;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int t0 = head_mode ? 0 : wave_u;
   const int dt = head_mode ? 1 : kWaves;
-  for (int t = t0; t < n_tiles; t += dt) {
-    const int kt = k_lo + t * kTile;
+  // Page rows and validity of the two 16-key blocks of tile t.
+  auto tile_rows = [&](int kt, long (&rbase)[2], bool (&bok)[2]) {
     // Each 16-key block lies inside one page (pages hold a multiple of 16
     // keys and blocks start at multiples of 16): resolve its row once.
-    long rbase[2];
-    bool bok[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int key0 = kt + kb * 16;
@@ -182,27 +221,9 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
         rbase[kb] = ((long)b * p.h_kv + kvh) * p.s_max + key0;
       }
     }
-    // K: lane loads key 16kb + col, d-chunks 8*row + 32c.
-    u32x4 kf[2][4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const bool ok = bok[kb] && kt + kb * 16 + col < k_hi;
-      const uint16_t* kp = p.k + (rbase[kb] + (ok ? col : 0) * kstride) * kD + row * 8;
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        kf[kb][c] = ok ? (STREAM ? load16_nt(kp + c * 32) : load16(kp + c * 32)) : u32x4{0, 0, 0, 0};
-    }
-    // V: lane (d-chunk col, key group row) loads keys 4*row+i and 16+4*row+i.
-    u32x4 vf[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int kb = i >> 2;
-      const int ko = row * 4 + (i & 3);
-      const bool ok = bok[kb] && kt + kb * 16 + ko < k_hi;
-      const uint16_t* vp = p.v + (rbase[kb] + ko * kstride) * kD + col * 8;
-      vf[i] = ok ? (STREAM ? load16_nt(vp) : load16(vp)) : u32x4{0, 0, 0, 0};
-    }
-
+  };
+  // QK, softmax, V^T staging and PV of one tile, from 16-bit operands.
+  auto tile_compute = [&](int kt, const bool (&bok)[2], const u32x4 (&kf)[2][4], const u32x4 (&vf)[8]) {
     f32x4 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -258,14 +279,105 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    const u32x4 pf = u32x4{E::pack2(s[0][0], s[0][1]), E::pack2(s[0][2], s[0][3]),
-                           E::pack2(s[1][0], s[1][1]), E::pack2(s[1][2], s[1][3])};
+    const u32x4 pf = u32x4{EP::pack2(s[0][0], s[0][1]), EP::pack2(s[0][2], s[0][3]),
+                           EP::pack2(s[1][0], s[1][1]), EP::pack2(s[1][2], s[1][3])};
+    lr_run = lr_run * alpha +
+             sum_rows16(EP::add_pair(pf[3], EP::add_pair(pf[2], EP::add_pair(pf[1], EP::add_pair(pf[0], 0.f)))));
 #pragma unroll
     for (int db = 0; db < 8; ++db)
-      acc[db] = E::mfma16(load16(&vt[(db * 16 + col) * kVtStr + row * 8]), pf, acc[db]);
+      acc[db] = EP::mfma16(load16(&vt[(db * 16 + col) * kVtStr + row * 8]), pf, acc[db]);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  if constexpr (!KV8) {
+    for (int t = t0; t < n_tiles; t += dt) {
+      const int kt = k_lo + t * kTile;
+      long rbase[2];
+      bool bok[2];
+      tile_rows(kt, rbase, bok);
+      // K: lane loads key 16kb + col, d-chunks 8*row + 32c.
+      u32x4 kf[2][4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bool ok = bok[kb] && kt + kb * 16 + col < k_hi;
+        const KE* kp = k_el + (rbase[kb] + (ok ? col : 0) * kstride) * kD + row * 8;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kf[kb][c] = ok ? (STREAM ? load16_nt(kp + c * 32) : load16(kp + c * 32)) : u32x4{0, 0, 0, 0};
+      }
+      // V: lane (d-chunk col, key group row) loads keys 4*row+i and 16+4*row+i.
+      u32x4 vf[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int kb = i >> 2;
+        const int ko = row * 4 + (i & 3);
+        const bool ok = bok[kb] && kt + kb * 16 + ko < k_hi;
+        const KE* vp = v_el + (rbase[kb] + ko * kstride) * kD + col * 8;
+        vf[i] = ok ? (STREAM ? load16_nt(vp) : load16(vp)) : u32x4{0, 0, 0, 0};
+      }
+
+      tile_compute(kt, bok, kf, vf);
+    }
+  } else {
+    // 8-bit K/V: each wave loads two of its tiles at once (half the bytes of
+    // a 16-bit tile each), the second tile's loads in flight while the first
+    // is computed. The page rows of both tiles are read before any tile load
+    // is issued (loads retire in order: waiting for a page id read after a
+    // tile's loads would wait for those loads too).
+    // K: lane (key col, row) loads 16 codes, bytes [16 (row + 4 hh), +16) of
+    // its key; MFMA step c takes d-chunk 2 row + (c & 1) + 8 (c >> 1), as Q.
+    // V: lane (d-chunk col, key group row) loads 8 codes of keys 4 row + i
+    // and 16 + 4 row + i.
+    struct Raw {
+      u32x4 k[2][2];
+      u32x2 v[8];
+      long rbase[2];
+      bool bok[2];
+    };
+    auto load_raw = [&](int kt, Raw& r) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bool ok = r.bok[kb] && kt + kb * 16 + col < k_hi;
+        const KE* kp = k_el + (r.rbase[kb] + (ok ? col : 0) * kstride) * kD + row * 16;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          r.k[kb][hh] = ok ? (STREAM ? load16_nt(kp + 64 * hh) : load16(kp + 64 * hh)) : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int kb = i >> 2;
+        const int ko = row * 4 + (i & 3);
+        const bool ok = r.bok[kb] && kt + kb * 16 + ko < k_hi;
+        const KE* vp = v_el + (r.rbase[kb] + ko * kstride) * kD + col * 8;
+        r.v[i] = ok ? (STREAM ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vp))
+                              : *reinterpret_cast<const u32x2*>(vp))
+                    : u32x2{0, 0};
+      }
+    };
+    auto compute_raw = [&](int kt, const Raw& r) {
+      u32x4 kf[2][4], vf[8];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          kf[kb][2 * hh] = cvt8<DT>(u32x2{r.k[kb][hh][0], r.k[kb][hh][1]});
+          kf[kb][2 * hh + 1] = cvt8<DT>(u32x2{r.k[kb][hh][2], r.k[kb][hh][3]});
+        }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) vf[i] = cvt8<PDT>(r.v[i]);
+      tile_compute(kt, r.bok, kf, vf);
+    };
+    for (int t = t0; t < n_tiles; t += 2 * dt) {
+      const bool two = t + dt < n_tiles;
+      Raw ra, rb;
+      tile_rows(k_lo + t * kTile, ra.rbase, ra.bok);
+      tile_rows(k_lo + (t + dt) * kTile, rb.rbase, rb.bok);   // past the keys: no valid block
+      load_raw(k_lo + t * kTile, ra);
+      load_raw(k_lo + (t + dt) * kTile, rb);
+      compute_raw(k_lo + t * kTile, ra);
+      if (two) compute_raw(k_lo + (t + dt) * kTile, rb);
+    }
   }
 
   if (head_mode) {
@@ -274,8 +386,10 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
     if (col < hn) {
       const size_t hs = (size_t)b * p.h + kvh * p.g + hb0 + col;
       float* po = p.part_o + (hs * p.max_splits + split) * kD;
+      float f = lr_run > 0.f ? l_run / lr_run : 1.f;
+      if (KV8) f *= p.v_scale;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(&po[db * 16 + row * 4]) = acc[db];
+      for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(&po[db * 16 + row * 4]) = acc[db] * f;
       if (row == 0) {
         p.part_m[hs * p.max_splits + split] = m_run == -INFINITY ? -INFINITY : m_run * kLn2;
         p.part_l[hs * p.max_splits + split] = l_run;
@@ -287,14 +401,15 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
   // Merge the 4 wave states through LDS (reusing the V^T regions).
   __syncthreads();
   float* red = reinterpret_cast<float*>(lds);            // [wave][16 heads][128 d]
-  float* red_ml = red + kWaves * 16 * kD;                 // [wave][16][2]
+  float* red_ml = red + kWaves * 16 * kD;                 // [wave][16][3]: m, l, l~
   // acc[db] lane (col, row) reg r: head col, d = 16db + 4row + r
 #pragma unroll
   for (int db = 0; db < 8; ++db)
     *reinterpret_cast<f32x4*>(&red[(wave * 16 + col) * kD + db * 16 + row * 4]) = acc[db];
   if (row == 0) {
-    red_ml[(wave * 16 + col) * 2 + 0] = m_run;
-    red_ml[(wave * 16 + col) * 2 + 1] = l_run;
+    red_ml[(wave * 16 + col) * 3 + 0] = m_run;
+    red_ml[(wave * 16 + col) * 3 + 1] = l_run;
+    red_ml[(wave * 16 + col) * 3 + 2] = lr_run;
   }
   __syncthreads();
 
@@ -304,21 +419,24 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
     float mw[kWaves], m_all = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      mw[w] = red_ml[(w * 16 + j) * 2];
+      mw[w] = red_ml[(w * 16 + j) * 3];
       m_all = fmaxf(m_all, mw[w]);
     }
     f32x4 o = f32x4{};
-    float l_all = 0.f;
+    float l_all = 0.f, lr_all = 0.f;
     if (m_all != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
         const float wt = fast_exp2(mw[w] - m_all);   // empty wave: 2^-inf = 0
-        l_all += wt * red_ml[(w * 16 + j) * 2 + 1];
+        l_all += wt * red_ml[(w * 16 + j) * 3 + 1];
+        lr_all += wt * red_ml[(w * 16 + j) * 3 + 2];
         o += wt * *reinterpret_cast<const f32x4*>(&red[(w * 16 + j) * kD + d]);
       }
     }
+    float f = lr_all > 0.f ? l_all / lr_all : 1.f;
+    if (KV8) f *= p.v_scale;
     const size_t hs = (size_t)b * p.h + kvh * p.g + hb0 + j;
-    *reinterpret_cast<f32x4*>(&p.part_o[(hs * p.max_splits + split) * kD + d]) = o;
+    *reinterpret_cast<f32x4*>(&p.part_o[(hs * p.max_splits + split) * kD + d]) = o * f;
     if ((tid & 31) == 0) {
       p.part_m[hs * p.max_splits + split] = m_all == -INFINITY ? -INFINITY : m_all * kLn2;
       p.part_l[hs * p.max_splits + split] = l_all;
@@ -326,7 +444,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
   }
 }
 
-template <int DT>
+template <int DT, bool KV8>
 hipError_t dispatch_decode(const DecodeParams& p, bool paged, hipStream_t stream) {
   const long units = (long)p.max_splits * p.h_kv * p.B;
   const long n_hg = (p.n_hb + kWaves - 1) / kWaves;
@@ -334,22 +452,22 @@ hipError_t dispatch_decode(const DecodeParams& p, bool paged, hipStream_t stream
                                 : dim3((unsigned)(((units + 7) / 8) * 8 * n_hg));
   const bool stream_kv = p.n_hb == 1;
   if (paged) {
-    if (stream_kv) hipLaunchKernelGGL((decode_split_kernel<DT, true, true>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((decode_split_kernel<DT, true, false>), grid, dim3(256), 0, stream, p);
+    if (stream_kv) hipLaunchKernelGGL((decode_split_kernel<DT, true, true, KV8>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((decode_split_kernel<DT, true, false, KV8>), grid, dim3(256), 0, stream, p);
   } else {
-    if (stream_kv) hipLaunchKernelGGL((decode_split_kernel<DT, false, true>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((decode_split_kernel<DT, false, false>), grid, dim3(256), 0, stream, p);
+    if (stream_kv) hipLaunchKernelGGL((decode_split_kernel<DT, false, true, KV8>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((decode_split_kernel<DT, false, false, KV8>), grid, dim3(256), 0, stream, p);
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t decode_split(const void* q, const void* k, const void* v, const int32_t* block_table,
-                        int max_pages, int page_size, int num_pages, const int32_t* seq_lens,
-                        int s_max, int B, int h, int h_kv, int chunk_keys, int max_splits,
-                        int dtype, float scale, float* part_o, float* part_m, float* part_l,
-                        hipStream_t stream) {
+namespace {
+DecodeParams decode_params(const void* q, const void* k, const void* v, const int32_t* block_table,
+                           int max_pages, int page_size, int num_pages, const int32_t* seq_lens, int s_max,
+                           int B, int h, int h_kv, int chunk_keys, int max_splits, float scale, float* part_o,
+                           float* part_m, float* part_l) {
   DecodeParams p;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
@@ -371,9 +489,39 @@ hipError_t decode_split(const void* q, const void* k, const void* v, const int32
   p.chunk = chunk_keys;
   p.max_splits = max_splits;
   p.c = scale * kLog2e;
+  p.v_scale = 1.f;
+  return p;
+}
+}  // namespace
+
+hipError_t decode_split(const void* q, const void* k, const void* v, const int32_t* block_table,
+                        int max_pages, int page_size, int num_pages, const int32_t* seq_lens,
+                        int s_max, int B, int h, int h_kv, int chunk_keys, int max_splits,
+                        int dtype, float scale, float* part_o, float* part_m, float* part_l,
+                        hipStream_t stream) {
+  const DecodeParams p = decode_params(q, k, v, block_table, max_pages, page_size, num_pages, seq_lens, s_max, B,
+                                       h, h_kv, chunk_keys, max_splits, scale, part_o, part_m, part_l);
   if (B == 0 || h == 0) return hipSuccess;
-  if (dtype == ATTN_DTYPE_BF16) return dispatch_decode<ATTN_DTYPE_BF16>(p, block_table != nullptr, stream);
-  return dispatch_decode<ATTN_DTYPE_F16>(p, block_table != nullptr, stream);
+  if (dtype == ATTN_DTYPE_BF16) return dispatch_decode<ATTN_DTYPE_BF16, false>(p, block_table != nullptr, stream);
+  return dispatch_decode<ATTN_DTYPE_F16, false>(p, block_table != nullptr, stream);
+}
+
+// 8-bit E4M3 K/V with per-tensor scales: k_scale joins the logit scale (the
+// scores are (q . k_code) * k_scale * scale), v_scale multiplies each
+// split's O~ (l and m do not involve V). Every group size runs on this
+// file's kernel (head blocks of 16 beyond 16 query heads per KV head).
+hipError_t decode_split_fp8kv(const void* q, const void* k, const void* v, const int32_t* block_table,
+                             int max_pages, int page_size, int num_pages, const int32_t* seq_lens, int s_max,
+                             int B, int h, int h_kv, int chunk_keys, int max_splits, int dtype, float scale,
+                             float k_scale, float v_scale, float* part_o, float* part_m, float* part_l,
+                             hipStream_t stream) {
+  DecodeParams p = decode_params(q, k, v, block_table, max_pages, page_size, num_pages, seq_lens, s_max, B, h,
+                                 h_kv, chunk_keys, max_splits, scale, part_o, part_m, part_l);
+  p.c = scale * k_scale * kLog2e;
+  p.v_scale = v_scale;
+  if (B == 0 || h == 0) return hipSuccess;
+  if (dtype == ATTN_DTYPE_BF16) return dispatch_decode<ATTN_DTYPE_BF16, true>(p, block_table != nullptr, stream);
+  return dispatch_decode<ATTN_DTYPE_F16, true>(p, block_table != nullptr, stream);
 }
 
 // Split plan. The unsplit grid has B * h_kv workgroups; the split count that

@@ -156,6 +156,49 @@ def test_decode_rejects_before_launch(lib, kw, code):
     assert "attn_decode" in lib.attn_last_error().decode()
 
 
+def fp8_call(lib, one_call, **kw):
+    args = dict(q=1, k=1, v=1, bt=NULL, max_pages=0, page_size=16, num_pages=0, sl=1, s_max=64, B=1,
+                h=8, h_kv=1, d=128, chunk=64, splits=1, dtype=1, scale=0.088, ks=0.5, vs=2.0, po=1, pm=1, pl=1,
+                o=1, lse=NULL)
+    args.update(kw)
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    head = (p(args["q"]), p(args["k"]), p(args["v"]), p(args["bt"]), args["max_pages"], args["page_size"],
+            args["num_pages"], p(args["sl"]), args["s_max"], args["B"], args["h"], args["h_kv"], args["d"],
+            args["chunk"], args["splits"], args["dtype"], args["scale"], args["ks"], args["vs"],
+            p(args["po"]), p(args["pm"]), p(args["pl"]))
+    if one_call:
+        return lib.attn_decode_fp8kv(*head, p(args["o"]), p(args["lse"]), None)
+    return lib.attn_decode_split_fp8kv(*head, None)
+
+
+@pytest.mark.parametrize("one_call", [False, True])
+@pytest.mark.parametrize("kw,code", [
+    (dict(ks=0.0), 1),                     # scales finite and > 0
+    (dict(vs=-1.0), 1),
+    (dict(ks=float("inf")), 1),
+    (dict(vs=float("nan")), 1),
+    (dict(scale=0.0), 1),
+    (dict(h=514, h_kv=2), 2),
+    (dict(chunk=40), 1),
+    (dict(splits=0), 1),
+    (dict(bt=1, page_size=8, max_pages=4, num_pages=4), 2),
+    (dict(d=96), 2),
+    (dict(dtype=2), 2),
+    (dict(pl=None), 1),
+    (dict(k=None), 1),
+    (dict(s_max=(1 << 23) + 1), 2),
+])
+def test_fp8kv_decode_rejects_before_launch(lib, one_call, kw, code):
+    assert fp8_call(lib, one_call, **kw) == code
+    assert "fp8kv" in lib.attn_last_error().decode()
+
+
+def test_fp8kv_decode_needs_o_only_in_one_call(lib):
+    assert fp8_call(lib, True, o=None) == 1
+    assert fp8_call(lib, False, o=None, B=0) == 0
+    assert fp8_call(lib, True, B=0, q=None, k=None, v=None, sl=None, po=None, pm=None, pl=None, o=None) == 0
+
+
 def test_decode_empty_batch_is_ok_without_launch(lib):
     assert decode_call(lib, B=0, q=None, k=None, v=None, sl=None, po=None, pm=None, pl=None, o=None) == 0
 
