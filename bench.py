@@ -502,6 +502,9 @@ def run_only(args, dev):
     elif args.only == "decode_fp8":
         r = bench_decode_fp8kv(args.steps, args.warmup, dev, "paged_decode_llama3_8b_b64")
         print(json.dumps(r))
+    elif args.only == "decode_fp8_70b":
+        r = bench_decode_fp8kv(args.steps, args.warmup, dev, "decode_70b_tp8_s32768", copies=40)
+        print(json.dumps(r))
     elif args.only == "decode_70b":
         r = bench_decode_contiguous(args.steps, args.warmup, dev)
         print(json.dumps(r))
@@ -529,7 +532,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="only the headline prefill")
     ap.add_argument("--only", choices=["prefill", "stress", "chunked", "decode_70b", "decode_paged", "decode_g128",
-                                       "decode_fp8", "merge_lse", "copy"],
+                                       "decode_fp8", "decode_fp8_70b", "merge_lse", "copy"],
                     default=None,
                     help="run one workload only (for profiler counter runs) and print its timing")
     ap.add_argument("--copy-mb", type=int, default=1024,

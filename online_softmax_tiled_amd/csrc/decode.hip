@@ -93,6 +93,16 @@ __device__ __forceinline__ u32x4 cvt8(u32x2 x) {
                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[1], 1.0f, true))};
 }
 
+// Word sel (0: codes 0-1, 1: codes 2-3) of cvt8 of one word.
+template <int DT>
+__device__ __forceinline__ uint32_t cvt8w(uint32_t w, int sel) {
+  if constexpr (DT == ATTN_DTYPE_BF16)
+    return sel ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))
+               : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  else
+    return sel ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true))
+               : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+}
 
 // Max / sum of x over the four 16-lane rows of a wave (lanes l, l^16,
 // l^32, l^48).
@@ -223,13 +233,17 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
     }
   };
   // QK, softmax, V^T staging and PV of one tile, from 16-bit operands.
-  auto tile_compute = [&](int kt, const bool (&bok)[2], const u32x4 (&kf)[2][4], const u32x4 (&vf)[8]) {
+  // K fragments come from kfrag(kb, c), word e of V row i from vword(i, e); after_stage()
+  // runs once the tile's K and V registers are consumed (after the V^T
+  // stores), so the 8-bit path can reuse them for the next loads.
+  auto tile_compute = [&](int kt, const bool (&bok_in)[2], auto&& kfrag, auto&& vword, auto&& after_stage) {
+    const bool bok[2] = {bok_in[0], bok_in[1]};
     f32x4 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x4{};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) s[kb] = E::mfma16(kf[kb][c], qf[c], s[kb]);
+      for (int c = 0; c < 4; ++c) s[kb] = E::mfma16(kfrag(kb, c), qf[c], s[kb]);
     }
     // Exclude keys outside [k_lo, k_hi) or on an invalid page: register r of
     // block kb holds key kt + 16kb + 4row + r.
@@ -267,6 +281,9 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
     const int pos = vt_pos(row * 4);   // keys 4row..4row+3 -> pos..pos+3; 16+4row.. -> pos+4..
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
+      uint32_t vf[8][4];   // word e of each V row (only [.][e] is used)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) vf[i][e] = vword(i, e);
       const int d = col * 8 + 2 * e;
       store16(&vt[d * kVtStr + pos],
               u32x4{pack_lo16(vf[0][e], vf[1][e]), pack_lo16(vf[2][e], vf[3][e]),
@@ -275,6 +292,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
               u32x4{pack_hi16(vf[0][e], vf[1][e]), pack_hi16(vf[2][e], vf[3][e]),
                     pack_hi16(vf[4][e], vf[5][e]), pack_hi16(vf[6][e], vf[7][e])});
     }
+    after_stage();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -317,14 +335,21 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
         vf[i] = ok ? (STREAM ? load16_nt(vp) : load16(vp)) : u32x4{0, 0, 0, 0};
       }
 
-      tile_compute(kt, bok, kf, vf);
+      tile_compute(
+          kt, bok, [&](int kb, int c) { return kf[kb][c]; }, [&](int i, int e) { return vf[i][e]; }, [] {});
     }
   } else {
-    // 8-bit K/V: each wave loads two of its tiles at once (half the bytes of
-    // a 16-bit tile each), the second tile's loads in flight while the first
-    // is computed. The page rows of both tiles are read before any tile load
-    // is issued (loads retire in order: waiting for a page id read after a
-    // tile's loads would wait for those loads too).
+    // 8-bit K/V, software-pipelined: each wave keeps the loads of its next
+    // two tiles in flight. A tile's registers are refilled with the loads of
+    // the tile two steps on as soon as its K and V have been converted and
+    // staged, before its PV product, so the loads run under the compute.
+    // Every load is an unconditional buffer load: a 16-key block gets a
+    // buffer resource whose range ends after its last key in bounds (none
+    // for a block past the split or on a page outside the pool), so keys out
+    // of range read as zeros with no branch, and the load counter waits can
+    // name the exact tile they need. The page ids of a tile's two blocks
+    // (lanes 0 and 1 of one vector load) are read one step ahead, in the
+    // same in-order stream as the tile loads.
     // K: lane (key col, row) loads 16 codes, bytes [16 (row + 4 hh), +16) of
     // its key; MFMA step c takes d-chunk 2 row + (c & 1) + 8 (c >> 1), as Q.
     // V: lane (d-chunk col, key group row) loads 8 codes of keys 4 row + i
@@ -332,52 +357,122 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
     struct Raw {
       u32x4 k[2][2];
       u32x2 v[8];
-      long rbase[2];
       bool bok[2];
     };
-    auto load_raw = [&](int kt, Raw& r) {
+    constexpr int kAux = STREAM ? 2 : 0;   // buffer-load cache policy: nt
+    const __amdgpu_buffer_rsrc_t r_bt =
+        make_rsrc(PAGED ? p.bt + (size_t)b * p.max_pages : p.bt, PAGED ? (uint32_t)p.max_pages * 4u : 0u);
+    // Paged: a cursor per use walks one slot's tiles (every (2 dt)-th tile
+    // of the wave) as (table index, key offset in the page) of the tile's
+    // first key, advanced by adds instead of a division per tile. Blocks
+    // start at multiples of 16 keys and pages hold multiples of 16, so a
+    // tile's second block is 16 keys on, in the same page or at the start of
+    // the next. Entries past the table read as zero through r_bt's range;
+    // their keys lie past the sequence and are excluded anyway.
+    struct Cursor {
+      int idx, off;
+    };
+    const int ps = PAGED ? p.page_size : 16;
+    const int slot_keys = 2 * dt * kTile;
+    const int adv_pages = PAGED ? slot_keys / ps : 0, adv_keys = PAGED ? slot_keys % ps : 0;
+    auto cursor_at = [&](int t) {
+      const int key0 = k_lo + t * kTile;
+      return Cursor{PAGED ? key0 / ps : 0, PAGED ? key0 % ps : 0};
+    };
+    auto advance = [&](Cursor& c) {
+      c.idx += adv_pages;
+      c.off += adv_keys;
+      if (c.off >= ps) {
+        c.off -= ps;
+        ++c.idx;
+      }
+    };
+    // page ids of the tile at cursor c: block 0 on lane 0, block 1 on lane 1
+    auto page_load = [&](Cursor& c) -> int {
+      if constexpr (!PAGED) return 0;
+      const int i1 = c.idx + (c.off + 16 >= ps ? 1 : 0);
+      const int pg = (int)__builtin_amdgcn_raw_buffer_load_b32(r_bt, ((lane & 1) ? i1 : c.idx) * 4, 0, 0);
+      advance(c);
+      return pg;
+    };
+    // per-lane byte offsets inside a block (all in the vector offset, which
+    // the range check covers)
+    const int row_bytes = (int)kstride * kD;
+    const int k_off = col * row_bytes + row * 16;
+    const int v_off = row * 4 * row_bytes + col * 8;
+    auto issue = [&](int t, int pg, Cursor& c, Raw& r) {
+      const int kt = k_lo + t * kTile;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bool ok = r.bok[kb] && kt + kb * 16 + col < k_hi;
-        const KE* kp = k_el + (r.rbase[kb] + (ok ? col : 0) * kstride) * kD + row * 16;
+        const int key0 = kt + kb * 16;
+        bool ok = key0 < k_hi;
+        long rb;
+        if (PAGED) {
+          const int page = __builtin_amdgcn_readlane(pg, kb);
+          ok = ok && page >= 0 && page < p.num_pages;
+          const int off = kb == 0 ? c.off : (c.off + 16 >= ps ? c.off + 16 - ps : c.off + 16);
+          rb = ((long)(ok ? page : 0) * ps + off) * p.h_kv + kvh;
+        } else {
+          rb = ((long)b * p.h_kv + kvh) * p.s_max + key0;
+        }
+        const int nv = ok ? min(16, k_hi - key0) : 0;
+        r.bok[kb] = ok;
+        const uint32_t bytes = nv > 0 ? (uint32_t)(((long)(nv - 1) * kstride + 1) * kD) : 0u;
+        const __amdgpu_buffer_rsrc_t kr = make_rsrc(k_el + rb * kD, bytes);
+        const __amdgpu_buffer_rsrc_t vr = make_rsrc(v_el + rb * kD, bytes);
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
-          r.k[kb][hh] = ok ? (STREAM ? load16_nt(kp + 64 * hh) : load16(kp + 64 * hh)) : u32x4{0, 0, 0, 0};
+          r.k[kb][hh] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, k_off + 64 * hh, 0, kAux));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          r.v[kb * 4 + i] = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_raw_buffer_load_b64(vr, v_off + i * row_bytes, 0, kAux));
       }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int kb = i >> 2;
-        const int ko = row * 4 + (i & 3);
-        const bool ok = r.bok[kb] && kt + kb * 16 + ko < k_hi;
-        const KE* vp = v_el + (r.rbase[kb] + ko * kstride) * kD + col * 8;
-        r.v[i] = ok ? (STREAM ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vp))
-                              : *reinterpret_cast<const u32x2*>(vp))
-                    : u32x2{0, 0};
-      }
+      if (PAGED) advance(c);
     };
-    auto compute_raw = [&](int kt, const Raw& r) {
-      u32x4 kf[2][4], vf[8];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          kf[kb][2 * hh] = cvt8<DT>(u32x2{r.k[kb][hh][0], r.k[kb][hh][1]});
-          kf[kb][2 * hh + 1] = cvt8<DT>(u32x2{r.k[kb][hh][2], r.k[kb][hh][3]});
-        }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) vf[i] = cvt8<PDT>(r.v[i]);
-      tile_compute(kt, r.bok, kf, vf);
+    auto compute8 = [&](int t, Raw& r, auto&& refill) {
+      tile_compute(
+          k_lo + t * kTile, r.bok,
+          [&](int kb, int c) {
+            const u32x4 w = r.k[kb][c >> 1];
+            return (c & 1) ? cvt8<DT>(u32x2{w[2], w[3]}) : cvt8<DT>(u32x2{w[0], w[1]});
+          },
+          [&](int i, int e) { return cvt8w<PDT>(r.v[i][e >> 1], e & 1); }, refill);
     };
-    for (int t = t0; t < n_tiles; t += 2 * dt) {
-      const bool two = t + dt < n_tiles;
-      Raw ra, rb;
-      tile_rows(k_lo + t * kTile, ra.rbase, ra.bok);
-      tile_rows(k_lo + (t + dt) * kTile, rb.rbase, rb.bok);   // past the keys: no valid block
-      load_raw(k_lo + t * kTile, ra);
-      load_raw(k_lo + (t + dt) * kTile, rb);
-      compute_raw(k_lo + t * kTile, ra);
-      if (two) compute_raw(k_lo + (t + dt) * kTile, rb);
+    Raw ra, rb;
+    // load cursors (la, lb) run one slot tile ahead of the issue cursors
+    Cursor la = cursor_at(t0), lb = cursor_at(t0 + dt), ia = la, ib = lb;
+    int pga = page_load(la), pgb = page_load(lb);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(t0, pga, ia, ra);
+    __builtin_amdgcn_sched_barrier(0);
+    pga = page_load(la);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(t0 + dt, pgb, ib, rb);
+    __builtin_amdgcn_sched_barrier(0);
+    pgb = page_load(lb);
+    __builtin_amdgcn_sched_barrier(0);
+    // Whole pairs in the loop, so that its back edge is reached only after
+    // both refills were issued (the load-counter waits at the loop head then
+    // count exactly the loads issued since); an odd last tile after it.
+    int t = t0;
+    for (; t + dt < n_tiles; t += 2 * dt) {
+      compute8(t, ra, [&] {
+        __builtin_amdgcn_sched_barrier(0);
+        issue(t + 2 * dt, pga, ia, ra);
+        __builtin_amdgcn_sched_barrier(0);
+        pga = page_load(la);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      compute8(t + dt, rb, [&] {
+        __builtin_amdgcn_sched_barrier(0);
+        issue(t + 3 * dt, pgb, ib, rb);
+        __builtin_amdgcn_sched_barrier(0);
+        pgb = page_load(lb);
+        __builtin_amdgcn_sched_barrier(0);
+      });
     }
+    if (t < n_tiles) compute8(t, ra, [] {});
   }
 
   if (head_mode) {
