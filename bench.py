@@ -229,19 +229,27 @@ def bench_merge_lse(steps, warmup, dev, copies=3):
                 rotated_input_sets=copies)
 
 
-def bench_decode_large_group(steps, warmup, dev, paged=False):
+def bench_decode_large_group(steps, warmup, dev, paged=False, kv8=False, scales=(0.37, 0.29)):
     """Decode with a 128-head group on one KV head (g = 128, the heads as
     the rows of the prefill kernel): 32 sequences of 32768 keys, 537 MB of
     K+V (more than the 256 MB last-level cache), synthetic N(0,1) drawn on
     the device; contiguous, or (paged) in 16-token pages placed by a seeded
-    permutation of the pool. GB/s = K+V bytes / (split + merge time)."""
+    permutation of the pool. kv8: K and V as E4M3 codes drawn on the device
+    (sign, mantissa and an exponent field in 4..9 uniform; 268 MB), decoded
+    with ``scales``. GB/s = K+V bytes / (split + merge time)."""
     import torch
     from online_softmax_tiled_amd import api
     B, h, h_kv, s, d = 32, 128, 1, 32768, 128
     g = torch.Generator(device=dev).manual_seed(1007)
     q = torch.randn((B, h, d), generator=g, device=dev).to(torch.bfloat16)
-    k = torch.randn((B, h_kv, s, d), generator=g, device=dev).to(torch.bfloat16)
-    v = torch.randn((B, h_kv, s, d), generator=g, device=dev).to(torch.bfloat16)
+    if kv8:
+        def codes():
+            r = torch.randint(0, 96, (B, h_kv, s, d), generator=g, device=dev, dtype=torch.int32)
+            return ((r // 48) * 128 + (4 + (r % 48) // 8) * 8 + r % 8).to(torch.uint8)
+        k, v = codes(), codes()
+    else:
+        k = torch.randn((B, h_kv, s, d), generator=g, device=dev).to(torch.bfloat16)
+        v = torch.randn((B, h_kv, s, d), generator=g, device=dev).to(torch.bfloat16)
     bt, page = None, 16
     if paged:
         n_pg = s // page
@@ -260,17 +268,22 @@ def bench_decode_large_group(steps, warmup, dev, paged=False):
     pl = torch.empty_like(pm)
     o = torch.empty((B, h, d), dtype=q.dtype, device=dev)
     lse = torch.empty((B, h), dtype=torch.float32, device=dev)
-    kv_bytes = 2 * B * h_kv * s * d * 2
+    kv_bytes = 2 * B * h_kv * s * d * (1 if kv8 else 2)
 
     def full(i=0):
-        api.decode_split(q, k, v, sl, chunk, splits, block_table=bt, page_size=page, part_o=po, part_m=pm,
-                         part_l=pl)
+        if kv8:
+            api.decode_split_fp8kv(q, k, v, sl, chunk, splits, scales[0], scales[1], block_table=bt, page_size=page,
+                                   part_o=po, part_m=pm, part_l=pl)
+        else:
+            api.decode_split(q, k, v, sl, chunk, splits, block_table=bt, page_size=page, part_o=po, part_m=pm,
+                             part_l=pl)
         api.merge_states(po, pm, pl, sl, chunk, q.dtype, out=o, lse=lse)
 
     ms, _ = time_loop(full, steps, warmup)
     return dict(kv_bytes=kv_bytes, us_per_step=ms * 1e3, gbs=kv_bytes / (ms * 1e-3) / 1e9,
                 frac_hbm=kv_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, plan=[chunk, splits],
-                shape="B=32 h=128 h_kv=1 s=32768 d=128 bf16" + (", 16-token pages" if paged else ""))
+                shape="B=32 h=128 h_kv=1 s=32768 d=128 bf16" + (", E4M3 K/V" if kv8 else "")
+                + (", 16-token pages" if paged else ""))
 
 
 def bench_decode_contiguous(steps, warmup, dev, copies=40):
@@ -512,6 +525,8 @@ def run_only(args, dev):
         print(json.dumps(bench_merge_lse(args.steps, args.warmup, dev)))
     elif args.only == "decode_g128":
         print(json.dumps(bench_decode_large_group(args.steps, args.warmup, dev)))
+    elif args.only == "decode_g128_fp8":
+        print(json.dumps(bench_decode_large_group(args.steps, args.warmup, dev, kv8=True)))
     elif args.only == "decode_paged":
         from online_softmax_tiled_amd.workloads import make_config
         r = bench_decode_paged(args.steps, args.warmup, dev, make_config("paged_decode_llama3_8b_b64"))
@@ -532,7 +547,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="only the headline prefill")
     ap.add_argument("--only", choices=["prefill", "stress", "chunked", "decode_70b", "decode_paged", "decode_g128",
-                                       "decode_fp8", "decode_fp8_70b", "merge_lse", "copy"],
+                                       "decode_fp8", "decode_fp8_70b", "decode_g128_fp8", "merge_lse", "copy"],
                     default=None,
                     help="run one workload only (for profiler counter runs) and print its timing")
     ap.add_argument("--copy-mb", type=int, default=1024,
@@ -615,6 +630,12 @@ def main():
         r9 = bench_decode_fp8kv(max(20, args.steps), 3, dev, "paged_decode_llama3_8b_b64")
         log(f"decode paged b64 fp8 KV: {r9['us_per_step']:.1f} us/step, {r9['gbs']:.0f} GB/s")
         decode["paged_decode_llama3_8b_b64_fp8kv"] = r9
+        r10 = bench_decode_large_group(max(20, args.steps), 3, dev, kv8=True)
+        log(f"decode g=128 b32 s32768 fp8 KV: {r10['us_per_step']:.1f} us/step, {r10['gbs']:.0f} GB/s")
+        decode["decode_g128_b32_s32768_fp8kv"] = r10
+        r11 = bench_decode_large_group(max(20, args.steps), 3, dev, paged=True, kv8=True)
+        log(f"decode g=128 b32 s32768 paged fp8 KV: {r11['us_per_step']:.1f} us/step, {r11['gbs']:.0f} GB/s")
+        decode["decode_g128_b32_s32768_paged_fp8kv"] = r11
         for v in decode.values():
             for key in list(v):
                 if isinstance(v[key], float):

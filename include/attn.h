@@ -280,8 +280,11 @@ int attn_decode(const void* q, const void* k, const void* v,
  *   k_scale, v_scale  finite and > 0 (else ATTN_ERR_INVALID).
  * Everything else (sizes, plans, partial buffers, the written splits,
  * errors) as attn_decode_split; the partials merge with attn_merge_states.
- * Up to 256 query heads per KV head, in blocks of 16; page sizes any
- * multiple of 16.
+ * Up to 256 query heads per KV head; page sizes any multiple of 16.
+ * Groups of 17-128 heads on contiguous K/V, or on pages whose size is a
+ * power of two in a pool of under 4 GB, run as the rows of the prefill
+ * kernel (as attn_decode_split does for 16-bit K/V); other groups run in
+ * blocks of 16 heads. Both forms write the same partial layout.
  */
 int attn_decode_split_fp8kv(const void* q, const void* k, const void* v,
                             const int32_t* block_table, int max_pages, int page_size, int num_pages,

@@ -33,7 +33,9 @@ hipError_t decode_split_fp8kv(const void* q, const void* k, const void* v, const
 hipError_t decode_split_rows(const void* q, const void* k, const void* v, const int32_t* block_table,
                              int max_pages, int page_shift, int num_pages, const int32_t* seq_lens, int s_max,
                              int B, int h, int h_kv, int chunk_keys, int max_splits, int dtype, float scale,
-                             float* part_o, float* part_m, float* part_l, hipStream_t stream);
+                             float* part_o, float* part_m, float* part_l, hipStream_t stream, bool kv8,
+                             float k_scale, float v_scale);
+bool decode_rows_fp8_supported(int g, bool paged, int num_pages, int h_kv, int page_shift);
 hipError_t merge_states(const float* part_o, const float* part_m, const float* part_l,
                         const int32_t* seq_lens, int chunk_keys, int B, int h, int max_splits,
                         void* o, float* lse, int dtype, hipStream_t stream);
@@ -173,9 +175,28 @@ hipError_t launch_split(const void* q, const void* k, const void* v, const int32
   const int shift = block_table ? log2_exact(page_size) : 0;
   if (h / h_kv >= kRowsMinGroup && shift >= 0)
     return attn::decode_split_rows(q, k, v, block_table, max_pages, shift, num_pages, seq_lens, s_max, B, h, h_kv,
-                                   chunk_keys, max_splits, dtype, scale, part_o, part_m, part_l, stream);
+                                   chunk_keys, max_splits, dtype, scale, part_o, part_m, part_l, stream, false, 1.f,
+                                   1.f);
   return attn::decode_split(q, k, v, block_table, max_pages, page_size, num_pages, seq_lens, s_max, B, h, h_kv,
                             chunk_keys, max_splits, dtype, scale, part_o, part_m, part_l, stream);
+}
+
+// Stage 1 over 8-bit K/V: the heads as rows for 17-128 heads per KV head
+// (power-of-two pages, pools that 32-bit offsets address), else blocks of 16
+// heads.
+hipError_t launch_split_fp8(const void* q, const void* k, const void* v, const int32_t* block_table, int max_pages,
+                            int page_size, int num_pages, const int32_t* seq_lens, int s_max, int B, int h, int h_kv,
+                            int chunk_keys, int max_splits, int dtype, float scale, float k_scale, float v_scale,
+                            float* part_o, float* part_m, float* part_l, hipStream_t stream) {
+  const int shift = block_table ? log2_exact(page_size) : 0;
+  if (h / h_kv >= kRowsMinGroup && shift >= 0 &&
+      attn::decode_rows_fp8_supported(h / h_kv, block_table != nullptr, num_pages, h_kv, shift))
+    return attn::decode_split_rows(q, k, v, block_table, max_pages, shift, num_pages, seq_lens, s_max, B, h, h_kv,
+                                   chunk_keys, max_splits, dtype, scale, part_o, part_m, part_l, stream, true,
+                                   k_scale, v_scale);
+  return attn::decode_split_fp8kv(q, k, v, block_table, max_pages, page_size, num_pages, seq_lens, s_max, B, h, h_kv,
+                                  chunk_keys, max_splits, dtype, scale, k_scale, v_scale, part_o, part_m, part_l,
+                                  stream);
 }
 
 }  // namespace
@@ -309,9 +330,9 @@ int attn_decode_split_fp8kv(const void* q, const void* k, const void* v, const i
   if (int e = check_kv_scales(fn, k_scale, v_scale)) return e;
   if (B == 0) return ok();
   REQUIRE(part_o && part_m && part_l, ATTN_ERR_INVALID, "%s: a required pointer is NULL", fn);
-  return from_hip(attn::decode_split_fp8kv(q, k, v, block_table, max_pages, page_size, num_pages, seq_lens, s_max, B,
-                                           h, h_kv, chunk_keys, max_splits, dtype, scale, k_scale, v_scale, part_o,
-                                           part_m, part_l, static_cast<hipStream_t>(stream)),
+  return from_hip(launch_split_fp8(q, k, v, block_table, max_pages, page_size, num_pages, seq_lens, s_max, B, h, h_kv,
+                                   chunk_keys, max_splits, dtype, scale, k_scale, v_scale, part_o, part_m, part_l,
+                                   static_cast<hipStream_t>(stream)),
                   fn);
 }
 
@@ -329,9 +350,9 @@ int attn_decode_fp8kv(const void* q, const void* k, const void* v, const int32_t
   REQUIRE(part_o && part_m && part_l && o, ATTN_ERR_INVALID, "%s: a required pointer is NULL", fn);
   REQUIRE((long)B * h < (1L << 31), ATTN_ERR_UNSUPPORTED, "%s: grid too large", fn);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = attn::decode_split_fp8kv(q, k, v, block_table, max_pages, page_size, num_pages, seq_lens,
-                                                s_max, B, h, h_kv, chunk_keys, max_splits, dtype, scale, k_scale,
-                                                v_scale, part_o, part_m, part_l, s);
+  const hipError_t e = launch_split_fp8(q, k, v, block_table, max_pages, page_size, num_pages, seq_lens, s_max, B, h,
+                                       h_kv, chunk_keys, max_splits, dtype, scale, k_scale, v_scale, part_o, part_m,
+                                       part_l, s);
   if (e != hipSuccess) return from_hip(e, fn);
   return from_hip(attn::merge_states(part_o, part_m, part_l, seq_lens, chunk_keys, B, h, max_splits, o, lse, dtype, s),
                   fn);

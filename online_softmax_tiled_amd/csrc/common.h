@@ -100,6 +100,36 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t x, float& vmax) {
 }
 constexpr float kF16Overflow = 65536.f;   // smallest bf16 magnitude fp16 cannot hold
 
+// Eight E4M3 codes (two words, code e in byte e % 4 of word e / 4) as eight
+// 16-bit operands of type DT, with gfx950's packed fp8 conversion at scale
+// 1, which is exact (every E4M3 value is an fp16 and a bf16 value); element
+// e lands in half e % 2 of word e / 2, as a 16-bit load would put it.
+template <int DT>
+__device__ __forceinline__ u32x4 cvt8(u32x2 x) {
+  // (the half-word select of the conversion is an immediate)
+  if constexpr (DT == ATTN_DTYPE_BF16)
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[0], 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[0], 1.0f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[1], 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[1], 1.0f, true))};
+  else
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[0], 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[0], 1.0f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[1], 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[1], 1.0f, true))};
+}
+
+// Word sel (0: codes 0-1, 1: codes 2-3) of cvt8 of one word.
+template <int DT>
+__device__ __forceinline__ uint32_t cvt8w(uint32_t w, int sel) {
+  if constexpr (DT == ATTN_DTYPE_BF16)
+    return sel ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))
+               : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  else
+    return sel ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true))
+               : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+}
+
 // Byte select of v_perm_b32: result byte i = byte sel[i] of {hi:lo} (0-3 lo).
 __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);

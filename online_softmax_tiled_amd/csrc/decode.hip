@@ -74,36 +74,6 @@ struct DecodeParams {
   float v_scale;   // 8-bit K/V: V's tensor scale, applied to O~ as it is written
 };
 
-// Eight E4M3 codes (two words, code e in byte e % 4 of word e / 4) as eight
-// 16-bit operands of type DT, with gfx950's packed fp8 conversion at scale
-// 1, which is exact (every E4M3 value is an fp16 and a bf16 value); element
-// e lands in half e % 2 of word e / 2, as a 16-bit load would put it.
-template <int DT>
-__device__ __forceinline__ u32x4 cvt8(u32x2 x) {
-  // (the half-word select of the conversion is an immediate)
-  if constexpr (DT == ATTN_DTYPE_BF16)
-    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[0], 1.0f, false)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[0], 1.0f, true)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[1], 1.0f, false)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[1], 1.0f, true))};
-  else
-    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[0], 1.0f, false)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[0], 1.0f, true)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[1], 1.0f, false)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[1], 1.0f, true))};
-}
-
-// Word sel (0: codes 0-1, 1: codes 2-3) of cvt8 of one word.
-template <int DT>
-__device__ __forceinline__ uint32_t cvt8w(uint32_t w, int sel) {
-  if constexpr (DT == ATTN_DTYPE_BF16)
-    return sel ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))
-               : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
-  else
-    return sel ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true))
-               : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
-}
-
 // Max / sum of x over the four 16-lane rows of a wave (lanes l, l^16,
 // l^32, l^48).
 __device__ __forceinline__ float max_rows16(float x) {

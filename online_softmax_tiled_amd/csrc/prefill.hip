@@ -133,7 +133,7 @@ struct PrefillParams {
   int g;        // h / h_kv
   int n_rb;     // row blocks per (batch, kv head) = g * ceil(T_q / 32)
   int n_grp;    // workgroups per (batch, kv head) = ceil(n_rb / kWaves)
-  float c;      // scale * log2(e)
+  float c;      // scale * log2(e) (times k_scale for 8-bit K/V)
   // Paged, variable-length form (PAGED): Q and O token-major [total_q, h, d]
   // with sequence b at rows cu_q[b] .. cu_q[b+1]; LSE [total_q, h]; K/V in
   // pools [num_pages, page_size, h_kv, d] addressed through the block table;
@@ -160,18 +160,38 @@ struct PrefillParams {
   // when the host knows the key counts; n_order = 0 means natural order.
   int n_order;
   uint16_t order[kMaxOrder];
+  float v_scale;   // 8-bit K/V (DEC): V's tensor scale, applied to the split's O~
 };
 
 // OPT flags: kStagers = decode with staging waves (at most 4 row blocks);
-// kPool32 = paged pool under 4 GB, addressed with 32-bit buffer offsets.
+// kPool32 = paged pool under 4 GB, addressed with 32-bit buffer offsets;
+// kKV8 = K and V hold one OCP E4M3 byte per element (decode with staging
+// waves, contiguous or kPool32): the loads read 8 codes where a 16-bit tile
+// has a 16-byte chunk, and the codes are converted as they are stored to LDS
+// (K to the query type, V to fp16; both exact), so the compute waves see the
+// tiles of the 16-bit form.
 constexpr int kStagers = 1;
 constexpr int kPool32 = 2;
+constexpr int kKV8 = 4;
 
 template <int DT, bool CAUSAL, bool KMASK, bool PAGED, bool DEC, int OPT>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   using E = Elem<DT>;
   constexpr bool stagers = (OPT & kStagers) != 0;
   constexpr bool pool32 = (OPT & kPool32) != 0;
+  constexpr bool kv8 = (OPT & kKV8) != 0;
+  static_assert(!kv8 || (DEC && stagers && (!PAGED || pool32)), "8-bit K/V: decode with staging waves");
+  constexpr uint32_t kEB = kv8 ? 1u : 2u;   // bytes per stored K/V element
+  // Raw load of 8 K/V elements, and its 16-bit form for the LDS tiles.
+  using KVRaw = std::conditional_t<kv8, u32x2, u32x4>;
+  auto kv_load = [](__amdgpu_buffer_rsrc_t r, uint32_t byte_off) -> KVRaw {
+    if constexpr (kv8) return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)byte_off, 0, 0));
+    else return buffer_load16(r, byte_off);
+  };
+  auto k16 = [](KVRaw x) -> u32x4 {
+    if constexpr (kv8) return cvt8<DT>(x);
+    else return x;
+  };
   static_assert(!PAGED || KMASK, "paged K/V are addressed through the key-bit path");
   static_assert(!stagers || DEC, "staging waves are a decode form (at most 4 row blocks)");
   static_assert(!pool32 || PAGED, "32-bit pool offsets are a paged form");
@@ -267,17 +287,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
 
   const size_t kv_base = PAGED ? 0 : DEC ? ((size_t)bk * p.s_max + k_lo) * kD : (size_t)bk * T_k * kD;
   // (kPool32: the whole pools)
-  const uint32_t kv_range = PAGED ? (pool32 ? p.pool_bytes : 0u) : (uint32_t)T_k * kD * 2;
-  const auto rk = make_rsrc(p.k + kv_base, kv_range);
-  const auto rv = make_rsrc(p.v + kv_base, kv_range);
+  const uint32_t kv_range = PAGED ? (pool32 ? p.pool_bytes : 0u) : (uint32_t)T_k * kD * kEB;
+  const auto rk = make_rsrc(reinterpret_cast<const uint8_t*>(p.k) + kv_base * kEB, kv_range);
+  const auto rv = make_rsrc(reinterpret_cast<const uint8_t*>(p.v) + kv_base * kEB, kv_range);
 
   // Staging: 1024 16-byte chunks per tile for K and for V; chunk tid + 512 i
   // holds key chunk / 16, d-chunk chunk % 16.
-  u32x4 kreg[2], vreg[2];
+  KVRaw kreg[2], vreg[2];
   // (unsigned: the tiles just past the end of the longest key range lie at
   // about 2^31 bytes, which the buffer range check turns into zeros)
   auto tile_byte = [&](int t, int i) {
-    return ((uint32_t)(t * kBc + ((tid + kThreads * i) >> 4)) * kD + (uint32_t)(tid & 15) * 8u) * 2u;
+    return ((uint32_t)(t * kBc + ((tid + kThreads * i) >> 4)) * kD + (uint32_t)(tid & 15) * 8u) * kEB;
   };
   // Per-lane loads that decide masking (block-table entries, key-mask bytes)
   // are range-checked buffer loads over the sequence's row: past its end
@@ -317,56 +337,64 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   // past the pool's range (reads zeros) when the row is past T_k or the page
   // lies outside the pool.
   const uint32_t main_lane_off =
-      ((uint32_t)(lane >> 4) * (uint32_t)p.h_kv + (uint32_t)kvh) * (kD * 2u) + (uint32_t)(tid & 15) * 16u;
+      ((uint32_t)(lane >> 4) * (uint32_t)p.h_kv + (uint32_t)kvh) * (kD * kEB) + (uint32_t)(tid & 15) * 8u * kEB;
   auto pool_off = [&](int t, int i, int page) -> uint32_t {
     const int g = t * kBc + 4 * wave + 32 * i;   // first key of the wave's 4 rows, counted from k_lo
     const bool ok = (uint32_t)page < (uint32_t)p.num_pages;
     const uint32_t slot0 = (uint32_t)(k_lo + g) & ((1u << p.page_shift) - 1u);
-    const uint32_t go = ok ? (uint32_t)page * p.page_bytes + slot0 * (uint32_t)p.h_kv * (kD * 2u) : p.pool_bytes;
+    const uint32_t go = ok ? (uint32_t)page * p.page_bytes + slot0 * (uint32_t)p.h_kv * (kD * kEB) : p.pool_bytes;
     return g + (lane >> 4) < T_k ? go + main_lane_off : 0xFFFFFFF0u;
   };
   int pg_k[2] = {-1, -1}, pg_v[2] = {-1, -1}, pg_n[2] = {-1, -1};
   auto load_k = [&](int t) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      if (PAGED && pool32) {
-        kreg[i] = buffer_load16(rk, pool_off(t, i, pg_k[i]));
-      } else if (PAGED) {
+      if constexpr (PAGED && pool32) {
+        kreg[i] = kv_load(rk, pool_off(t, i, pg_k[i]));
+      } else if constexpr (PAGED && !kv8) {
         const long r = paged_row(t, i, pg_k[i]);
         kreg[i] = r >= 0 ? load16(p.k + r * kD + (tid & 15) * 8) : u32x4{0u, 0u, 0u, 0u};
       } else {
-        kreg[i] = buffer_load16(rk, tile_byte(t, i));
+        kreg[i] = kv_load(rk, tile_byte(t, i));
       }
     }
   };
   auto load_v = [&](int t) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      if (PAGED && pool32) {
-        vreg[i] = buffer_load16(rv, pool_off(t, i, pg_v[i]));
-      } else if (PAGED) {
+      if constexpr (PAGED && pool32) {
+        vreg[i] = kv_load(rv, pool_off(t, i, pg_v[i]));
+      } else if constexpr (PAGED && !kv8) {
         const long r = paged_row(t, i, pg_v[i]);
         vreg[i] = r >= 0 ? load16(p.v + r * kD + (tid & 15) * 8) : u32x4{0u, 0u, 0u, 0u};
       } else {
-        vreg[i] = buffer_load16(rv, tile_byte(t, i));
+        vreg[i] = kv_load(rv, tile_byte(t, i));
       }
     }
   };
   auto store_k = [&](int slot) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) store16(&lds_k[slot][((tid + kThreads * i) >> 4) * kKStr + (tid & 15) * 8], kreg[i]);
+    for (int i = 0; i < 2; ++i)
+      store16(&lds_k[slot][((tid + kThreads * i) >> 4) * kKStr + (tid & 15) * 8], k16(kreg[i]));
   };
   // V tiles reach LDS in the element type of the PV product: fp16 in the
   // fp16 pass (bf16 inputs are converted here, exactly below 65536 in
   // magnitude; v_max records the largest magnitude staged), the input type
   // in the fallback pass.
+  // (8-bit V: codes straight to the pass's type; at most 448 in magnitude,
+  // they never take the bf16 pass.)
   float v_max = 0.f;
-  auto conv_v = [&](u32x4 x, auto pv16) -> u32x4 {
-    if constexpr (decltype(pv16)::value && DT == ATTN_DTYPE_BF16) {
+  auto conv_v = [&](KVRaw raw, auto pv16) -> u32x4 {
+    if constexpr (kv8) {
+      return cvt8<decltype(pv16)::value ? ATTN_DTYPE_F16 : DT>(raw);
+    } else {
+      u32x4 x = raw;
+      if constexpr (decltype(pv16)::value && DT == ATTN_DTYPE_BF16) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = bf16x2_to_f16x2(x[e], v_max);
+        for (int e = 0; e < 4; ++e) x[e] = bf16x2_to_f16x2(x[e], v_max);
+      }
+      return x;
     }
-    return x;
   };
   auto store_v = [&](int slot, auto pv16) {
 #pragma unroll
@@ -559,7 +587,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     // constant; a group past the keys or on a page outside the pool gets the
     // pool's size, past the range, which reads zeros.
     const uint32_t lane_off =
-        ((uint32_t)(st >> 4) * (uint32_t)p.h_kv + (uint32_t)kvh) * (kD * 2u) + (uint32_t)(st & 15) * 16u;
+        ((uint32_t)(st >> 4) * (uint32_t)p.h_kv + (uint32_t)kvh) * (kD * kEB) + (uint32_t)(st & 15) * 8u * kEB;
     auto grp_page = [&](int t, int i) -> int {   // first key of the group: t * kBc + 16 i from k_lo
       return bt_row[min((k_lo + t * kBc + 16 * i) >> p.page_shift, p.max_pages - 1)];
     };
@@ -567,7 +595,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
       const int g = t * kBc + 16 * i;
       const bool ok = g < T_k && (uint32_t)page < (uint32_t)p.num_pages;
       const uint32_t slot0 = (uint32_t)(k_lo + g) & ((1u << p.page_shift) - 1u);
-      return ok ? (uint32_t)page * p.page_bytes + slot0 * (uint32_t)p.h_kv * (kD * 2u) : p.pool_bytes;
+      return ok ? (uint32_t)page * p.page_bytes + slot0 * (uint32_t)p.h_kv * (kD * kEB) : p.pool_bytes;
     };
     // Paged: a chunk whose row is past the keys or on a page outside the pool
     // reads zeros through an offset past the pool's range (kPool32), or, with
@@ -576,17 +604,24 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     // conditional load would make the compiler count it as possibly not
     // issued and wait for later loads too.
     auto s_load = [&](const uint16_t* pool, const decltype(rk)& r, int t, int i, int page, uint32_t& ok,
-                      int bit) -> u32x4 {
-      if (!PAGED) return buffer_load16(r, ((uint32_t)(t * kBc + s_row(i)) * kD + (uint32_t)(st & 15) * 8u) * 2u);
-      const int key_l = t * kBc + s_row(i);
-      if (pool32) return buffer_load16(r, key_l < T_k ? grp_off(t, i, page) + lane_off : 0xFFFFFFF0u);
-      const bool valid = key_l < T_k && page >= 0 && page < p.num_pages;
-      const long row =
-          valid ? (((long)page << p.page_shift) + ((k_lo + key_l) & ((1 << p.page_shift) - 1))) * p.h_kv + kvh : 0;
-      ok |= valid ? 1u << bit : 0u;
-      return load16(pool + row * kD + (st & 15) * 8);
+                      int bit) -> KVRaw {
+      if constexpr (!PAGED) {
+        return kv_load(r, ((uint32_t)(t * kBc + s_row(i)) * kD + (uint32_t)(st & 15) * 8u) * kEB);
+      } else {
+        const int key_l = t * kBc + s_row(i);
+        if constexpr (pool32) {
+          return kv_load(r, key_l < T_k ? grp_off(t, i, page) + lane_off : 0xFFFFFFF0u);
+        } else {
+          const bool valid = key_l < T_k && page >= 0 && page < p.num_pages;
+          const long row =
+              valid ? (((long)page << p.page_shift) + ((k_lo + key_l) & ((1 << p.page_shift) - 1))) * p.h_kv + kvh
+                    : 0;
+          ok |= valid ? 1u << bit : 0u;
+          return load16(pool + row * kD + (st & 15) * 8);
+        }
+      }
     };
-    u32x4 sk[2][4], sv[2][4];
+    KVRaw sk[2][4], sv[2][4];
     uint32_t ok[2] = {0u, 0u};
     int pgk[2][4], pgv[2][4];   // paged: pages of the K and V loads of the next two iterations
     auto lookup = [&](int u, int tk, int tv) {
@@ -606,11 +641,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
       }
     };
     auto put = [&](int j, int u) {
-      const u32x4 zero = {0u, 0u, 0u, 0u};
+      const KVRaw zero = {};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool as_is = !PAGED || pool32;
-        store16(&lds_k[j & 1][s_row(i) * kKStr + (st & 15) * 8], as_is || (ok[u] >> i & 1u) ? sk[u][i] : zero);
+        store16(&lds_k[j & 1][s_row(i) * kKStr + (st & 15) * 8], k16(as_is || (ok[u] >> i & 1u) ? sk[u][i] : zero));
         store16(&lds_v[(j + 1) % 3][s_row(i) * kVStr + (st & 15) * 8],
                 conv_v(as_is || (ok[u] >> (4 + i) & 1u) ? sv[u][i] : zero, pv16));
       }
@@ -833,10 +868,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   if (DEC) {
     // Partial state of the split at the reference m: O~ accumulated the
     // rounded weights, so it is scaled by l / l~ to pair with l (the merge
-    // divides the combined O~ by the combined l). No visible key: m = -inf,
-    // l = 0, O~ = 0.
+    // divides the combined O~ by the combined l), and, with 8-bit V, by V's
+    // tensor scale. No visible key: m = -inf, l = 0, O~ = 0.
     const bool none = l_tot == 0.f;
-    const float rs = none ? 0.f : l_tot / lr_tot;
+    const float rs = none ? 0.f : l_tot / lr_tot * (kv8 ? p.v_scale : 1.f);
     const size_t hs = ((size_t)b * p.h + head + qrow) * p.max_splits + split;
     float* po = p.part_o + hs * kD;
 #pragma unroll
@@ -884,12 +919,21 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
 }
 
 // Split-KV decode on the prefill kernel (paged launches take the key-bit
-// path for page ids outside the pool).
-template <int DT, bool PAGED>
+// path for page ids outside the pool). 8-bit K/V: staging waves only (at
+// most 128 heads), contiguous or with 32-bit pool offsets.
+template <int DT, bool PAGED, bool KV8>
 hipError_t launch_decode_rows(const PrefillParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((long)p.B * p.h_kv * p.max_splits));
   const bool stg = p.n_rb <= 4;
-  if constexpr (PAGED) {
+  if constexpr (KV8) {
+    if (!stg || (PAGED && p.pool_bytes == 0)) return hipErrorInvalidValue;
+    if constexpr (PAGED)
+      hipLaunchKernelGGL((prefill_kernel<DT, false, true, true, true, kStagers | kPool32 | kKV8>), grid,
+                         dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((prefill_kernel<DT, false, false, false, true, kStagers | kKV8>), grid, dim3(kThreads), 0,
+                         stream, p);
+  } else if constexpr (PAGED) {
     if (p.pool_bytes != 0) {
       if (stg)
         hipLaunchKernelGGL((prefill_kernel<DT, false, true, true, true, kStagers | kPool32>), grid, dim3(kThreads), 0,
@@ -922,12 +966,12 @@ hipError_t dispatch_prefill_paged(const PrefillParams& p, bool causal, hipStream
   return causal ? launch_prefill<DT, true, true, true>(p, s) : launch_prefill<DT, false, true, true>(p, s);
 }
 
-// kPool32 when a pool [num_pages, page_size, h_kv, d] is under 4 GB, with
-// room above it for the out-of-range offsets of invalid rows (the pool's size
-// plus an in-page offset must not wrap); else the pool_bytes = 0 left by the
-// caller selects the 64-bit addressing.
-void set_pool32(PrefillParams& p, int num_pages, int h_kv, int page_shift) {
-  const uint64_t page_bytes = ((uint64_t)h_kv << page_shift) * kD * 2;
+// kPool32 when a pool [num_pages, page_size, h_kv, d] of elem_bytes-byte
+// elements is under 4 GB, with room above it for the out-of-range offsets of
+// invalid rows (the pool's size plus an in-page offset must not wrap); else
+// the pool_bytes = 0 left by the caller selects the 64-bit addressing.
+void set_pool32(PrefillParams& p, int num_pages, int h_kv, int page_shift, int elem_bytes = 2) {
+  const uint64_t page_bytes = ((uint64_t)h_kv << page_shift) * kD * (uint64_t)elem_bytes;
   const uint64_t pool_bytes = (uint64_t)num_pages * page_bytes;
   if (pool_bytes + page_bytes <= 0xFFFFFF00ull) {
     p.pool_bytes = (uint32_t)pool_bytes;
@@ -952,6 +996,7 @@ PrefillParams common_params(const void* q, const void* k, const void* v, void* o
   p.n_rb = p.g * ((T_q + kRows - 1) / kRows);
   p.n_grp = (p.n_rb + kWaves - 1) / kWaves;
   p.c = scale * kLog2e;
+  p.v_scale = 1.f;
   return p;
 }
 
@@ -1000,10 +1045,14 @@ hipError_t prefill_paged(const void* q, const int32_t* cu_seqlens_q, int max_q, 
 // Split-KV decode with the query heads of a group as the MFMA rows: the
 // stage-1 producer for groups of more than 16 heads (up to 256, one wave per
 // 32 heads). page_shift < 0 means contiguous K/V [B, h_kv, s_max, d].
+// kv8: K and V are E4M3 codes with tensor scales k_scale and v_scale (at most
+// 128 heads per KV head; paged pools must fit 32-bit offsets, see
+// decode_rows_fp8_supported).
 hipError_t decode_split_rows(const void* q, const void* k, const void* v, const int32_t* block_table,
                              int max_pages, int page_shift, int num_pages, const int32_t* seq_lens, int s_max,
                              int B, int h, int h_kv, int chunk_keys, int max_splits, int dtype, float scale,
-                             float* part_o, float* part_m, float* part_l, hipStream_t stream) {
+                             float* part_o, float* part_m, float* part_l, hipStream_t stream, bool kv8,
+                             float k_scale, float v_scale) {
   PrefillParams p = common_params(q, k, v, nullptr, nullptr, B, h, h_kv, h / h_kv, 0, scale);
   p.n_rb = (p.g + kRows - 1) / kRows;
   p.n_grp = 1;
@@ -1018,12 +1067,34 @@ hipError_t decode_split_rows(const void* q, const void* k, const void* v, const 
   p.chunk = chunk_keys;
   p.max_splits = max_splits;
   p.s_max = s_max;
+  if (kv8) {
+    p.c *= k_scale;   // scores (q . k_code) k_scale, in the one multiply by scale log2(e)
+    p.v_scale = v_scale;
+  }
   const bool paged = block_table != nullptr;
-  if (paged) set_pool32(p, num_pages, h_kv, page_shift);
+  if (paged) set_pool32(p, num_pages, h_kv, page_shift, kv8 ? 1 : 2);
   if (B == 0 || h == 0) return hipSuccess;
-  if (dtype == ATTN_DTYPE_BF16)
-    return paged ? launch_decode_rows<ATTN_DTYPE_BF16, true>(p, stream) : launch_decode_rows<ATTN_DTYPE_BF16, false>(p, stream);
-  return paged ? launch_decode_rows<ATTN_DTYPE_F16, true>(p, stream) : launch_decode_rows<ATTN_DTYPE_F16, false>(p, stream);
+  const bool bf = dtype == ATTN_DTYPE_BF16;
+  if (kv8) {
+    if (bf) return paged ? launch_decode_rows<ATTN_DTYPE_BF16, true, true>(p, stream)
+                         : launch_decode_rows<ATTN_DTYPE_BF16, false, true>(p, stream);
+    return paged ? launch_decode_rows<ATTN_DTYPE_F16, true, true>(p, stream)
+                 : launch_decode_rows<ATTN_DTYPE_F16, false, true>(p, stream);
+  }
+  if (bf) return paged ? launch_decode_rows<ATTN_DTYPE_BF16, true, false>(p, stream)
+                       : launch_decode_rows<ATTN_DTYPE_BF16, false, false>(p, stream);
+  return paged ? launch_decode_rows<ATTN_DTYPE_F16, true, false>(p, stream)
+               : launch_decode_rows<ATTN_DTYPE_F16, false, false>(p, stream);
+}
+
+// Whether decode_split_rows takes 8-bit K/V of this shape: staging waves
+// (g <= 128) and, paged, a pool that 32-bit offsets address.
+bool decode_rows_fp8_supported(int g, bool paged, int num_pages, int h_kv, int page_shift) {
+  if (g > 4 * kRows) return false;
+  if (!paged) return true;
+  PrefillParams p = {};
+  set_pool32(p, num_pages, h_kv, page_shift, 1);
+  return p.pool_bytes != 0;
 }
 
 }  // namespace attn

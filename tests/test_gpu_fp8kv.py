@@ -67,14 +67,79 @@ def test_fp8kv_decode_small(paged, page_size, dtype, one_call):
         assert_outputs(o, lse, o_ref, lse_ref, dtype, f"fp8 KV decode paged={paged} plan={used} one_call={one_call}")
 
 
-@pytest.mark.parametrize("h,h_kv,paged", [(64, 2, False), (128, 1, True), (40, 2, True)])
-def test_fp8kv_decode_large_groups(h, h_kv, paged):
-    # more than 16 query heads per KV head: head blocks of 16 on the same kernel
+@pytest.mark.parametrize("h,h_kv,paged,page_size", [(64, 2, False, 32), (128, 1, True, 32), (40, 2, True, 48),
+                                                   (256, 1, False, 16), (160, 1, True, 48)])
+def test_fp8kv_decode_large_groups(h, h_kv, paged, page_size):
+    # more than 16 query heads per KV head: the heads as rows (up to 128,
+    # power-of-two pages), else head blocks of 16 on the split kernel (pages
+    # of 48 keys, 160 and 256 heads)
     dec = make_decode(B=3, h=h, h_kv=h_kv, d=128, dtype="bf16", seed=h + h_kv, seq_lens=[777, 64, 2049],
-                      paged=paged, page_size=32, spare_pages=2, kv_codes=True)
+                      paged=paged, page_size=page_size, spare_pages=2, kv_codes=True)
     o_ref, lse_ref = oracle_fp8(dec, K_SCALE, V_SCALE)
     o, lse, _ = run_fp8(dec, K_SCALE, V_SCALE)
     assert_outputs(o, lse, o_ref, lse_ref, "bf16", f"fp8 KV decode g={h // h_kv}")
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "paged16", "paged64"])
+@pytest.mark.parametrize("g", [17, 24, 32, 64, 128])
+def test_fp8kv_decode_heads_as_rows(g, layout):
+    # 17-128 query heads per KV head (power-of-two pages) take the prefill
+    # kernel with the heads as its rows; its staging waves convert the codes
+    # as they store the K/V tiles
+    paged = layout != "contiguous"
+    h_kv = 2 if g <= 32 else 1
+    dtype = "f16" if g in (24, 128) else "bf16"
+    dec = make_decode(B=3, h=g * h_kv, h_kv=h_kv, d=128, dtype=dtype, seed=900 + g, seq_lens=[1000, 33, 2500],
+                      paged=paged, page_size=64 if layout == "paged64" else 16, spare_pages=2, kv_codes=True)
+    o_ref, lse_ref = oracle_fp8(dec, K_SCALE, V_SCALE)
+    for plan in (None, (64, 40), (512, 5), (16, 157)):
+        o, lse, used = run_fp8(dec, K_SCALE, V_SCALE, plan, one_call=plan != (512, 5))
+        assert_outputs(o, lse, o_ref, lse_ref, dtype, f"fp8 KV decode rows g={g} {layout} plan={used}")
+
+
+_UNDER_4GB = lambda page_bytes: 0xFFFFFF00 // page_bytes - 1
+_OVER_4GB = lambda page_bytes: (1 << 32) // page_bytes + 64
+
+
+@pytest.mark.parametrize("size", ["under_4gb", "over_4gb"])
+def test_fp8kv_decode_rows_large_pools(size):
+    # 8-bit pools of 16-key pages (NaN code 0x7F everywhere else) just under
+    # the largest the rows form addresses with 32-bit offsets, and just over
+    # 4 GB (blocks of 16 heads then); half the used pages at the top of the
+    # pool, one table entry outside the pool (its keys are excluded)
+    page_bytes = 16 * 128
+    n_big = (_UNDER_4GB if size == "under_4gb" else _OVER_4GB)(page_bytes)
+    assert (n_big * page_bytes + page_bytes <= 0xFFFFFF00) == (size == "under_4gb")
+    k_big = torch.empty((n_big, 16, 1, 128), dtype=torch.uint8, device=DEV)
+    v_big = torch.empty_like(k_big)
+    lens = [500, 77]
+    dec = make_decode(B=2, h=64, h_kv=1, d=128, dtype="bf16", seed=47, seq_lens=lens, paged=True, page_size=16,
+                      kv_codes=True)
+    n_used = dec["k_pool"].shape[0]
+    new_id = np.array([n_big - 1 - p if p % 2 == 0 else p for p in range(n_used)], dtype=np.int64)
+    assert 0 not in new_id
+    k_big.fill_(0x7F)
+    v_big.fill_(0x7F)
+    idx = torch.from_numpy(new_id).to(DEV)
+    k_big[idx] = to_dev(dec["k_pool"])
+    v_big[idx] = to_dev(dec["v_pool"])
+    bt = dec["block_table"].astype(np.int64)
+    bt = np.where(bt >= 0, new_id[np.maximum(bt, 0)], -1).astype(np.int32)
+    bt[0, 3] = n_big + 9                       # keys 48..63 of sequence 0
+    keep0 = np.r_[0:48, 64:500]
+    kept = dict(dec, k_seqs=[dec["k_seqs"][0][:, keep0], dec["k_seqs"][1]],
+                v_seqs=[dec["v_seqs"][0][:, keep0], dec["v_seqs"][1]], seq_lens=np.array([keep0.size, 77]))
+    o_ref, lse_ref = oracle_fp8(kept, K_SCALE, V_SCALE)
+    sl = to_dev(dec["seq_lens"])
+    for plan in (None, (64, 9)):
+        o, lse, used = api.decode_fp8kv(to_dev(dec["q"]), k_big, v_big, sl, K_SCALE, V_SCALE,
+                                        seq_lens_host=dec["seq_lens"], block_table=to_dev(bt), page_size=16,
+                                        scale=dec["scale"], plan=plan)
+        torch.cuda.synchronize()
+        assert_outputs(o, lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16",
+                       f"fp8 KV decode g=64 on {size} pools of {n_big} pages plan={used}")
+    del k_big, v_big
+    torch.cuda.empty_cache()
 
 
 def test_fp8kv_every_finite_code():
