@@ -384,11 +384,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   // (8-bit V: codes straight to the pass's type; at most 448 in magnitude,
   // they never take the bf16 pass.)
   float v_max = 0.f;
-  auto conv_v = [&](KVRaw raw, auto pv16) -> u32x4 {
+  auto conv_v = [&](KVRaw x, auto pv16) -> u32x4 {
     if constexpr (kv8) {
-      return cvt8<decltype(pv16)::value ? ATTN_DTYPE_F16 : DT>(raw);
+      return cvt8<decltype(pv16)::value ? ATTN_DTYPE_F16 : DT>(x);
     } else {
-      u32x4 x = raw;
       if constexpr (decltype(pv16)::value && DT == ATTN_DTYPE_BF16) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = bf16x2_to_f16x2(x[e], v_max);
