@@ -399,6 +399,31 @@ const char* attn_last_error(void);
 /* Library version string. */
 const char* attn_version(void);
 
+/*
+ * Device-side bounds checks (debug build). libattn_checked.so is built from
+ * the same sources with ATTN_DEVICE_CHECKS defined: before every global
+ * memory access that is not made through a range-checked buffer resource,
+ * and for every buffer range a kernel builds, the kernel tests the address
+ * against the extent of its tensor, computed from the call's own sizes. A
+ * failing access is not made (a load gives zeros, a store is dropped) and
+ * the flag of its site (one of ATTN_CHECK_SITES, numbered per kernel and
+ * access in the library's sources) is set. Not a page citation: a test aid
+ * for the index arithmetic of the kernels above.
+ *
+ * attn_check_report: after the device is synchronised, copies the flags
+ *   (1 = some access at that site failed its test since the last clear) into
+ *   hits[0 .. ATTN_CHECK_SITES); n_sites must be at least ATTN_CHECK_SITES.
+ * attn_check_clear: sets every flag to 0 (synchronous).
+ * attn_check_selftest: launches a kernel on `stream` that tests one address
+ *   inside a 64-byte extent from `base` (site 62) and one past it (site 63),
+ *   accessing neither: afterwards flag 63 is set and flag 62 is not.
+ * In the product library (libattn.so) all three return ATTN_ERR_UNSUPPORTED.
+ */
+#define ATTN_CHECK_SITES 64
+int attn_check_report(uint32_t* hits, int n_sites);
+int attn_check_clear(void);
+int attn_check_selftest(const void* base, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

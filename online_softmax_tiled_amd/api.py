@@ -8,6 +8,7 @@ library's HIP kernels; there is no fallback. If the library is missing or
 fails to load, every call raises.
 """
 
+import contextlib
 import ctypes
 import math
 import os
@@ -17,6 +18,8 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattn.so")
+# The bounds-checking debug build of the same sources (see checked_library).
+CHECKED_LIB_PATH = os.path.join(_HERE, "libattn_checked.so")
 
 DTYPE_CODES = {torch.float16: 0, torch.bfloat16: 1}
 HEAD_DIM = 128
@@ -40,12 +43,18 @@ _SIGNATURES = {
     "attn_merge_lse": [_c_void_p] * 4 + [_c_int] * 2 + [_c_void_p, _c_void_p, _c_int, _c_void_p],
     "attn_paged_gather": [_c_void_p] * 3 + [_c_int] * 8 + [_c_void_p, _c_void_p],
     "attn_stream_read": [_c_void_p, ctypes.c_uint64, _c_int, _c_void_p, _c_void_p],
+    "attn_check_report": [_c_void_p, _c_int],
+    "attn_check_clear": [],
+    "attn_check_selftest": [_c_void_p, _c_void_p],
     "attn_last_error": [],
     "attn_version": [],
 }
 EXPORTS = tuple(_SIGNATURES)
+CHECK_SITES = 64   # ATTN_CHECK_SITES
 
 _lib = None
+_checked_lib = None
+_active = None     # a library that load() returns instead (checked_library)
 
 
 class AttnError(RuntimeError):
@@ -56,22 +65,63 @@ class AttnError(RuntimeError):
         self.code = code
 
 
-def load():
-    """Load libattn.so once. torch is imported first so that the library's
-    HIP runtime dependency (libamdhip64.so.7) binds to the copy torch already
-    loaded: one runtime per process, so torch's streams are valid here."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m online_softmax_tiled_amd.build`")
-    lib = ctypes.CDLL(LIB_PATH)
+def _open(path):
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m online_softmax_tiled_amd.build`")
+    lib = ctypes.CDLL(path)
     for name, args in _SIGNATURES.items():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_char_p if name in ("attn_last_error", "attn_version") else ctypes.c_int
-    _lib = lib
     return lib
+
+
+def load():
+    """Load libattn.so once. torch is imported first so that the library's
+    HIP runtime dependency (libamdhip64.so.7) binds to the copy torch already
+    loaded: one runtime per process, so torch's streams are valid here.
+    Inside ``checked_library()`` the debug library is returned instead."""
+    global _lib
+    if _active is not None:
+        return _active
+    if _lib is None:
+        _lib = _open(LIB_PATH)
+    return _lib
+
+
+@contextlib.contextmanager
+def checked_library():
+    """Route every call made in the block to libattn_checked.so, the build
+    whose kernels test each raw global access against its tensor's extent
+    (include/attn.h, attn_check_report). A test aid: the product library is
+    used again after the block."""
+    global _checked_lib, _active
+    if _checked_lib is None:
+        _checked_lib = _open(CHECKED_LIB_PATH)
+    prev, _active = _active, _checked_lib
+    try:
+        yield _checked_lib
+    finally:
+        _active = prev
+
+
+def check_clear():
+    """Clear the access-check flags (checked library)."""
+    _check("attn_check_clear", load().attn_check_clear())
+
+
+def check_report():
+    """Sites whose access checks failed since the last clear (checked
+    library; the device is synchronised first)."""
+    torch.cuda.synchronize()
+    hits = (ctypes.c_uint32 * CHECK_SITES)()
+    _check("attn_check_report", load().attn_check_report(ctypes.cast(hits, _c_void_p), CHECK_SITES))
+    return [i for i in range(CHECK_SITES) if hits[i]]
+
+
+def check_selftest(base):
+    """Launch the checker's self-test on a device tensor's address."""
+    _check("attn_check_selftest", load().attn_check_selftest(_ptr(base), _stream(base.device)))
 
 
 def version():

@@ -53,6 +53,21 @@ int decode_plan(int B, const int32_t* seq_lens, int units_per_split, int wgs_per
                 int32_t* max_splits);
 hipError_t stream_read(const void* src, uint64_t bytes, int chunks, uint32_t* out, hipStream_t stream);
 size_t decode_scratch_bytes();
+#ifdef ATTN_DEVICE_CHECKS
+hipError_t check_read_decode(uint32_t* hits);
+hipError_t check_read_prefill(uint32_t* hits);
+hipError_t check_read_merge(uint32_t* hits);
+hipError_t check_read_merge_lse(uint32_t* hits);
+hipError_t check_read_gather(uint32_t* hits);
+hipError_t check_read_stream(uint32_t* hits);
+hipError_t check_clear_decode();
+hipError_t check_clear_prefill();
+hipError_t check_clear_merge();
+hipError_t check_clear_merge_lse();
+hipError_t check_clear_gather();
+hipError_t check_clear_stream();
+hipError_t check_selftest(const void* base, hipStream_t stream);
+#endif
 hipError_t decode_scratch(void** ptr);
 }  // namespace attn
 
@@ -464,6 +479,61 @@ int attn_stream_read(const void* src, uint64_t bytes, int chunks, uint32_t* out,
 
 const char* attn_last_error(void) { return g_last_error.c_str(); }
 
-const char* attn_version(void) { return "libattn 0.1 (gfx950)"; }
+const char* attn_version(void) {
+#ifdef ATTN_DEVICE_CHECKS
+  return "libattn 0.1 (gfx950, device bounds checks)";
+#else
+  return "libattn 0.1 (gfx950)";
+#endif
+}
+
+int attn_check_report(uint32_t* hits, int n_sites) {
+  const char* fn = "attn_check_report";
+#ifdef ATTN_DEVICE_CHECKS
+  REQUIRE(hits != nullptr && n_sites >= ATTN_CHECK_SITES, ATTN_ERR_INVALID, "%s: need room for %d sites", fn,
+          (int)ATTN_CHECK_SITES);
+  hipError_t (*readers[])(uint32_t*) = {attn::check_read_decode, attn::check_read_prefill, attn::check_read_merge,
+                                        attn::check_read_merge_lse, attn::check_read_gather, attn::check_read_stream};
+  for (int i = 0; i < ATTN_CHECK_SITES; ++i) hits[i] = 0u;
+  for (auto rd : readers) {
+    uint32_t part[ATTN_CHECK_SITES];
+    const hipError_t e = rd(part);
+    if (e != hipSuccess) return from_hip(e, fn);
+    for (int i = 0; i < ATTN_CHECK_SITES; ++i) hits[i] |= part[i];
+  }
+  return ok();
+#else
+  (void)hits;
+  (void)n_sites;
+  return fail(ATTN_ERR_UNSUPPORTED, "%s: this library was built without device bounds checks", fn);
+#endif
+}
+
+int attn_check_selftest(const void* base, void* stream) {
+  const char* fn = "attn_check_selftest";
+#ifdef ATTN_DEVICE_CHECKS
+  REQUIRE(base != nullptr, ATTN_ERR_INVALID, "%s: base must not be NULL", fn);
+  return from_hip(attn::check_selftest(base, static_cast<hipStream_t>(stream)), fn);
+#else
+  (void)base;
+  (void)stream;
+  return fail(ATTN_ERR_UNSUPPORTED, "%s: this library was built without device bounds checks", fn);
+#endif
+}
+
+int attn_check_clear(void) {
+  const char* fn = "attn_check_clear";
+#ifdef ATTN_DEVICE_CHECKS
+  hipError_t (*clears[])() = {attn::check_clear_decode, attn::check_clear_prefill, attn::check_clear_merge,
+                              attn::check_clear_merge_lse, attn::check_clear_gather, attn::check_clear_stream};
+  for (auto cl : clears) {
+    const hipError_t e = cl();
+    if (e != hipSuccess) return from_hip(e, fn);
+  }
+  return ok();
+#else
+  return fail(ATTN_ERR_UNSUPPORTED, "%s: this library was built without device bounds checks", fn);
+#endif
+}
 
 }  // extern "C"

@@ -165,6 +165,50 @@ __device__ __forceinline__ float sum_halves(float x) {
   return lo + hi;
 }
 
+// Debug build with device-side bounds checks (-DATTN_DEVICE_CHECKS,
+// libattn_checked.so). Every raw global access (one not made through a
+// range-checked buffer resource), and every buffer range a kernel builds, is
+// first tested against the extent of its tensor, computed from the kernel's
+// own parameters. A failing access is not made (a load gives zeros, a store
+// is dropped) and the flag of its site is set with a plain vector store; the
+// host reads the flags back (attn_check_report). In the product build the
+// tests compile away. Sites are numbered across the kernel files (CheckSite).
+enum CheckSite {
+  kSiteDecSeqLens = 0, kSiteDecQ, kSiteDecTable, kSiteDecK16, kSiteDecV16, kSiteDecK8, kSiteDecV8, kSiteDecTable8,
+  kSiteDecPartO, kSiteDecPartML,
+  kSitePreLens = 16, kSitePreQ, kSitePreKV, kSitePreKeyRow, kSitePreTableRow, kSitePrePagedKV, kSitePrePartO,
+  kSitePrePartML, kSitePreO, kSitePreLse, kSitePreRowMask,
+  kSiteMrgLens = 32, kSiteMrgPartML, kSiteMrgPartO, kSiteMrgO, kSiteMrgLse,
+  kSiteMlseIn = 40, kSiteMlseO, kSiteMlseLse,
+  kSiteGthLens = 44, kSiteGthTable, kSiteGthPool, kSiteGthOut,
+  kSiteStream = 48,
+  kSiteSelfTestIn = 62, kSiteSelfTestOut = 63,   // attn_check_selftest
+  kCheckSites = ATTN_CHECK_SITES
+};
+#ifdef ATTN_DEVICE_CHECKS
+static __device__ uint32_t check_hits[kCheckSites];
+__device__ __forceinline__ bool in_range(const void* p, size_t bytes, const void* base, size_t extent, int site) {
+  const char* a = static_cast<const char*>(p);
+  const char* b = static_cast<const char*>(base);
+  const bool ok = a >= b && (size_t)(a - b) + bytes <= extent;
+  if (!ok) check_hits[site] = 1u;
+  return ok;
+}
+#define ATTN_IN_RANGE(p, bytes, base, extent, site) ::attn::in_range((p), (bytes), (base), (extent), (site))
+// The host side of one kernel file's flags (each file has its own array).
+#define ATTN_DEFINE_CHECK_READER(name)                                                        \
+  hipError_t check_read_##name(uint32_t* hits) {                                              \
+    return hipMemcpyFromSymbol(hits, HIP_SYMBOL(check_hits), sizeof(uint32_t) * kCheckSites); \
+  }                                                                                           \
+  hipError_t check_clear_##name() {                                                           \
+    uint32_t z[kCheckSites] = {};                                                             \
+    return hipMemcpyToSymbol(HIP_SYMBOL(check_hits), z, sizeof(z));                           \
+  }
+#else
+#define ATTN_IN_RANGE(p, bytes, base, extent, site) true
+#define ATTN_DEFINE_CHECK_READER(name)
+#endif
+
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 // Streaming load: non-temporal hint, for data read exactly once (decode K/V),
 // so it does not displace reused lines from the caches.

@@ -140,7 +140,14 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
   const int hn = min(16, p.g - hb0);     // heads in this block
   const int b = (int)gz;
   const int split = (int)((gx + gy + gz) % (unsigned)p.max_splits);
-  const int s_raw = p.seq_lens[b];
+#ifdef ATTN_DEVICE_CHECKS
+  // extents of the tensors, in bytes
+  const size_t q_bytes = (size_t)p.B * p.h * kD * 2;
+  const size_t kv_bytes = (PAGED ? (size_t)p.num_pages * p.page_size : (size_t)p.B * p.s_max) * p.h_kv * kD * sizeof(KE);
+  const size_t bt_bytes = (size_t)p.B * p.max_pages * 4;
+  const size_t part_rows = (size_t)p.B * p.h * p.max_splits;
+#endif
+  const int s_raw = ATTN_IN_RANGE(p.seq_lens + b, 4, p.seq_lens, (size_t)p.B * 4, kSiteDecSeqLens) ? p.seq_lens[b] : 0;
   if (s_raw <= 0) return;
   const int n_split = min(p.max_splits, (s_raw + p.chunk - 1) / p.chunk);
   if (split >= n_split) return;
@@ -163,7 +170,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int chunk = KV8 ? 2 * row + (c & 1) + 8 * (c >> 1) : row + 4 * c;
-      qf[c] = ok ? load16(qh + chunk * 8) : u32x4{0, 0, 0, 0};
+      qf[c] = ok && ATTN_IN_RANGE(qh + chunk * 8, 16, p.q, q_bytes, kSiteDecQ) ? load16(qh + chunk * 8)
+                                                                               : u32x4{0, 0, 0, 0};
     }
   }
 
@@ -193,7 +201,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
       const int key0 = kt + kb * 16;
       bok[kb] = key0 < k_hi;
       if (PAGED) {
-        int page = bok[kb] ? p.bt[(size_t)b * p.max_pages + key0 / p.page_size] : 0;
+        const int32_t* pe = p.bt + (size_t)b * p.max_pages + key0 / p.page_size;
+        int page = bok[kb] && ATTN_IN_RANGE(pe, 4, p.bt, bt_bytes, kSiteDecTable) ? *pe : 0;
         page = __builtin_amdgcn_readfirstlane(page);
         bok[kb] = bok[kb] && page >= 0 && page < p.num_pages;
         rbase[kb] = ((long)(bok[kb] ? page : 0) * p.page_size + key0 % p.page_size) * p.h_kv + kvh;
@@ -292,7 +301,10 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
         const bool ok = bok[kb] && kt + kb * 16 + col < k_hi;
         const KE* kp = k_el + (rbase[kb] + (ok ? col : 0) * kstride) * kD + row * 8;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) kf[kb][c] = ok ? (STREAM ? load16_nt(kp + c * 32) : load16(kp + c * 32)) : u32x4{0, 0, 0, 0};
+        for (int c = 0; c < 4; ++c)
+          kf[kb][c] = ok && ATTN_IN_RANGE(kp + c * 32, 16, p.k, kv_bytes, kSiteDecK16)
+                          ? (STREAM ? load16_nt(kp + c * 32) : load16(kp + c * 32))
+                          : u32x4{0, 0, 0, 0};
       }
       // V: lane (d-chunk col, key group row) loads keys 4*row+i and 16+4*row+i.
       u32x4 vf[8];
@@ -302,7 +314,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
         const int ko = row * 4 + (i & 3);
         const bool ok = bok[kb] && kt + kb * 16 + ko < k_hi;
         const KE* vp = v_el + (rbase[kb] + ko * kstride) * kD + col * 8;
-        vf[i] = ok ? (STREAM ? load16_nt(vp) : load16(vp)) : u32x4{0, 0, 0, 0};
+        vf[i] = ok && ATTN_IN_RANGE(vp, 16, p.v, kv_bytes, kSiteDecV16) ? (STREAM ? load16_nt(vp) : load16(vp))
+                                                                        : u32x4{0, 0, 0, 0};
       }
 
       tile_compute(
@@ -330,8 +343,10 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
       bool bok[2];
     };
     constexpr int kAux = STREAM ? 2 : 0;   // buffer-load cache policy: nt
+    const bool bt_ok = !PAGED || ATTN_IN_RANGE(p.bt + (size_t)b * p.max_pages, (size_t)p.max_pages * 4, p.bt, bt_bytes,
+                                               kSiteDecTable8);
     const __amdgpu_buffer_rsrc_t r_bt =
-        make_rsrc(PAGED ? p.bt + (size_t)b * p.max_pages : p.bt, PAGED ? (uint32_t)p.max_pages * 4u : 0u);
+        make_rsrc(PAGED ? p.bt + (size_t)b * p.max_pages : p.bt, PAGED && bt_ok ? (uint32_t)p.max_pages * 4u : 0u);
     // Paged: a cursor per use walks one slot's tiles (every (2 dt)-th tile
     // of the wave) as (table index, key offset in the page) of the tile's
     // first key, advanced by adds instead of a division per tile. Blocks
@@ -387,7 +402,10 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
         }
         const int nv = ok ? min(16, k_hi - key0) : 0;
         r.bok[kb] = ok;
-        const uint32_t bytes = nv > 0 ? (uint32_t)(((long)(nv - 1) * kstride + 1) * kD) : 0u;
+        uint32_t bytes = nv > 0 ? (uint32_t)(((long)(nv - 1) * kstride + 1) * kD) : 0u;
+        if (bytes != 0 && !(ATTN_IN_RANGE(k_el + rb * kD, bytes, p.k, kv_bytes, kSiteDecK8) &&
+                            ATTN_IN_RANGE(v_el + rb * kD, bytes, p.v, kv_bytes, kSiteDecV8)))
+          bytes = 0u;
         const __amdgpu_buffer_rsrc_t kr = make_rsrc(k_el + rb * kD, bytes);
         const __amdgpu_buffer_rsrc_t vr = make_rsrc(v_el + rb * kD, bytes);
 #pragma unroll
@@ -454,8 +472,11 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
       float f = lr_run > 0.f ? l_run / lr_run : 1.f;
       if (KV8) f *= p.v_scale;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(&po[db * 16 + row * 4]) = acc[db] * f;
-      if (row == 0) {
+      for (int db = 0; db < 8; ++db)
+        if (ATTN_IN_RANGE(&po[db * 16 + row * 4], 16, p.part_o, part_rows * kD * 4, kSiteDecPartO))
+          *reinterpret_cast<f32x4*>(&po[db * 16 + row * 4]) = acc[db] * f;
+      if (row == 0 && ATTN_IN_RANGE(p.part_m + hs * p.max_splits + split, 4, p.part_m, part_rows * 4, kSiteDecPartML) &&
+          ATTN_IN_RANGE(p.part_l + hs * p.max_splits + split, 4, p.part_l, part_rows * 4, kSiteDecPartML)) {
         p.part_m[hs * p.max_splits + split] = m_run == -INFINITY ? -INFINITY : m_run * kLn2;
         p.part_l[hs * p.max_splits + split] = l_run;
       }
@@ -501,8 +522,12 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
     float f = lr_all > 0.f ? l_all / lr_all : 1.f;
     if (KV8) f *= p.v_scale;
     const size_t hs = (size_t)b * p.h + kvh * p.g + hb0 + j;
-    *reinterpret_cast<f32x4*>(&p.part_o[(hs * p.max_splits + split) * kD + d]) = o * f;
-    if ((tid & 31) == 0) {
+    if (ATTN_IN_RANGE(&p.part_o[(hs * p.max_splits + split) * kD + d], 16, p.part_o, part_rows * kD * 4,
+                      kSiteDecPartO))
+      *reinterpret_cast<f32x4*>(&p.part_o[(hs * p.max_splits + split) * kD + d]) = o * f;
+    if ((tid & 31) == 0 &&
+        ATTN_IN_RANGE(p.part_m + hs * p.max_splits + split, 4, p.part_m, part_rows * 4, kSiteDecPartML) &&
+        ATTN_IN_RANGE(p.part_l + hs * p.max_splits + split, 4, p.part_l, part_rows * 4, kSiteDecPartML)) {
       p.part_m[hs * p.max_splits + split] = m_all == -INFINITY ? -INFINITY : m_all * kLn2;
       p.part_l[hs * p.max_splits + split] = l_all;
     }
@@ -558,6 +583,8 @@ DecodeParams decode_params(const void* q, const void* k, const void* v, const in
   return p;
 }
 }  // namespace
+
+ATTN_DEFINE_CHECK_READER(decode)
 
 hipError_t decode_split(const void* q, const void* k, const void* v, const int32_t* block_table,
                         int max_pages, int page_size, int num_pages, const int32_t* seq_lens,

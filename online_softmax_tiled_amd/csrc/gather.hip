@@ -32,8 +32,12 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
   const int tid = threadIdx.x;
   const int pos = blockIdx.x * 16 + (tid >> 4);
   const int chunk = tid & 15;
+  if (!ATTN_IN_RANGE(p.seq_lens + b, 4, p.seq_lens, (size_t)p.B * 4, kSiteGthLens)) return;
   const int s_len = min(min(p.seq_lens[b], p.s_max), p.max_pages * p.page_size);
   if (pos >= s_len) return;
+  if (!ATTN_IN_RANGE(p.bt + (size_t)b * p.max_pages + pos / p.page_size, 4, p.bt, (size_t)p.B * p.max_pages * 4,
+                     kSiteGthTable))
+    return;
   const int page = p.bt[(size_t)b * p.max_pages + pos / p.page_size];
   if (page < 0 || page >= p.num_pages) return;
   const size_t src = ((size_t)page * p.page_size + pos % p.page_size) * p.h_kv;
@@ -41,15 +45,23 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
     u32x4 v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (h0 + i < p.h_kv) v[i] = load16_nt(p.pool + (src + h0 + i) * kD + chunk * 8);
+      if (h0 + i < p.h_kv)
+        v[i] = ATTN_IN_RANGE(p.pool + (src + h0 + i) * kD + chunk * 8, 16, p.pool,
+                             (size_t)p.num_pages * p.page_size * p.h_kv * kD * 2, kSiteGthPool)
+                   ? load16_nt(p.pool + (src + h0 + i) * kD + chunk * 8)
+                   : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (h0 + i < p.h_kv)
+      if (h0 + i < p.h_kv &&
+          ATTN_IN_RANGE(p.out + (((size_t)b * p.h_kv + h0 + i) * p.s_max + pos) * kD + chunk * 8, 16, p.out,
+                        (size_t)p.B * p.h_kv * p.s_max * kD * 2, kSiteGthOut))
         store16_nt(p.out + (((size_t)b * p.h_kv + h0 + i) * p.s_max + pos) * kD + chunk * 8, v[i]);
   }
 }
 
 }  // namespace
+
+ATTN_DEFINE_CHECK_READER(gather)
 
 hipError_t paged_gather(const void* pool, const int32_t* block_table, const int32_t* seq_lens,
                         int B, int h_kv, int page_size, int max_pages, int num_pages, int s_max,

@@ -72,7 +72,10 @@ __global__ __launch_bounds__(kD / ND / (4 * V) * kSL) void merge_kernel(MergePar
   const int d0 = blockIdx.y * kSlice;
   const int b = bh / p.h;
   const int tid = threadIdx.x;
-  const int s_len = p.seq_lens[b];
+#ifdef ATTN_DEVICE_CHECKS
+  const size_t part_rows = (size_t)p.B * p.h * p.max_splits;
+#endif
+  const int s_len = ATTN_IN_RANGE(p.seq_lens + b, 4, p.seq_lens, (size_t)p.B * 4, kSiteMrgLens) ? p.seq_lens[b] : 0;
   const int n = s_len <= 0 ? 0 : min(p.max_splits, (s_len + p.chunk - 1) / p.chunk);
   const size_t base = (size_t)bh * p.max_splits;
 
@@ -92,15 +95,22 @@ __global__ __launch_bounds__(kD / ND / (4 * V) * kSL) void merge_kernel(MergePar
 #pragma unroll
   for (int u = 0; u < U0; ++u) {
     const int i = sl + u * kSL;
-    const bool in = i < lim;
+    const bool in = i < lim && ATTN_IN_RANGE(p.part_l + base + i, 4, p.part_l, part_rows * 4, kSiteMrgPartML) &&
+                    ATTN_IN_RANGE(p.part_m + base + i, 4, p.part_m, part_rows * 4, kSiteMrgPartML);
     li0[u] = in ? p.part_l[base + i] : 0.f;
     mi0[u] = in ? p.part_m[base + i] : -INFINITY;
 #pragma unroll
     for (int c = 0; c < V; ++c)
-      oi0[u][c] = in ? *reinterpret_cast<const f32x4*>(&p.part_o[(base + i) * kD + d0 + d + 4 * c]) : f32x4{};
+      oi0[u][c] = in && ATTN_IN_RANGE(&p.part_o[(base + i) * kD + d0 + d + 4 * c], 16, p.part_o, part_rows * kD * 4,
+                                      kSiteMrgPartO)
+                      ? *reinterpret_cast<const f32x4*>(&p.part_o[(base + i) * kD + d0 + d + 4 * c])
+                      : f32x4{};
   }
   float mloc = -INFINITY;
   for (int i = tid; i < lim; i += NT) {
+    if (!(ATTN_IN_RANGE(p.part_m + base + i, 4, p.part_m, part_rows * 4, kSiteMrgPartML) &&
+          ATTN_IN_RANGE(p.part_l + base + i, 4, p.part_l, part_rows * 4, kSiteMrgPartML)))
+      continue;
     const float mi = p.part_m[base + i];
     if (i < n && p.part_l[base + i] > 0.f) mloc = fmaxf(mloc, mi);
   }
@@ -113,8 +123,11 @@ __global__ __launch_bounds__(kD / ND / (4 * V) * kSL) void merge_kernel(MergePar
 
   uint16_t* op = p.o + (size_t)bh * kD + d0;
   if (big == -INFINITY) {   // no visible key in any split: zero output
-    if (tid < kSlice / 2) reinterpret_cast<uint32_t*>(op)[tid] = 0u;
-    if (tid == 0 && blockIdx.y == 0 && p.lse != nullptr) p.lse[bh] = -INFINITY;
+    if (tid < kSlice / 2 && ATTN_IN_RANGE(op + 2 * tid, 4, p.o, (size_t)p.B * p.h * kD * 2, kSiteMrgO))
+      reinterpret_cast<uint32_t*>(op)[tid] = 0u;
+    if (tid == 0 && blockIdx.y == 0 && p.lse != nullptr &&
+        ATTN_IN_RANGE(p.lse + bh, 4, p.lse, (size_t)p.B * p.h * 4, kSiteMrgLse))
+      p.lse[bh] = -INFINITY;
     return;
   }
 
@@ -137,12 +150,16 @@ __global__ __launch_bounds__(kD / ND / (4 * V) * kSL) void merge_kernel(MergePar
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = i0 + u * kSL;
-      const bool ok = i < n;
+      const bool ok = i < n && ATTN_IN_RANGE(p.part_l + base + i, 4, p.part_l, part_rows * 4, kSiteMrgPartML) &&
+                      ATTN_IN_RANGE(p.part_m + base + i, 4, p.part_m, part_rows * 4, kSiteMrgPartML);
       li[u] = ok ? p.part_l[base + i] : 0.f;
       mi[u] = ok ? p.part_m[base + i] : -INFINITY;
 #pragma unroll
       for (int c = 0; c < V; ++c)
-        oi[u][c] = ok ? *reinterpret_cast<const f32x4*>(&p.part_o[(base + i) * kD + d0 + d + 4 * c]) : f32x4{};
+        oi[u][c] = ok && ATTN_IN_RANGE(&p.part_o[(base + i) * kD + d0 + d + 4 * c], 16, p.part_o,
+                                       part_rows * kD * 4, kSiteMrgPartO)
+                       ? *reinterpret_cast<const f32x4*>(&p.part_o[(base + i) * kD + d0 + d + 4 * c])
+                       : f32x4{};
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -170,8 +187,11 @@ __global__ __launch_bounds__(kD / ND / (4 * V) * kSL) void merge_kernel(MergePar
       o1 += red_o[s][dd + 1];
     }
     const float inv = 1.f / l_all;
-    reinterpret_cast<uint32_t*>(op)[tid] = E::pack2(o0 * inv, o1 * inv);
-    if (tid == 0 && blockIdx.y == 0 && p.lse != nullptr) p.lse[bh] = big + fast_log2(l_all) * kLn2;
+    if (ATTN_IN_RANGE(op + 2 * tid, 4, p.o, (size_t)p.B * p.h * kD * 2, kSiteMrgO))
+      reinterpret_cast<uint32_t*>(op)[tid] = E::pack2(o0 * inv, o1 * inv);
+    if (tid == 0 && blockIdx.y == 0 && p.lse != nullptr &&
+        ATTN_IN_RANGE(p.lse + bh, 4, p.lse, (size_t)p.B * p.h * 4, kSiteMrgLse))
+      p.lse[bh] = big + fast_log2(l_all) * kLn2;
   }
 }
 
@@ -196,6 +216,8 @@ hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
 }
 
 }  // namespace
+
+ATTN_DEFINE_CHECK_READER(merge)
 
 hipError_t merge_states(const float* part_o, const float* part_m, const float* part_l,
                         const int32_t* seq_lens, int chunk_keys, int B, int h, int max_splits,

@@ -43,6 +43,9 @@ __global__ __launch_bounds__(256) void merge_lse_kernel(MergeLseParams p) {
   const int row = blockIdx.x * kRowsPerWg + (threadIdx.x >> 4);
   if (row >= p.rows) return;
   const int c = threadIdx.x & 15;
+  const bool rows_ok = ATTN_IN_RANGE(p.lse_a + row, 4, p.lse_a, (size_t)p.rows * 4, kSiteMlseLse) &&
+                       ATTN_IN_RANGE(p.lse_b + row, 4, p.lse_b, (size_t)p.rows * 4, kSiteMlseLse);
+  if (!rows_ok) return;
   float la = p.lse_a[row];
   float lb = p.lse_b[row];
   la = la == INFINITY ? -INFINITY : la;
@@ -61,7 +64,7 @@ __global__ __launch_bounds__(256) void merge_lse_kernel(MergeLseParams p) {
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    if (ea > 0.f) {
+    if (ea > 0.f && ATTN_IN_RANGE(p.o_a + off, 16, p.o_a, (size_t)p.rows * kD * 2, kSiteMlseIn)) {
       const u32x4 va = load16_nt(p.o_a + off);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -69,7 +72,7 @@ __global__ __launch_bounds__(256) void merge_lse_kernel(MergeLseParams p) {
         acc[2 * i + 1] += pa * E::to_f32((uint16_t)(va[i] >> 16));
       }
     }
-    if (eb > 0.f) {
+    if (eb > 0.f && ATTN_IN_RANGE(p.o_b + off, 16, p.o_b, (size_t)p.rows * kD * 2, kSiteMlseIn)) {
       const u32x4 vb = load16_nt(p.o_b + off);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -81,11 +84,14 @@ __global__ __launch_bounds__(256) void merge_lse_kernel(MergeLseParams p) {
     for (int i = 0; i < 4; ++i) out[i] = E::pack2(acc[2 * i], acc[2 * i + 1]);
     lse_out = big + fast_log2(tot) * kLn2;
   }
-  store16_nt(p.o + off, out);
-  if (p.lse != nullptr && c == 0) p.lse[row] = lse_out;
+  if (ATTN_IN_RANGE(p.o + off, 16, p.o, (size_t)p.rows * kD * 2, kSiteMlseO)) store16_nt(p.o + off, out);
+  if (p.lse != nullptr && c == 0 && ATTN_IN_RANGE(p.lse + row, 4, p.lse, (size_t)p.rows * 4, kSiteMlseLse))
+    p.lse[row] = lse_out;
 }
 
 }  // namespace
+
+ATTN_DEFINE_CHECK_READER(merge_lse)
 
 hipError_t merge_lse(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, void* o,
                      float* lse, int rows, int dtype, hipStream_t stream) {

@@ -231,13 +231,23 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   const int b = bk / p.h_kv;
   const int kvh = bk - b * p.h_kv;
 
+#ifdef ATTN_DEVICE_CHECKS
+  // extents of the tensors (bytes; rows of Q, O and LSE)
+  const size_t e_pool = PAGED ? ((size_t)p.num_pages << p.page_shift) * p.h_kv * kD * kEB : 0;
+  const size_t e_kv = PAGED ? e_pool
+                      : DEC ? (size_t)p.B * p.h_kv * p.s_max * kD * kEB
+                            : (size_t)p.B * p.h_kv * p.T_k * kD * kEB;
+  const size_t q_rows = DEC ? (size_t)p.B * p.h : PAGED ? (size_t)p.cu_q[p.B] * p.h : (size_t)p.B * p.h * p.T_q;
+  const size_t e_bt = (size_t)p.B * p.max_pages * 4;
+  const size_t part_rows = DEC ? (size_t)p.B * p.h * p.max_splits : 0;
+#endif
   // Lengths of this sequence (uniform over the workgroup).
   int T_q = p.T_q, T_k = p.T_k, n_rb = p.n_rb, q_start = 0;
   int k_lo = 0;   // first key of the workgroup's range (DEC)
   if (DEC) {
     // Splits past the sequence write nothing; the merge counts the valid
     // ones from the same key count.
-    const int s_raw = p.seq_k[b];
+    const int s_raw = ATTN_IN_RANGE(p.seq_k + b, 4, p.seq_k, (size_t)p.B * 4, kSitePreLens) ? p.seq_k[b] : 0;
     if (s_raw <= 0) return;
     if (split >= min(p.max_splits, (s_raw + p.chunk - 1) / p.chunk)) return;
     const int s_len = min(s_raw, PAGED ? p.max_pages << p.page_shift : p.s_max);
@@ -245,9 +255,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     const int k_hi = split == p.max_splits - 1 ? s_len : min(s_len, k_lo + p.chunk);
     T_k = max(0, k_hi - k_lo);   // keys counted from k_lo
   } else if (PAGED) {
-    q_start = p.cu_q[b];
-    T_q = min(p.cu_q[b + 1] - q_start, p.T_q);
-    T_k = min(p.seq_k[b], p.max_pages << p.page_shift);
+    const bool lens_ok = ATTN_IN_RANGE(p.cu_q + b, 8, p.cu_q, ((size_t)p.B + 1) * 4, kSitePreLens) &&
+                         ATTN_IN_RANGE(p.seq_k + b, 4, p.seq_k, (size_t)p.B * 4, kSitePreLens);
+    q_start = lens_ok ? p.cu_q[b] : 0;
+    T_q = lens_ok ? min(p.cu_q[b + 1] - q_start, p.T_q) : 0;
+    T_k = lens_ok ? min(p.seq_k[b], p.max_pages << p.page_shift) : 0;
     n_rb = p.g * ((T_q + kRows - 1) / kRows);
     if (grp * kWaves >= n_rb) return;   // whole workgroup past this sequence's rows
   }
@@ -280,14 +292,21 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     const uint16_t* qbase = DEC     ? p.q + ((size_t)b * p.h + hq) * kD
                             : PAGED ? p.q + ((size_t)q_start * p.h + hq) * kD
                                     : p.q + (size_t)(b * p.h + hq) * T_q * kD;
-    const auto rq = make_rsrc(qbase, wave_valid ? (uint32_t)T_q * q_rstride * 2 : 0u);
+    // (checked build: the rows this wave reads, head hq of rows 0 .. T_q - 1)
+    const bool q_ok = !wave_valid || T_q <= 0 ||
+                      ATTN_IN_RANGE(qbase, ((size_t)(T_q - 1) * q_rstride + kD) * 2, p.q, q_rows * kD * 2, kSitePreQ);
+    const auto rq = make_rsrc(qbase, wave_valid && q_ok ? (uint32_t)T_q * q_rstride * 2 : 0u);
 #pragma unroll
     for (int c = 0; c < 8; ++c) qf[c] = buffer_load16(rq, (uint32_t)(qrow * q_rstride + c * 16 + half * 8) * 2u);
   }
 
   const size_t kv_base = PAGED ? 0 : DEC ? ((size_t)bk * p.s_max + k_lo) * kD : (size_t)bk * T_k * kD;
   // (kPool32: the whole pools)
-  const uint32_t kv_range = PAGED ? (pool32 ? p.pool_bytes : 0u) : (uint32_t)T_k * kD * kEB;
+  uint32_t kv_range = PAGED ? (pool32 ? p.pool_bytes : 0u) : (uint32_t)T_k * kD * kEB;
+  if (kv_range != 0 &&
+      !(ATTN_IN_RANGE(reinterpret_cast<const uint8_t*>(p.k) + kv_base * kEB, kv_range, p.k, e_kv, kSitePreKV) &&
+        ATTN_IN_RANGE(reinterpret_cast<const uint8_t*>(p.v) + kv_base * kEB, kv_range, p.v, e_kv, kSitePreKV)))
+    kv_range = 0u;
   const auto rk = make_rsrc(reinterpret_cast<const uint8_t*>(p.k) + kv_base * kEB, kv_range);
   const auto rv = make_rsrc(reinterpret_cast<const uint8_t*>(p.v) + kv_base * kEB, kv_range);
 
@@ -305,9 +324,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   // where the value is used. A branch around such a load would make the
   // compiler wait for it (and, loads retiring in order, for every tile load
   // issued before it) right where the branches join, before the products.
+  const bool key_row_ok =
+      !KMASK || (PAGED ? ATTN_IN_RANGE(p.bt + (size_t)b * p.max_pages, (size_t)p.max_pages * 4, p.bt, e_bt, kSitePreKeyRow)
+                       : ATTN_IN_RANGE(p.key_mask + (size_t)b * T_k, (size_t)T_k, p.key_mask, (size_t)p.B * p.T_k,
+                                       kSitePreKeyRow));
   const auto r_key = !KMASK ? make_rsrc(nullptr, 0u)
-                     : PAGED ? make_rsrc(p.bt + (size_t)b * p.max_pages, (uint32_t)p.max_pages * 4u)
-                             : make_rsrc(p.key_mask + (size_t)b * T_k, (uint32_t)T_k);
+                     : PAGED ? make_rsrc(p.bt + (size_t)b * p.max_pages, key_row_ok ? (uint32_t)p.max_pages * 4u : 0u)
+                             : make_rsrc(p.key_mask + (size_t)b * T_k, key_row_ok ? (uint32_t)T_k : 0u);
   // Paged: the block-table entry of staging row i of tile t, and the pool row
   // it gives; keys past T_k or on a page id outside the pool read as zeros.
   // Page ids are fetched one iteration before the K tile that needs them and
@@ -321,8 +344,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   const __attribute__((address_space(4))) int32_t* bt_row =
       (const __attribute__((address_space(4))) int32_t*)(PAGED ? p.bt + (size_t)b * p.max_pages : p.bt);
   auto page_of = [&](int t, int i) -> int {
-    if (pool32)   // rows 4 wave + 32 i + 0..3 of tile t
-      return bt_row[min((k_lo + t * kBc + 4 * wave + 32 * i) >> p.page_shift, p.max_pages - 1)];
+    if (pool32) {   // rows 4 wave + 32 i + 0..3 of tile t
+      const int idx = min((k_lo + t * kBc + 4 * wave + 32 * i) >> p.page_shift, p.max_pages - 1);
+      return ATTN_IN_RANGE(p.bt + (size_t)b * p.max_pages + idx, 4, p.bt, e_bt, kSitePreTableRow) ? bt_row[idx] : -1;
+    }
     const uint32_t key = (uint32_t)(k_lo + t * kBc + ((tid + kThreads * i) >> 4));
     return (int)__builtin_amdgcn_raw_buffer_load_b32(r_key, (int)((key >> p.page_shift) * 4u), 0, 0);
   };
@@ -353,7 +378,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
         kreg[i] = kv_load(rk, pool_off(t, i, pg_k[i]));
       } else if constexpr (PAGED && !kv8) {
         const long r = paged_row(t, i, pg_k[i]);
-        kreg[i] = r >= 0 ? load16(p.k + r * kD + (tid & 15) * 8) : u32x4{0u, 0u, 0u, 0u};
+        kreg[i] = r >= 0 && ATTN_IN_RANGE(p.k + r * kD + (tid & 15) * 8, 16, p.k, e_pool, kSitePrePagedKV)
+                      ? load16(p.k + r * kD + (tid & 15) * 8)
+                      : u32x4{0u, 0u, 0u, 0u};
       } else {
         kreg[i] = kv_load(rk, tile_byte(t, i));
       }
@@ -366,7 +393,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
         vreg[i] = kv_load(rv, pool_off(t, i, pg_v[i]));
       } else if constexpr (PAGED && !kv8) {
         const long r = paged_row(t, i, pg_v[i]);
-        vreg[i] = r >= 0 ? load16(p.v + r * kD + (tid & 15) * 8) : u32x4{0u, 0u, 0u, 0u};
+        vreg[i] = r >= 0 && ATTN_IN_RANGE(p.v + r * kD + (tid & 15) * 8, 16, p.v, e_pool, kSitePrePagedKV)
+                      ? load16(p.v + r * kD + (tid & 15) * 8)
+                      : u32x4{0u, 0u, 0u, 0u};
       } else {
         vreg[i] = kv_load(rv, tile_byte(t, i));
       }
@@ -588,7 +617,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     const uint32_t lane_off =
         ((uint32_t)(st >> 4) * (uint32_t)p.h_kv + (uint32_t)kvh) * (kD * kEB) + (uint32_t)(st & 15) * 8u * kEB;
     auto grp_page = [&](int t, int i) -> int {   // first key of the group: t * kBc + 16 i from k_lo
-      return bt_row[min((k_lo + t * kBc + 16 * i) >> p.page_shift, p.max_pages - 1)];
+      const int idx = min((k_lo + t * kBc + 16 * i) >> p.page_shift, p.max_pages - 1);
+      return ATTN_IN_RANGE(p.bt + (size_t)b * p.max_pages + idx, 4, p.bt, e_bt, kSitePreTableRow) ? bt_row[idx] : -1;
     };
     auto grp_off = [&](int t, int i, int page) -> uint32_t {
       const int g = t * kBc + 16 * i;
@@ -616,7 +646,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
               valid ? (((long)page << p.page_shift) + ((k_lo + key_l) & ((1 << p.page_shift) - 1))) * p.h_kv + kvh
                     : 0;
           ok |= valid ? 1u << bit : 0u;
-          return load16(pool + row * kD + (st & 15) * 8);
+          return ATTN_IN_RANGE(pool + row * kD + (st & 15) * 8, 16, pool, e_pool, kSitePrePagedKV)
+                     ? load16(pool + row * kD + (st & 15) * 8)
+                     : u32x4{0u, 0u, 0u, 0u};
         }
       }
     };
@@ -877,17 +909,21 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4)
-        *reinterpret_cast<f32x4*>(po + db * 32 + g4 * 8 + half * 4) =
-            f32x4{acc[db][g4 * 4 + 0] * rs, acc[db][g4 * 4 + 1] * rs, acc[db][g4 * 4 + 2] * rs,
-                  acc[db][g4 * 4 + 3] * rs};
-    if (half == 0) {
+        if (ATTN_IN_RANGE(po + db * 32 + g4 * 8 + half * 4, 16, p.part_o, part_rows * kD * 4, kSitePrePartO))
+          *reinterpret_cast<f32x4*>(po + db * 32 + g4 * 8 + half * 4) =
+              f32x4{acc[db][g4 * 4 + 0] * rs, acc[db][g4 * 4 + 1] * rs, acc[db][g4 * 4 + 2] * rs,
+                    acc[db][g4 * 4 + 3] * rs};
+    if (half == 0 && ATTN_IN_RANGE(p.part_m + hs, 4, p.part_m, part_rows * 4, kSitePrePartML) &&
+        ATTN_IN_RANGE(p.part_l + hs, 4, p.part_l, part_rows * 4, kSitePrePartML)) {
       p.part_m[hs] = none ? -INFINITY : m_ref * kLn2;
       p.part_l[hs] = l_tot;
     }
     return;
   }
   bool empty = l_tot == 0.f;
-  if (!PAGED && p.row_mask != nullptr) empty = empty || p.row_mask[(size_t)b * T_q + qrow] == 0;
+  if (!PAGED && p.row_mask != nullptr &&
+      ATTN_IN_RANGE(p.row_mask + (size_t)b * T_q + qrow, 1, p.row_mask, (size_t)p.B * p.T_q, kSitePreRowMask))
+    empty = empty || p.row_mask[(size_t)b * T_q + qrow] == 0;
   const float inv = empty ? 0.f : 1.f / lr_tot;
   const size_t orow = PAGED ? (size_t)(q_start + qrow) * p.h + head : (size_t)(b * p.h + head) * T_q + qrow;
   uint16_t* op = p.o + orow * kD;
@@ -899,10 +935,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
       float v0 = acc[db][g4 * 4 + 0] * inv, v1 = acc[db][g4 * 4 + 1] * inv;
       float v2 = acc[db][g4 * 4 + 2] * inv, v3 = acc[db][g4 * 4 + 3] * inv;
       if (empty) v0 = v1 = v2 = v3 = 0.f;
-      store8(op + d, u32x2{E::pack2(v0, v1), E::pack2(v2, v3)});
+      if (ATTN_IN_RANGE(op + d, 8, p.o, q_rows * kD * 2, kSitePreO))
+        store8(op + d, u32x2{E::pack2(v0, v1), E::pack2(v2, v3)});
     }
   }
-  if (p.lse != nullptr && half == 0)
+  if (p.lse != nullptr && half == 0 && ATTN_IN_RANGE(p.lse + orow, 4, p.lse, q_rows * 4, kSitePreLse))
     p.lse[orow] = empty ? -INFINITY : (m_ref + fast_log2(l_tot)) * kLn2;
 }
 
@@ -1000,6 +1037,8 @@ PrefillParams common_params(const void* q, const void* k, const void* v, void* o
 }
 
 }  // namespace
+
+ATTN_DEFINE_CHECK_READER(prefill)
 
 hipError_t prefill_fwd(const void* q, const void* k, const void* v, const uint8_t* key_mask,
                        const uint8_t* row_mask, void* o, float* lse, int B, int h, int h_kv,

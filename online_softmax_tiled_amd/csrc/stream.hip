@@ -23,7 +23,8 @@ __global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(const u32x4
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const uint64_t k = i + (uint64_t)u * kStreamThreads;
-      v[u] = k < hi ? load16_nt(src + k) : u32x4{0u, 0u, 0u, 0u};
+      v[u] = k < hi && ATTN_IN_RANGE(src + k, 16, src, n16 * 16, kSiteStream) ? load16_nt(src + k)
+                                                                             : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
@@ -37,7 +38,26 @@ __global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(const u32x4
   if (threadIdx.x == 0) out[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
 }
 
+#ifdef ATTN_DEVICE_CHECKS
+// The checker's own test: one address inside a 64-byte extent and one past
+// it, tested and not accessed.
+__global__ void check_selftest_kernel(const uint8_t* base) {
+  if (threadIdx.x != 0) return;
+  (void)ATTN_IN_RANGE(base + 56, 8, base, 64, kSiteSelfTestIn);
+  (void)ATTN_IN_RANGE(base + 60, 8, base, 64, kSiteSelfTestOut);
+}
+#endif
+
 }  // namespace
+
+ATTN_DEFINE_CHECK_READER(stream)
+
+#ifdef ATTN_DEVICE_CHECKS
+hipError_t check_selftest(const void* base, hipStream_t stream) {
+  hipLaunchKernelGGL(check_selftest_kernel, dim3(1), dim3(64), 0, stream, static_cast<const uint8_t*>(base));
+  return hipGetLastError();
+}
+#endif
 
 // chunks: workgroups (each reads bytes / chunks, rounded up to 16 bytes).
 hipError_t stream_read(const void* src, uint64_t bytes, int chunks, uint32_t* out, hipStream_t stream) {

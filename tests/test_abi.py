@@ -397,3 +397,31 @@ def test_stream_read_rejects_before_launch(lib):
     assert lib.attn_stream_read(p(16), 64, 4, None, None) == 1
     assert lib.attn_stream_read(p(24), 64, 4, p(16), None) == 1          # misaligned source
     assert "attn_stream_read" in lib.attn_last_error().decode()
+
+
+# ---------------------------------------------------------------- bounds-checking debug build
+
+def test_checked_library_exports_every_declared_symbol(lib):
+    from online_softmax_tiled_amd import api
+    if not os.path.exists(api.CHECKED_LIB_PATH):
+        from online_softmax_tiled_amd.build import build
+        build()
+    out = subprocess.run(["nm", "-D", "--defined-only", api.CHECKED_LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s(attn_\w+)$", out, re.M))
+    assert set(declared_symbols()) <= exported
+    with api.checked_library() as checked:
+        assert "bounds checks" in api.version()
+        # rejected before any device call
+        hits = (ctypes.c_uint32 * 8)()
+        assert checked.attn_check_report(ctypes.cast(hits, ctypes.c_void_p), 8) == 1
+        assert checked.attn_check_report(None, 64) == 1
+        assert checked.attn_check_selftest(None, None) == 1
+    assert "bounds checks" not in api.version()   # the product library again
+
+
+def test_product_library_has_no_bounds_checks(lib):
+    hits = (ctypes.c_uint32 * 64)()
+    assert lib.attn_check_report(ctypes.cast(hits, ctypes.c_void_p), 64) == 2
+    assert "without device bounds checks" in lib.attn_last_error().decode()
+    assert lib.attn_check_clear() == 2
+    assert lib.attn_check_selftest(ctypes.c_void_p(16), None) == 2
