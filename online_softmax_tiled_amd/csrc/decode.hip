@@ -43,6 +43,14 @@
 // Keys outside the split, past the sequence, or on a page id outside the
 // pool are excluded (score -inf) and their V rows are zeroed before use, so
 // poisoned (NaN) slots never reach the result.
+//
+// 8-bit K/V (KV8; "The Online Softmax Recurrence", section "Where it
+// breaks": FP8 operands with fp32 statistics). K and V hold OCP E4M3 codes
+// with one fp32 scale per tensor. The codes become MFMA operands in
+// registers (K in the query's type, V in fp16, both exact); k_scale joins
+// the score constant and v_scale the factor each split's O~ is written
+// with. The loads of each wave's next two tiles stay in flight while a tile
+// is computed (see the KV8 loop).
 #include <type_traits>
 
 #include "common.h"
