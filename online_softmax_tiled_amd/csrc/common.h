@@ -86,19 +86,35 @@ struct Elem<ATTN_DTYPE_F16> {
   }
 };
 
-// A pair of bf16 values (lo in bits [15:0]) as a pair of fp16 values. Every
-// bf16 value of magnitude in [2^-14, 65536) is an fp16 value (fp16 has more
-// significand bits and covers that exponent range), so these convert
-// exactly; smaller ones land on the fp16 subnormal grid (absolute error below
-// 2^-24), and magnitudes of 65536 or more do not fit (they come out as
-// +-65504). `vmax` keeps the largest magnitude seen, so the caller can tell.
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t x, float& vmax) {
+// A pair of bf16 values (lo in bits [15:0]) as a pair of fp16 values,
+// rounded to nearest. Every bf16 value of magnitude in [2^-14, 65536) is an
+// fp16 value (fp16 has more significand bits and covers that exponent range),
+// so these convert exactly; smaller ones land on the fp16 subnormal grid
+// (absolute error at most 2^-25), and magnitudes of 65536 or more overflow to
+// +-inf (the largest bf16 value below 65536 is 65280, which fp16 holds), so
+// that a product that uses one comes out inf or NaN.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t x) {
   const float lo = __builtin_bit_cast(float, x << 16);
   const float hi = __builtin_bit_cast(float, x & 0xffff0000u);
-  vmax = fmaxf(vmax, fmaxf(fabsf(lo), fabsf(hi)));
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+  return Elem<ATTN_DTYPE_F16>::pack2(lo, hi);
 }
-constexpr float kF16Overflow = 65536.f;   // smallest bf16 magnitude fp16 cannot hold
+
+// True when any of the 64 accumulator values is inf or NaN (exponent field
+// all ones), tested on the bits so that no floating-point assumption about
+// NaN can remove the test. Each element is copied to a scalar before the
+// bit cast: this compiler lowers a bit cast of a subscripted vector element
+// as a load from the vector's first element, whatever the subscript.
+__device__ __forceinline__ bool any_nonfinite(const f32x16 (&acc)[4]) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float x = acc[i][e];
+      m = max(m, __builtin_bit_cast(uint32_t, x) & 0x7fffffffu);
+    }
+  return m >= 0x7f800000u;
+}
 
 // Eight E4M3 codes (two words, code e in byte e % 4 of word e / 4) as eight
 // 16-bit operands of type DT, with gfx950's packed fp8 conversion at scale

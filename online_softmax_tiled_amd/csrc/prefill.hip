@@ -67,7 +67,10 @@
 //   split), and the epilogue writes the split's partial state for the merge.
 //   With at most 128 heads (kStagers), waves 4-7 hold no rows and stage
 //   every K/V tile two iterations ahead, so a CU keeps two tile pairs of
-//   loads in flight while waves 0-3 compute.
+//   loads in flight while waves 0-3 compute. With 8-bit K/V (kKV8) the
+//   staging waves read E4M3 codes and convert them as they store the tiles,
+//   so the compute waves run the 16-bit form unchanged; k_scale is folded
+//   into the score multiplier and v_scale into the epilogue's O~ factor.
 //
 // Paged pools under 4 GB (kPool32, paged and decode forms): K/V rows are
 // addressed with range-checked 32-bit buffer offsets over the whole pool; a
@@ -408,18 +411,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   };
   // V tiles reach LDS in the element type of the PV product: fp16 in the
   // fp16 pass (bf16 inputs are converted here, exactly below 65536 in
-  // magnitude; v_max records the largest magnitude staged), the input type
-  // in the fallback pass.
-  // (8-bit V: codes straight to the pass's type; at most 448 in magnitude,
-  // they never take the bf16 pass.)
-  float v_max = 0.f;
+  // magnitude, to +-inf from 65536 up), the input type in the fallback pass.
+  // (8-bit V: codes straight to the pass's type; at most 448 in magnitude.)
   auto conv_v = [&](KVRaw x, auto pv16) -> u32x4 {
     if constexpr (kv8) {
       return cvt8<decltype(pv16)::value ? ATTN_DTYPE_F16 : DT>(x);
     } else {
       if constexpr (decltype(pv16)::value && DT == ATTN_DTYPE_BF16) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = bf16x2_to_f16x2(x[e], v_max);
+        for (int e = 0; e < 4; ++e) x[e] = bf16x2_to_f16x2(x[e]);
       }
       return x;
     }
@@ -538,7 +538,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   // (P rounded to fp16 -- 3 more significand bits than bf16 -- and V as
   // staged by store_v); with bf16 inputs the pass is run again with bf16
   // operands if a V value of magnitude 65536 or more was staged (fp16 cannot
-  // hold it). Every wave of the workgroup takes the same passes.
+  // hold it; it was staged as +-inf). Every wave of the workgroup takes the
+  // same passes.
   auto pass = [&](auto pv16) {
   constexpr bool PV16 = decltype(pv16)::value;
   using EP = Elem<PV16 ? ATTN_DTYPE_F16 : DT>;
@@ -775,9 +776,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
       float mx, base, rs = 0.f;
       // slice 0: PV chunk 0 | row maxima
       read_v(0, fa);
+      // one chain of three-operand maxima (max(max(m, a), b) is one v_max3)
       mx = fmaxf(sc[0][0], sc[1][0]);
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(sc[0][r], sc[1][r]));
+      for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, sc[0][r]), sc[1][r]);
       read_v(1, fb);
 #pragma unroll
       for (int db = 0; db < 4; ++db) acc[db] = EP::mfma32(fa[db], pp[0], acc[db]);
@@ -887,10 +889,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   };
 
   pass(std::true_type{});
-  if constexpr (DT == ATTN_DTYPE_BF16) {
-    // a staged V value fp16 cannot hold: the workgroup runs the pass again
-    // with bf16 operands (all waves take the same decision)
-    if (__syncthreads_or(v_max >= kF16Overflow)) pass(std::false_type{});
+  if constexpr (DT == ATTN_DTYPE_BF16 && !kv8) {
+    // A staged V value fp16 cannot hold was stored as +-inf. Every staged V
+    // row enters the PV product of every computing wave (a key a wave does
+    // not see has weight 0, and 0 * inf is NaN), and O~ is otherwise finite
+    // for finite inputs (at most 65280 * 2^kTau per key), so a non-finite O~
+    // in any wave means such a value, or a non-finite input. The workgroup
+    // then runs the pass again with bf16 operands (all waves take the same
+    // decision; with non-finite inputs the second pass gives what they give).
+    if (__syncthreads_or(any_nonfinite(acc))) pass(std::false_type{});
   }
   if (stagers && wave >= 4) return;
   if (!wave_valid || qrow >= T_q) return;
