@@ -401,6 +401,25 @@ def test_stream_read_rejects_before_launch(lib):
 
 # ---------------------------------------------------------------- bounds-checking debug build
 
+def test_no_bit_cast_of_a_subscripted_vector_element():
+    # The device compiler lowers __builtin_bit_cast(T, v[i]) of an element of
+    # an ext-vector as a load of the vector's first element, whatever i is
+    # (the subscript is computed and dropped). Kernel sources copy such an
+    # element to a scalar before a bit cast; this keeps the pattern out.
+    csrc = os.path.join(ROOT, "online_softmax_tiled_amd", "csrc")
+    pat = re.compile(r"__builtin_bit_cast\(\s*[\w:<>, ]+?,\s*[A-Za-z_][\w.]*\s*\[[^\]]*\]\s*(\[[^\]]*\]\s*)*\)")
+    hits = []
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            for no, line in enumerate(open(os.path.join(csrc, name)), 1):
+                if pat.search(line):
+                    hits.append(f"{name}:{no}: {line.strip()}")
+    assert not hits, "\n".join(hits)
+    # the pattern matches the form it is meant to catch
+    assert pat.search("m = max(m, __builtin_bit_cast(uint32_t, acc[i][e]) & 1u);")
+    assert not pat.search("__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi))")
+
+
 def test_checked_library_exports_every_declared_symbol(lib):
     from online_softmax_tiled_amd import api
     if not os.path.exists(api.CHECKED_LIB_PATH):

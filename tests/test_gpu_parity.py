@@ -945,6 +945,21 @@ def test_bf16_values_beyond_fp16_range_take_the_bf16_pass():
     _check_big_column(o, lse, o_ref, lse_ref, 100, "row-form decode with V = -2^17")
 
 
+@pytest.mark.parametrize("db,g4,half", [(db, g4, hf) for db in range(4) for g4 in range(4) for hf in range(2)])
+def test_bf16_large_v_found_in_every_accumulator_register(db, g4, half):
+    # A wave's output tile sits in 64 accumulator registers per lane: column
+    # d = 32 db + 8 g4 + 4 half + k lives in register 4 g4 + k of block db on
+    # the lanes of half-wave `half`. The fp16 pass sends a V value of 2^17 in
+    # column d to that register only (as inf or NaN), so the test that starts
+    # the bf16 pass must read every register; one run per (db, g4, half), k
+    # varied with them.
+    col = 32 * db + 8 * g4 + 4 * half + (db + g4 + half) % 4
+    inp = make_prefill(1, 4, 1, 64, 64, 128, "bf16", seed=200 + col, causal=True)
+    inp["v"][0, 0, 9, col] = -float(2 ** 17)
+    o, lse, o_ref, lse_ref = run_prefill(inp)
+    _check_big_column(o, lse, o_ref, lse_ref, col, f"prefill with V = -2^17 in column {col}")
+
+
 def test_stream_read_reads_every_word_once():
     # the read-rate calibration kernel: chunk c's output is the xor of the
     # 32-bit words of its contiguous chunk (bit for bit), for sizes that do
