@@ -204,10 +204,9 @@ int attn_decode_plan_fixed(int B, const int32_t* seq_lens_host, int split_keys,
  * n_b).
  * (m_i, l_i, O~_i) is a state in the sense of [OR] section "The recurrence":
  * m_i is its reference point, and any reference gives the same merged
- * result. With up to 16 query heads per KV head this library stores the
- * largest logit of the split; with more (the heads then form the MFMA rows
- * of the prefill kernel, 32 per wave, contiguous K/V or power-of-two pages)
- * it stores a reference at most 8 ln 2 below that logit.
+ * result. This library stores a reference at most 8 ln 2 below the largest
+ * logit of the split (the reference moves only when that logit exceeds it
+ * by more than 8 ln 2), so every weight exp(x - m_i) is at most 2^8.
  */
 int attn_decode_split(const void* q, const void* k, const void* v,
                       const int32_t* block_table, int max_pages, int page_size, int num_pages,

@@ -61,6 +61,7 @@ namespace {
 constexpr int kD = 128;
 constexpr int kWaves = 4;
 constexpr int kTile = 32;              // keys per wave tile
+constexpr float kTau = 8.f;            // allowed lag of the reference max (log2 units)
 constexpr int kVtStr = kTile + 8;      // V^T row stride in LDS (elements): 80 B
 constexpr int kWaveLds = kD * kVtStr;  // elements per wave region
 
@@ -233,22 +234,31 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
       for (int c = 0; c < 4; ++c) s[kb] = E::mfma16(kfrag(kb, c), qf[c], s[kb]);
     }
     // Exclude keys outside [k_lo, k_hi) or on an invalid page: register r of
-    // block kb holds key kt + 16kb + 4row + r.
+    // block kb holds key kt + 16kb + 4row + r. Only the last tile of a split
+    // and tiles on an invalid page need it (the test is wave-uniform).
+    if (!(bok[0] && bok[1] && kt + kTile <= k_hi)) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool ok = bok[kb] && kt + kb * 16 + row * 4 + r < k_hi;
-        s[kb][r] = ok ? s[kb][r] : -INFINITY;
+        for (int r = 0; r < 4; ++r) {
+          const bool ok = bok[kb] && kt + kb * 16 + row * 4 + r < k_hi;
+          s[kb][r] = ok ? s[kb][r] : -INFINITY;
+        }
       }
     }
 
     float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                      fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
     mx = max_rows16(mx);
-    const float m_new = fmaxf(m_run, mx * p.c);
-    const float base = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - base);
+    // Lagging reference ("The Online Softmax Recurrence", section "The
+    // recurrence": any reference gives the same state once merged): m_run
+    // moves only when a head's largest logit exceeds it by more than kTau,
+    // so every weight stays below 2^kTau and O~ is rescaled on few tiles.
+    const float mr = mx * p.c;
+    const bool move = mr > m_run + kTau;
+    const float alpha = move ? fast_exp2(m_run - mr) : 1.f;   // m_run = -inf: 0
+    m_run = move ? mr : m_run;
+    const float base = m_run == -INFINITY ? 0.f : m_run;
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -260,9 +270,10 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
       }
     }
     l_run = l_run * alpha + sum_rows16(rs);
-    m_run = m_new;
+    if (__ballot(move)) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] *= alpha;
+      for (int i = 0; i < 8; ++i) acc[i] *= alpha;
+    }
 
     // Stage V^T: lane (col = d-chunk, row = key group) writes 8 d-rows x 8 keys.
     const int pos = vt_pos(row * 4);   // keys 4row..4row+3 -> pos..pos+3; 16+4row.. -> pos+4..

@@ -397,7 +397,9 @@ def test_decode_split_partials_match_slices():
                 o_r, lse_r = finalize_ref((m[i, sp], l[i, sp], a[i, sp]))
                 assert np.max(np.abs(o_g - o_r)) < 1e-2
                 assert abs(lse_g - lse_r) / max(1.0, abs(lse_r)) < LSE_TOL
-                assert abs(float(pm[b, i, sp]) - m[i, sp]) < 1e-4 * max(1.0, abs(m[i, sp]))
+                # the stored reference lags the slice's largest logit by at most 8 ln 2
+                slack = 1e-4 * max(1.0, abs(m[i, sp]))
+                assert m[i, sp] - 8 * math.log(2) - slack <= float(pm[b, i, sp]) <= m[i, sp] + slack
 
 
 def test_decode_70b_tp8_s32768():
