@@ -37,9 +37,9 @@
 //   Accumulator: lane l holds head l%16 and keys 4*(l/16) + r of the block.
 //   Row max: in-lane over 8 scores, then across the four 16-lane rows.
 //   O~^T += V^T P^T: P^T comes from the score registers as the B operand
-//   (keys 4a+r of block 0 then of block 1, a = l/16); V^T is staged through a
-//   per-wave LDS region, stored transposed so the A operand (8 keys of one d)
-//   is one 16-byte LDS read.
+//   (keys 4a+r of block 0 then of block 1, a = l/16); V rows are stored as
+//   they are in a per-wave LDS region, and the A operand (8 keys of one d)
+//   is read with two of gfx950's transposing 8-byte LDS reads.
 // Keys outside the split, past the sequence, or on a page id outside the
 // pool are excluded (score -inf) and their V rows are zeroed before use, so
 // poisoned (NaN) slots never reach the result.
@@ -62,8 +62,11 @@ constexpr int kD = 128;
 constexpr int kWaves = 4;
 constexpr int kTile = 32;              // keys per wave tile
 constexpr float kTau = 8.f;            // allowed lag of the reference max (log2 units)
-constexpr int kVtStr = kTile + 8;      // V^T row stride in LDS (elements): 80 B
-constexpr int kWaveLds = kD * kVtStr;  // elements per wave region
+// V tile in LDS, one key row per 288 bytes: consecutive rows start 8 banks
+// apart, so the 4 rows x 32 bytes of a 16-lane transposing read never share
+// a bank.
+constexpr int kVrStr = kD + 16;
+constexpr int kWaveLds = kTile * kVrStr;  // elements per wave region
 
 struct DecodeParams {
   const uint16_t* q;
@@ -94,9 +97,6 @@ __device__ __forceinline__ float sum_rows16(float x) {
   return x + __shfl_xor(x, 32);
 }
 
-// Position of tile key kk (0..31) inside a V^T row: the A operand of lane
-// group a covers keys 4a..4a+3 and 16+4a..16+4a+3, stored contiguously.
-__device__ __forceinline__ int vt_pos(int kk) { return ((kk & 12) << 1) | ((kk & 16) >> 2) | (kk & 3); }
 
 // STREAM: K/V loads carry the non-temporal hint (each byte read once). In
 // head mode the waves of a workgroup (and, beyond 4 head blocks, several
@@ -275,20 +275,12 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
       for (int i = 0; i < 8; ++i) acc[i] *= alpha;
     }
 
-    // Stage V^T: lane (col = d-chunk, row = key group) writes 8 d-rows x 8 keys.
-    const int pos = vt_pos(row * 4);   // keys 4row..4row+3 -> pos..pos+3; 16+4row.. -> pos+4..
+    // Stage V: lane (col = d-chunk, row = key group) stores its 8 key rows
+    // (keys 4row+i and 16+4row+i) as they are, 16 bytes each.
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      uint32_t vf[8][4];   // word e of each V row (only [.][e] is used)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) vf[i][e] = vword(i, e);
-      const int d = col * 8 + 2 * e;
-      store16(&vt[d * kVtStr + pos],
-              u32x4{pack_lo16(vf[0][e], vf[1][e]), pack_lo16(vf[2][e], vf[3][e]),
-                    pack_lo16(vf[4][e], vf[5][e]), pack_lo16(vf[6][e], vf[7][e])});
-      store16(&vt[(d + 1) * kVtStr + pos],
-              u32x4{pack_hi16(vf[0][e], vf[1][e]), pack_hi16(vf[2][e], vf[3][e]),
-                    pack_hi16(vf[4][e], vf[5][e]), pack_hi16(vf[6][e], vf[7][e])});
+    for (int i = 0; i < 8; ++i) {
+      const int key = (i < 4 ? 0 : 16) + row * 4 + (i & 3);
+      store16(&vt[key * kVrStr + col * 8], u32x4{vword(i, 0), vword(i, 1), vword(i, 2), vword(i, 3)});
     }
     after_stage();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -299,9 +291,19 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
                            EP::pack2(s[1][0], s[1][1]), EP::pack2(s[1][2], s[1][3])};
     lr_run = lr_run * alpha +
              sum_rows16(EP::add_pair(pf[3], EP::add_pair(pf[2], EP::add_pair(pf[1], EP::add_pair(pf[0], 0.f)))));
+    // A operand V^T (d = 16db + col, keys 4row..4row+3 and 16+4row..+3, the
+    // key order of P^T) by transposing reads: lane (col, row) addresses key
+    // row 4row + col/4 (and 16 + that), d 16db + 4(col % 4), and receives
+    // element col % 4 of lanes 4k + col/4, i.e. d = 16db + col of keys
+    // 4row + k.
+    const uint16_t* vlo = vt + (row * 4 + (col >> 2)) * kVrStr + 4 * (col & 3);
+    const uint16_t* vhi = vlo + 16 * kVrStr;
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
-      acc[db] = EP::mfma16(load16(&vt[(db * 16 + col) * kVtStr + row * 8]), pf, acc[db]);
+    for (int db = 0; db < 8; ++db) {
+      const u32x2 lo = lds_read_tr16(vlo + 16 * db);
+      const u32x2 hi = lds_read_tr16(vhi + 16 * db);
+      acc[db] = EP::mfma16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf, acc[db]);
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
