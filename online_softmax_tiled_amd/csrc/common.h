@@ -164,7 +164,17 @@ __device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) { return p
 // wait states between a vector write of an operand and the swap reading it.
 __device__ __forceinline__ void swap_halves(float x, float& lo, float& hi) {
   uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  lo = __builtin_bit_cast(float, a);
+  hi = __builtin_bit_cast(float, b);
+}
+// v_permlane16_swap exchanges the odd 16-lane rows of its first operand with
+// the even rows of its second; with x in both, lo holds x of row 2j and hi x
+// of row 2j + 1 in every lane of the row pair j (same position in the row).
+// Assembly for the same reasons as above.
+__device__ __forceinline__ void swap_rows16(float x, float& lo, float& hi) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
   lo = __builtin_bit_cast(float, a);
   hi = __builtin_bit_cast(float, b);
 }

@@ -87,14 +87,17 @@ struct DecodeParams {
 };
 
 // Max / sum of x over the four 16-lane rows of a wave (lanes l, l^16,
-// l^32, l^48).
+// l^32, l^48), by the lane swaps (no LDS round trip); every lane gets the
+// same bits (sums add the lower row first).
 __device__ __forceinline__ float max_rows16(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
+  float lo, hi;
+  swap_rows16(x, lo, hi);
+  return max_halves(fmaxf(lo, hi));
 }
 __device__ __forceinline__ float sum_rows16(float x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
+  float lo, hi;
+  swap_rows16(x, lo, hi);
+  return sum_halves(lo + hi);
 }
 
 
