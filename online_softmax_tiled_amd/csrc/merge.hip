@@ -20,7 +20,8 @@
 // 32) or 16 (one slice of 128: 256 threads instead of 1024, so a CU holds
 // four times as many rows at once), with the loads of U splits in flight at
 // a time (with several slices, the first U before the maximum is known); the
-// 32 lane sums are then added through LDS in lane order.
+// 32 lane sums are then added by a fixed tree: lane exchanges inside each
+// wave, then the 4 waves in order through LDS.
 #include "common.h"
 
 namespace attn {
@@ -38,17 +39,42 @@ struct MergeParams {
   int B, h, max_splits, chunk;
 };
 
+// x of the lane R places round inside each 16-lane row (a DPP row
+// rotation); for R = 8 that is lane l ^ 8.
+template <int R>
+__device__ __forceinline__ float row_ror(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x120 + R, 0xf, 0xf, false));
+}
+// Maximum over the 64 lanes of a wave, by vector-ALU lane exchanges.
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-  return x;
+  float lo, hi;
+  swap_halves(x, lo, hi);
+  x = fmaxf(lo, hi);
+  swap_rows16(x, lo, hi);
+  x = fmaxf(lo, hi);
+  // rotations of each 16-lane row by 8, 4, 2, 1
+  x = fmaxf(x, row_ror<8>(x));
+  x = fmaxf(x, row_ror<4>(x));
+  x = fmaxf(x, row_ror<2>(x));
+  return fmaxf(x, row_ror<1>(x));
+}
+// Sum of x over lanes l, l ^ 8, l ^ 16, l ^ 32 of a wave (lane bits 3-5),
+// as a fixed tree; every lane gets the same bits (each step adds two values,
+// and floating-point addition of two values is commutative).
+__device__ __forceinline__ float sum_lanes_8_16_32(float x) {
+  x += row_ror<8>(x);
+  float lo, hi;
+  swap_rows16(x, lo, hi);
+  x = lo + hi;
+  swap_halves(x, lo, hi);
+  return lo + hi;
 }
 
 // ND: d-slices per (sequence, head); each slice is kD / ND values, handled
 // by FL = kD / ND / (4 V) d-lanes of V float4 each and kSL = 32 split lanes
 // (FL * 32 threads: 256 in both layouts used). Split lane s sums splits s,
 // s + 32, s + 64, ... in that order, with U partials in flight, and the 32
-// lane sums are added in lane order. The
+// lane sums are added by the same fixed tree in both layouts. The
 // summation order of a row therefore depends only on its own split count,
 // never on ND, on the batch or on max_splits: with a split length that does
 // not depend on the batch, every row's bits are batch-invariant ("Decode
@@ -64,9 +90,10 @@ __global__ __launch_bounds__(kD / ND / (4 * V) * kSL) void merge_kernel(MergePar
   constexpr int FL = kSlice / (4 * V);
   constexpr int NT = FL * kSL;
   constexpr int NW = NT / 64;
+  static_assert(FL == 8 && NW == 4, "the lane tree below takes 8 d-lanes and 4 waves of split lanes");
   __shared__ float red_m[NW];
-  __shared__ __attribute__((aligned(16))) float red_o[kSL][kSlice];
-  __shared__ float red_l[kSL];
+  // per wave and d-lane: its 8 split lanes' sums of O~ (4V values) and l
+  __shared__ __attribute__((aligned(16))) float red_w[NW][FL][4 * V + 4];
 
   const int bh = blockIdx.x;
   const int d0 = blockIdx.y * kSlice;
@@ -107,6 +134,12 @@ __global__ __launch_bounds__(kD / ND / (4 * V) * kSL) void merge_kernel(MergePar
                       : f32x4{};
   }
   float mloc = -INFINITY;
+  if (U0 * kSL >= lim) {
+    // the preloaded rows are every split row: the maximum comes from them
+#pragma unroll
+    for (int u = 0; u < U0; ++u)
+      if (sl + u * kSL < n && li0[u] > 0.f) mloc = fmaxf(mloc, mi0[u]);
+  } else
   for (int i = tid; i < lim; i += NT) {
     if (!(ATTN_IN_RANGE(p.part_m + base + i, 4, p.part_m, part_rows * 4, kSiteMrgPartML) &&
           ATTN_IN_RANGE(p.part_l + base + i, 4, p.part_l, part_rows * 4, kSiteMrgPartML)))
@@ -171,24 +204,38 @@ __global__ __launch_bounds__(kD / ND / (4 * V) * kSL) void merge_kernel(MergePar
       }
     }
   }
+  // The 32 split lanes' sums: the 8 of each wave by lane exchanges (split
+  // lane bits are lane bits 3-5), then the 4 waves in order through LDS.
 #pragma unroll
-  for (int c = 0; c < V; ++c) *reinterpret_cast<f32x4*>(&red_o[sl][d + 4 * c]) = acc[c];
-  if (tid % FL == 0) red_l[sl] = lacc;
+  for (int c = 0; c < V; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[c][e] = sum_lanes_8_16_32(acc[c][e]);
+  lacc = sum_lanes_8_16_32(lacc);
+  const int wave = tid >> 6, wl = tid & 63;
+  if (wl < FL) {
+#pragma unroll
+    for (int c = 0; c < V; ++c) *reinterpret_cast<f32x4*>(&red_w[wave][wl][4 * c]) = acc[c];
+    red_w[wave][wl][4 * V] = lacc;
+  }
   __syncthreads();
-  if (tid < kSlice / 2) {
-    float l_all = 0.f;
+  if (tid < FL) {
+    f32x4 o[V];
+    float l_all = red_w[0][tid][4 * V];
 #pragma unroll
-    for (int s = 0; s < kSL; ++s) l_all += red_l[s];
-    const int dd = tid * 2;
-    float o0 = 0.f, o1 = 0.f;
+    for (int c = 0; c < V; ++c) o[c] = *reinterpret_cast<const f32x4*>(&red_w[0][tid][4 * c]);
 #pragma unroll
-    for (int s = 0; s < kSL; ++s) {
-      o0 += red_o[s][dd];
-      o1 += red_o[s][dd + 1];
+    for (int w = 1; w < NW; ++w) {
+      l_all += red_w[w][tid][4 * V];
+#pragma unroll
+      for (int c = 0; c < V; ++c) o[c] += *reinterpret_cast<const f32x4*>(&red_w[w][tid][4 * c]);
     }
     const float inv = 1.f / l_all;
-    if (ATTN_IN_RANGE(op + 2 * tid, 4, p.o, (size_t)p.B * p.h * kD * 2, kSiteMrgO))
-      reinterpret_cast<uint32_t*>(op)[tid] = E::pack2(o0 * inv, o1 * inv);
+#pragma unroll
+    for (int c = 0; c < V; ++c) {
+      const f32x4 q = o[c] * inv;
+      if (ATTN_IN_RANGE(op + tid * 4 * V + 4 * c, 8, p.o, (size_t)p.B * p.h * kD * 2, kSiteMrgO))
+        store8(op + tid * 4 * V + 4 * c, u32x2{E::pack2(q[0], q[1]), E::pack2(q[2], q[3])});
+    }
     if (tid == 0 && blockIdx.y == 0 && p.lse != nullptr &&
         ATTN_IN_RANGE(p.lse + bh, 4, p.lse, (size_t)p.B * p.h * 4, kSiteMrgLse))
       p.lse[bh] = big + fast_log2(l_all) * kLn2;
