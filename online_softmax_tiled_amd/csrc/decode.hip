@@ -105,8 +105,10 @@ __device__ __forceinline__ float sum_rows16(float x) {
 // head mode the waves of a workgroup (and, beyond 4 head blocks, several
 // workgroups) read the same keys, and the loads must leave them in the
 // caches.
+// 8-bit forms: at most 168 registers, 3 workgroups per CU (they fit without
+// spills; the compiler would otherwise take 170 in the contiguous forms).
 template <int DT, bool PAGED, bool STREAM, bool KV8>
-__global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256, KV8 ? 3 : 2) void decode_split_kernel(DecodeParams p) {
   using E = Elem<DT>;
   // The PV product: on the operand type with 8-bit V it is fp16 whatever the
   // query type (E4M3 codes, at most 448 in magnitude, are exact fp16 values,
