@@ -54,6 +54,22 @@ def run_fp8(dec, k_scale, v_scale, plan=None, one_call=True):
     return o, lse.cpu().numpy().astype(np.float64), plan
 
 
+@pytest.mark.parametrize("plan", [(1024, 3), (4096, 1)])
+@pytest.mark.parametrize("paged", [False, True])
+def test_fp8kv_decode_reference_moves_mid_split(paged, plan):
+    # q scaled by 8 against E4M3 keys of magnitude up to 8 (k_scale 0.37):
+    # logits of std about 10 nats, whose running maximum keeps rising over the
+    # first tiles of each long split, so the kernel's lagging reference moves
+    # (and O~ is rescaled) after the first tile.
+    lens = [700, 1500, 2900]
+    dec = make_decode(B=3, h=8, h_kv=2, d=128, dtype="bf16", seed=78, seq_lens=lens, paged=paged, page_size=16,
+                      kv_codes=True)
+    dec["q"] = (dec["q"].float() * 8).to(dec["q"].dtype)
+    o_ref, lse_ref = oracle_fp8(dec, K_SCALE, V_SCALE)
+    o, lse, used = run_fp8(dec, K_SCALE, V_SCALE, plan)
+    assert_outputs(o, lse, o_ref, lse_ref, "bf16", f"fp8 KV decode, moving reference, paged={paged} plan={used}")
+
+
 @pytest.mark.parametrize("one_call", [True, False])
 @pytest.mark.parametrize("paged,page_size", [(False, 16), (True, 16), (True, 48)])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])

@@ -402,6 +402,36 @@ def test_decode_split_partials_match_slices():
                 assert m[i, sp] - 8 * math.log(2) - slack <= float(pm[b, i, sp]) <= m[i, sp] + slack
 
 
+@pytest.mark.parametrize("plan", [(1024, 3), (4096, 1)])
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_decode_reference_moves_mid_split(paged, dtype, plan):
+    # The decode kernels keep a reference maximum that moves only when a
+    # head's logit passes it by more than 2^8; N(0,1) logits hardly ever do
+    # after a split's first tile. Here q is scaled by 8 (logits of std about
+    # 8 nats, whose running maximum keeps rising over the first tiles) and
+    # each KV head gets one late key equal to 0.05 q of its group's first
+    # head (a logit about 36 nats, some 9 above the others' maximum), so the
+    # reference moves, and O~ is rescaled, in the middle of long splits.
+    lens = [700, 1500, 2900]
+    dec = make_decode(B=3, h=8, h_kv=2, d=128, dtype=dtype, seed=77, seq_lens=lens, paged=paged, page_size=16)
+    dec["q"] = (dec["q"].float() * 8).to(dec["q"].dtype)
+    g = dec["h"] // dec["h_kv"]
+    for b, s_b in enumerate(lens):
+        for kvh in range(dec["h_kv"]):
+            j = s_b - 40 - 7 * kvh
+            key = (dec["q"][b, kvh * g].float() * 0.05).to(dec["q"].dtype)
+            dec["k_seqs"][b][kvh, j] = key
+            if paged:
+                dec["k_pool"][dec["block_table"][b, j // 16], j % 16, kvh] = key
+            else:
+                dec["k"][b, kvh, j] = key
+    o_ref, lse_ref = decode_ref(dec["q"], dec["k_seqs"], dec["v_seqs"], dec["seq_lens"], dec["scale"])
+    assert lse_ref[:, 0].min() > 30          # the planted key dominates head 0 of each sequence
+    o, lse, used = run_decode(dec, plan=plan)
+    assert_outputs(o, lse, o_ref, lse_ref, dtype, f"decode, moving reference, paged={paged} plan={used}")
+
+
 def test_decode_70b_tp8_s32768():
     dec = make_config("decode_70b_tp8_s32768")
     o_ref, lse_ref = decode_ref(dec["q"], dec["k_seqs"], dec["v_seqs"], dec["seq_lens"], dec["scale"])
