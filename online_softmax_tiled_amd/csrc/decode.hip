@@ -35,7 +35,10 @@
 //   S^T = K Q^T: A = K rows loaded straight from global memory (lane l: key
 //   l%16 of a 16-key block, d in [8*(l/16) + 32c, +8)), B = Q^T in VGPRs.
 //   Accumulator: lane l holds head l%16 and keys 4*(l/16) + r of the block.
-//   Row max: in-lane over 8 scores, then across the four 16-lane rows.
+//   Row max: in-lane over 8 scores, then across the four 16-lane rows (lane
+//   swaps). The reference that the weights are taken against lags the
+//   running maximum by up to 2^8, so O~ is rescaled only on the few tiles
+//   where a head's maximum passes it by more.
 //   O~^T += V^T P^T: P^T comes from the score registers as the B operand
 //   (keys 4a+r of block 0 then of block 1, a = l/16); V rows are stored as
 //   they are in a per-wave LDS region, and the A operand (8 keys of one d)
