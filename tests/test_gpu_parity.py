@@ -315,20 +315,31 @@ def test_merge_on_oracle_partials():
     assert_outputs(of, lf.cpu().numpy().astype(np.float64), o_ref, lse_ref, "f16", "merge f16")
 
 
-def test_merge_many_splits():
-    rng = np.random.default_rng(10)
-    B, h, S = 1, 8, 256
+@pytest.mark.parametrize("S", [256, 300, 700])
+def test_merge_many_splits(S):
+    # Many splits and few rows take the four-slice layout; up to 256 splits its
+    # preloaded rows hold every split (the maximum is taken from them), beyond
+    # that the maximum is read in a loop. Sequence 1 has fewer valid splits
+    # than max_splits: its rows past the valid count hold NaN and must not count.
+    rng = np.random.default_rng(10 + S)
+    B, h, chunk = 2, 8, 128
     m = rng.normal(0, 20, size=(B, h, S)).astype(np.float32)
     l = (rng.random((B, h, S)) * 30 + 1).astype(np.float32)
     a = (rng.normal(size=(B, h, S, 128)) * l[..., None]).astype(np.float32)
-    lens = np.array([S * 128], dtype=np.int32)
-    o, lse = api.merge_states(to_dev(a), to_dev(m), to_dev(l), to_dev(lens), 128, torch.float16)
+    n_valid = [S, S - 37]
+    lens = np.array([n * chunk - 5 for n in n_valid], dtype=np.int32)
+    m[1, :, n_valid[1]:] = np.nan
+    l[1, :, n_valid[1]:] = np.nan
+    a[1, :, n_valid[1]:] = np.nan
+    o, lse = api.merge_states(to_dev(a), to_dev(m), to_dev(l), to_dev(lens), chunk, torch.float16)
     torch.cuda.synchronize()
     o_ref = np.zeros((B, h, 128))
     lse_ref = np.zeros((B, h))
-    for i in range(h):
-        o_ref[0, i], lse_ref[0, i] = merge_partials_ref(m[0, i], l[0, i], a[0, i])
-    assert_outputs(o, lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "f16", "merge 256 splits")
+    for b in range(B):
+        n = n_valid[b]
+        for i in range(h):
+            o_ref[b, i], lse_ref[b, i] = merge_partials_ref(m[b, i, :n], l[b, i, :n], a[b, i, :n])
+    assert_outputs(o, lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "f16", f"merge {S} splits")
 
 
 # ------------------------------------------------------------------ decode
