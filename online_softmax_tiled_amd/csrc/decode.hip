@@ -108,10 +108,11 @@ __device__ __forceinline__ float sum_rows16(float x) {
 // head mode the waves of a workgroup (and, beyond 4 head blocks, several
 // workgroups) read the same keys, and the loads must leave them in the
 // caches.
-// 8-bit forms: at most 168 registers, 3 workgroups per CU (they fit without
-// spills; the compiler would otherwise take 170 in the contiguous forms).
+// Paged 8-bit forms: at most 168 registers, 3 workgroups per CU (they fit
+// without spills). The contiguous 8-bit forms take a few more; they serve
+// batches of few long sequences, where the grid fills one workgroup per CU.
 template <int DT, bool PAGED, bool STREAM, bool KV8>
-__global__ __launch_bounds__(256, KV8 ? 3 : 2) void decode_split_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256, KV8 && PAGED ? 3 : 2) void decode_split_kernel(DecodeParams p) {
   using E = Elem<DT>;
   // The PV product: on the operand type with 8-bit V it is fp16 whatever the
   // query type (E4M3 codes, at most 448 in magnitude, are exact fp16 values,
@@ -513,18 +514,21 @@ __global__ __launch_bounds__(256, KV8 ? 3 : 2) void decode_split_kernel(DecodePa
     return;
   }
 
-  // Merge the 4 wave states through LDS (reusing the V^T regions).
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(lds);            // [wave][16 heads][128 d]
-  float* red_ml = red + kWaves * 16 * kD;                 // [wave][16][3]: m, l, l~
-  // acc[db] lane (col, row) reg r: head col, d = 16db + 4row + r
+  // Merge the 4 wave states through LDS. Each wave writes its state into its
+  // own V region, which no other wave uses, once its own tiles are done: [16
+  // heads][128 d] then [16][3] (m, l, l~). One barrier, before the reads.
+  static_assert((16 * kD + 16 * 3) * 4 <= kWaveLds * 2, "a wave's state fits its V region");
+  auto red_of = [&](int w) { return reinterpret_cast<float*>(lds + w * kWaveLds); };
+  {
+    float* r = red_of(wave);
+    // acc[db] lane (col, row) reg r: head col, d = 16db + 4row + r
 #pragma unroll
-  for (int db = 0; db < 8; ++db)
-    *reinterpret_cast<f32x4*>(&red[(wave * 16 + col) * kD + db * 16 + row * 4]) = acc[db];
-  if (row == 0) {
-    red_ml[(wave * 16 + col) * 3 + 0] = m_run;
-    red_ml[(wave * 16 + col) * 3 + 1] = l_run;
-    red_ml[(wave * 16 + col) * 3 + 2] = lr_run;
+    for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(&r[col * kD + db * 16 + row * 4]) = acc[db];
+    if (row == 0) {
+      r[16 * kD + col * 3 + 0] = m_run;
+      r[16 * kD + col * 3 + 1] = l_run;
+      r[16 * kD + col * 3 + 2] = lr_run;
+    }
   }
   __syncthreads();
 
@@ -534,7 +538,7 @@ __global__ __launch_bounds__(256, KV8 ? 3 : 2) void decode_split_kernel(DecodePa
     float mw[kWaves], m_all = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      mw[w] = red_ml[(w * 16 + j) * 3];
+      mw[w] = red_of(w)[16 * kD + j * 3];
       m_all = fmaxf(m_all, mw[w]);
     }
     f32x4 o = f32x4{};
@@ -543,9 +547,9 @@ __global__ __launch_bounds__(256, KV8 ? 3 : 2) void decode_split_kernel(DecodePa
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
         const float wt = fast_exp2(mw[w] - m_all);   // empty wave: 2^-inf = 0
-        l_all += wt * red_ml[(w * 16 + j) * 3 + 1];
-        lr_all += wt * red_ml[(w * 16 + j) * 3 + 2];
-        o += wt * *reinterpret_cast<const f32x4*>(&red[(w * 16 + j) * kD + d]);
+        l_all += wt * red_of(w)[16 * kD + j * 3 + 1];
+        lr_all += wt * red_of(w)[16 * kD + j * 3 + 2];
+        o += wt * *reinterpret_cast<const f32x4*>(&red_of(w)[j * kD + d]);
       }
     }
     float f = lr_all > 0.f ? l_all / lr_all : 1.f;

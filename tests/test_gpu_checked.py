@@ -57,11 +57,13 @@ CASES = [
     ("gather_48", lambda: P.test_paged_gather_bit_exact(48, 1)),
     ("gather_16_spare", lambda: P.test_paged_gather_bit_exact(16, 5)),
     ("merge_oracle_partials", lambda: P.test_merge_on_oracle_partials()),
-    ("merge_many_splits", lambda: P.test_merge_many_splits()),
+    ("merge_many_splits", lambda: P.test_merge_many_splits(256)),
+    ("merge_many_splits_loop", lambda: P.test_merge_many_splits(700)),
     ("decode_contiguous", lambda: P.test_decode_small(False, 16, "bf16", True)),
     ("decode_paged_32", lambda: P.test_decode_small(True, 32, "f16", False)),
     ("decode_no_keys", lambda: P.test_decode_no_keys_at_all(64)),
     ("decode_70b_tp8", lambda: P.test_decode_70b_tp8_s32768()),
+    ("decode_moving_reference", lambda: P.test_decode_reference_moves_mid_split(True, "bf16", (1024, 3))),
     ("decode_rows_paged_32", lambda: P.test_decode_head_rows("bf16", True, 32, [None, (208, 8)])),
     ("decode_head_mode_48", lambda: P.test_decode_head_rows("bf16", True, 48, [None, (96, 16)])),
     ("decode_rows_pool_under_4gb", lambda: P.test_decode_head_rows_large_pools("under_4gb")),
@@ -72,6 +74,7 @@ CASES = [
     ("merge_lse_empty_sides", lambda: P.test_merge_lse_against_oracle_with_empty_sides("bf16", 17)),
     ("stream_read", lambda: P.test_stream_read_reads_every_word_once()),
     ("fp8_decode_paged", lambda: F8.test_fp8kv_decode_small(True, 16, "bf16", True)),
+    ("fp8_decode_moving_reference", lambda: F8.test_fp8kv_decode_reference_moves_mid_split(False, (1024, 3))),
     ("fp8_decode_rows_paged", lambda: F8.test_fp8kv_decode_heads_as_rows(32, "paged16")),
     ("fp8_decode_rows_contiguous", lambda: F8.test_fp8kv_decode_heads_as_rows(128, "contiguous")),
     ("fp8_decode_pool_under_4gb", lambda: F8.test_fp8kv_decode_rows_large_pools("under_4gb")),
