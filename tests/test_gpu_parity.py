@@ -342,6 +342,43 @@ def test_merge_many_splits(S):
     assert_outputs(o, lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "f16", f"merge {S} splits")
 
 
+@pytest.mark.parametrize("n_max", [5, 8, 13, 16])
+def test_merge_bits_do_not_depend_on_max_splits(n_max):
+    # A row's merged bits depend only on its own split count: the same
+    # partials merged with max_splits = n_max and with the buffers padded to
+    # 40 splits (NaN rows beyond each row's valid count) agree bit for bit,
+    # including a column whose every term is -0.0.
+    rng = np.random.default_rng(40 + n_max)
+    B, h, chunk = 3, 4, 64
+    n_valid = [n_max, max(1, n_max - 2), 1]
+    lens = np.array([n * chunk - 3 for n in n_valid], dtype=np.int32)
+    m = rng.normal(0, 5, size=(B, h, n_max)).astype(np.float32)
+    l = (rng.random((B, h, n_max)) * 30 + 1).astype(np.float32)
+    a = (rng.normal(size=(B, h, n_max, 128)) * l[..., None]).astype(np.float32)
+    a[0, 0, :, 7] = -0.0                       # a column whose every term is -0
+    outs = []
+    for S in (n_max, 40):
+        pm = np.full((B, h, S), np.nan, dtype=np.float32)
+        pl = np.full((B, h, S), np.nan, dtype=np.float32)
+        po = np.full((B, h, S, 128), np.nan, dtype=np.float32)
+        for b in range(B):
+            k = n_valid[b]
+            pm[b, :, :k], pl[b, :, :k], po[b, :, :k] = m[b, :, :k], l[b, :, :k], a[b, :, :k]
+        o, lse = api.merge_states(to_dev(po), to_dev(pm), to_dev(pl), to_dev(lens), chunk, torch.bfloat16)
+        torch.cuda.synchronize()
+        outs.append((o.view(torch.int16).cpu().numpy(), lse.view(torch.int32).cpu().numpy()))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    o_ref = np.zeros((B, h, 128))
+    lse_ref = np.zeros((B, h))
+    for b in range(B):
+        for i in range(h):
+            k = n_valid[b]
+            o_ref[b, i], lse_ref[b, i] = merge_partials_ref(m[b, i, :k], l[b, i, :k], a[b, i, :k])
+    o_dev = torch.from_numpy(outs[0][0]).view(torch.bfloat16)
+    assert_outputs(o_dev, outs[0][1].view(np.float32).astype(np.float64), o_ref, lse_ref, "bf16",
+                   f"merge of at most {n_max} splits")
+
+
 # ------------------------------------------------------------------ decode
 
 def run_decode(dec, plan=None, one_call=True):
