@@ -162,6 +162,9 @@ __device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) { return p
 // combination of the two results into the first result alone (a kernel
 // returning their sum emits v_add_f32 v1, v1, v1). The s_nop gives the two
 // wait states between a vector write of an operand and the swap reading it.
+// Not volatile: the swap is a pure function of its operands, and a volatile
+// statement counts as a possible memory write, after which the compiler no
+// longer reads read-only tables (the decode's block table) with scalar loads.
 __device__ __forceinline__ void swap_halves(float x, float& lo, float& hi) {
   uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
   asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
