@@ -139,13 +139,14 @@ __global__ __launch_bounds__(kD / ND / (4 * V) * kSL) void merge_kernel(MergePar
 #pragma unroll
     for (int u = 0; u < U0; ++u)
       if (sl + u * kSL < n && li0[u] > 0.f) mloc = fmaxf(mloc, mi0[u]);
-  } else
-  for (int i = tid; i < lim; i += NT) {
-    if (!(ATTN_IN_RANGE(p.part_m + base + i, 4, p.part_m, part_rows * 4, kSiteMrgPartML) &&
-          ATTN_IN_RANGE(p.part_l + base + i, 4, p.part_l, part_rows * 4, kSiteMrgPartML)))
-      continue;
-    const float mi = p.part_m[base + i];
-    if (i < n && p.part_l[base + i] > 0.f) mloc = fmaxf(mloc, mi);
+  } else {
+    for (int i = tid; i < lim; i += NT) {
+      if (!(ATTN_IN_RANGE(p.part_m + base + i, 4, p.part_m, part_rows * 4, kSiteMrgPartML) &&
+            ATTN_IN_RANGE(p.part_l + base + i, 4, p.part_l, part_rows * 4, kSiteMrgPartML)))
+        continue;
+      const float mi = p.part_m[base + i];
+      if (i < n && p.part_l[base + i] > 0.f) mloc = fmaxf(mloc, mi);
+    }
   }
   mloc = wave_max(mloc);
   if ((tid & 63) == 0) red_m[tid >> 6] = mloc;
