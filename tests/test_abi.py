@@ -444,3 +444,15 @@ def test_product_library_has_no_bounds_checks(lib):
     assert "without device bounds checks" in lib.attn_last_error().decode()
     assert lib.attn_check_clear() == 2
     assert lib.attn_check_selftest(ctypes.c_void_p(16), None) == 2
+
+
+@pytest.mark.parametrize("n", [2, 8])
+def test_bench_refuses_more_than_one_gpu(n):
+    # The bench measures one GPU; a request for more exits before any GPU
+    # work (and before torch is imported) with a message naming the count.
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", str(n)],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert r.stdout == ""
+    assert f"--gpus {n}" in r.stderr and "one GPU" in r.stderr
